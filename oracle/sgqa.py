@@ -130,29 +130,33 @@ def proxy_keys(kp_bits: np.ndarray, positions: np.ndarray, cfg: Config,
 
 
 def merge(k_hat: np.ndarray, logits: np.ndarray) -> np.ndarray:
-    """One block: for every coordinate d, softmax over the block's tokens of
-    logits[:, d] (the common maximum subtracted first) weights k_hat[:, d]."""
-    m = logits.max(axis=0)
+    """Blocks [..., B, Di] -> summaries [..., Di]: for every coordinate d, the
+    softmax over the block's B tokens of logits[..., :, d] (the common
+    maximum subtracted first) weights k_hat[..., :, d]."""
+    m = logits.max(axis=-2, keepdims=True)
     a = np.exp(logits - m)
-    return (a * k_hat).sum(axis=0) / a.sum(axis=0)
+    return (a * k_hat).sum(axis=-2) / a.sum(axis=-2)
 
 
 def compress(kp_bits: np.ndarray, logits: np.ndarray, blocks, cfg: Config,
-             ln_gamma=None, ln_beta=None):
+             ln_gamma=None, ln_beta=None, chunk: int = 8192):
     """Store rows for the listed blocks of one sequence.
 
     ``kp_bits`` [T, Di] (bf16 bits) and ``logits`` [T, Di] (fp32) hold the
     sequence's tokens from position 0.  Returns ``(stored, exact)``: the
     stored values (fp32 result rounded to bf16, then to E4M3 when
     ``store_q8``) and the unrounded float64 summaries, both [len(blocks), Di].
+    Blocks are processed ``chunk`` at a time only to bound memory.
     """
     B = cfg.block_size
     blocks = np.asarray(blocks, dtype=np.int64).reshape(-1)
     exact = np.empty((blocks.size, cfg.idx_dim), dtype=np.float64)
-    for n, r in enumerate(blocks):
-        pos = np.arange(B * r, B * r + B)
-        k_hat = proxy_keys(kp_bits[pos], pos, cfg, ln_gamma, ln_beta)
-        exact[n] = merge(k_hat, np.asarray(logits[pos], dtype=np.float64))
+    for c0 in range(0, blocks.size, chunk):
+        r = blocks[c0:c0 + chunk]
+        pos = (r[:, None] * B + np.arange(B)[None, :])               # [n, B]
+        k_hat = proxy_keys(kp_bits[pos.reshape(-1)], pos.reshape(-1), cfg, ln_gamma, ln_beta)
+        lg = np.asarray(logits[pos.reshape(-1)], dtype=np.float64)
+        exact[c0:c0 + chunk] = merge(k_hat.reshape(r.size, B, -1), lg.reshape(r.size, B, -1))
     stored = q8(exact) if cfg.store_q8 else round_bf16(exact)
     return stored, exact
 

@@ -1,0 +1,446 @@
+// Host side of libsgqa.so: argument validation, launch policy, workspace
+// carving and the extern "C" entry points declared in include/sgqa.h.
+//
+// Every check runs before the first HIP call, so rejected calls are testable
+// on a machine without a GPU and enqueue nothing.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <string.h>
+
+#include <algorithm>
+#include <string>
+
+#include "sgqa.h"
+#include "sgqa_internal.hpp"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+int fail(int status, const char* fmt, ...) {
+    char buf[512];
+    va_list ap;
+    va_start(ap, fmt);
+    vsnprintf(buf, sizeof buf, fmt, ap);
+    va_end(ap);
+    g_last_error = buf;
+    return status;
+}
+
+int hip_fail(hipError_t e, const char* what) {
+    return fail(SGQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+constexpr int64_t kMaxExtent = (int64_t)1 << 40;   // bound on offsets / lengths
+constexpr size_t kAlign = 256;
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+int check_config(const sgqa_config* c) {
+    if (!c) return fail(SGQA_ERR_NULL, "cfg is NULL");
+    if (c->num_q_heads <= 0 || c->num_kv_groups <= 0 || c->head_dim <= 0 || c->idx_heads <= 0 ||
+        c->idx_dim <= 0 || c->rope_dim < 0 || c->block_size <= 0 || c->topk_blocks <= 0)
+        return fail(SGQA_ERR_CONFIG, "config sizes must be positive");
+    if (c->num_q_heads % c->num_kv_groups != 0)
+        return fail(SGQA_ERR_CONFIG, "num_q_heads (%d) is not a multiple of num_kv_groups (%d)",
+                    c->num_q_heads, c->num_kv_groups);
+    if (c->rope_dim % 2 != 0 || c->rope_dim > c->idx_dim)
+        return fail(SGQA_ERR_CONFIG, "rope_dim (%d) must be even and <= idx_dim", c->rope_dim);
+    if (!(isfinite(c->rope_base) && c->rope_base > 0.f))
+        return fail(SGQA_ERR_CONFIG, "rope_base must be finite and positive");
+    if (!(isfinite(c->softmax_scale) && c->softmax_scale > 0.f))
+        return fail(SGQA_ERR_CONFIG, "softmax_scale must be finite and positive");
+    if (!(isfinite(c->eps_rms) && c->eps_rms >= 0.f && isfinite(c->eps_ln) && c->eps_ln >= 0.f))
+        return fail(SGQA_ERR_CONFIG, "eps_rms / eps_ln must be finite and >= 0");
+    if (c->store_q8 != 0 && c->store_q8 != 1)
+        return fail(SGQA_ERR_CONFIG, "store_q8 must be 0 or 1");
+    if (c->num_q_heads != sgqa::kHeads || c->num_kv_groups != sgqa::kGroups ||
+        c->head_dim != sgqa::kHeadDim || c->idx_heads != sgqa::kIdxHeads ||
+        c->idx_dim != sgqa::kIdxDim || c->rope_dim != sgqa::kRopeDim)
+        return fail(SGQA_ERR_UNSUPPORTED,
+                    "compiled shapes are H=64, G=4, D=192, idx_heads=4, idx_dim=128, rope_dim=32");
+    const int B = c->block_size;
+    if (B != 1 && B != 2 && B != 4 && B != 8 && B != 16)
+        return fail(SGQA_ERR_UNSUPPORTED, "block_size %d not in {1,2,4,8,16}", B);
+    if (c->topk_blocks > sgqa::kMaxTopK)
+        return fail(SGQA_ERR_UNSUPPORTED, "topk_blocks %d above %d", c->topk_blocks, sgqa::kMaxTopK);
+    return SGQA_OK;
+}
+
+int check_seqs(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
+    if (!s) return fail(SGQA_ERR_NULL, "seqs is NULL");
+    if (n <= 0) return fail(SGQA_ERR_SHAPE, "n_seqs must be >= 1 (got %d)", n);
+    for (int32_t i = 0; i < n; ++i) {
+        const sgqa_seq& q = s[i];
+        const int64_t f[8] = {q.q_offset, q.n_q, q.pos0, q.cache_len,
+                              q.kv_offset, q.kv_capacity, q.store_offset, q.store_capacity};
+        for (int k = 0; k < 8; ++k)
+            if (f[k] < 0 || f[k] > kMaxExtent)
+                return fail(SGQA_ERR_SHAPE, "seqs[%d]: field %d out of range [0, 2^40]", i, k);
+        if (q.cache_len != q.pos0 + q.n_q)
+            return fail(SGQA_ERR_CAUSAL, "seqs[%d]: cache_len %lld != pos0 %lld + n_q %lld", i,
+                        (long long)q.cache_len, (long long)q.pos0, (long long)q.n_q);
+        if (q.cache_len > q.kv_capacity)
+            return fail(SGQA_ERR_CAPACITY, "seqs[%d]: cache_len %lld > kv_capacity %lld", i,
+                        (long long)q.cache_len, (long long)q.kv_capacity);
+        if (q.cache_len / c->block_size > q.store_capacity)
+            return fail(SGQA_ERR_CAPACITY, "seqs[%d]: %lld blocks exceed store_capacity %lld", i,
+                        (long long)(q.cache_len / c->block_size), (long long)q.store_capacity);
+    }
+    return SGQA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// launch policy
+// ---------------------------------------------------------------------------
+struct IndexPlan {
+    int n_split = 1;
+    int split_blocks = 0;
+    int cap = 0;
+    int64_t rows = 0;           // packed query rows spanned (max q_offset + n_q)
+    size_t ws = 0;
+};
+
+struct AttnPlan {
+    int n_split = 1;
+    int chunks_per_split = 0;
+    int64_t rows = 0;
+    size_t ws = 0;
+};
+
+int64_t packed_rows(const sgqa_seq* s, int32_t n) {
+    int64_t r = 0;
+    for (int32_t i = 0; i < n; ++i)
+        if (s[i].n_q > 0) r = std::max(r, s[i].q_offset + s[i].n_q);
+    return r;
+}
+
+IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
+    IndexPlan p;
+    const int K = c->topk_blocks;
+    p.cap = (K + 256 + 63) / 64 * 64;
+    p.rows = packed_rows(s, n);
+    int64_t total_q = 0, max_b = 0;
+    for (int32_t i = 0; i < n; ++i) {
+        total_q += s[i].n_q;
+        if (s[i].n_q > 0) max_b = std::max(max_b, (s[i].cache_len - 1) / c->block_size);
+    }
+    const int64_t max_split_lds = std::max<int64_t>(1, 16384 / K);
+    int64_t want = total_q > 0 ? (2048 + total_q - 1) / total_q : 1;
+    int64_t split = std::min<int64_t>({want, max_split_lds, std::max<int64_t>(1, max_b / 256)});
+    if (split <= 1 || max_b <= 0) {
+        p.n_split = 1;
+        p.split_blocks = 0x7FFFFFF0;
+        return p;
+    }
+    int64_t per = (max_b + split - 1) / split;
+    per = (per + 15) / 16 * 16;
+    p.split_blocks = (int)per;
+    p.n_split = (int)((max_b + per - 1) / per);
+    if (p.n_split <= 1) {
+        p.n_split = 1;
+        p.split_blocks = 0x7FFFFFF0;
+        return p;
+    }
+    const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split;
+    p.ws = align_up(parts * K * 4) * 2 + align_up(parts * 4);
+    return p;
+}
+
+AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
+    AttnPlan p;
+    p.rows = packed_rows(s, n);
+    int64_t total_q = 0;
+    for (int32_t i = 0; i < n; ++i) total_q += s[i].n_q;
+    const int64_t max_chunks =
+        ((int64_t)c->topk_blocks * c->block_size + c->block_size + 15) / 16;
+    const int64_t units = total_q * sgqa::kGroups;
+    int64_t want = units > 0 ? (1024 + units - 1) / units : 1;
+    int64_t split = std::min<int64_t>(want, std::max<int64_t>(1, max_chunks / 8));
+    if (split <= 1) {
+        p.n_split = 1;
+        p.chunks_per_split = (int)std::min<int64_t>(max_chunks + 4, 0x7FFFFFF0);
+        return p;
+    }
+    int64_t per = (max_chunks + split - 1) / split;
+    per = (per + 3) / 4 * 4;
+    p.chunks_per_split = (int)per;
+    p.n_split = (int)((max_chunks + per - 1) / per);
+    if (p.n_split <= 1) {
+        p.n_split = 1;
+        p.chunks_per_split = (int)(max_chunks + 4);
+        return p;
+    }
+    const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split * sgqa::kHeadsPerGroup;
+    p.ws = align_up(parts * sgqa::kHeadDim * 4) + align_up(parts * 2 * 4);
+    return p;
+}
+
+int check_ws(size_t need, void* ws, size_t ws_bytes) {
+    if (need == 0) return SGQA_OK;
+    if (!ws) return fail(SGQA_ERR_WORKSPACE, "workspace of %zu bytes required, ws is NULL", need);
+    if (ws_bytes < need)
+        return fail(SGQA_ERR_WORKSPACE, "workspace of %zu bytes required, %zu given", need, ws_bytes);
+    if (((uintptr_t)ws) % kAlign != 0)
+        return fail(SGQA_ERR_WORKSPACE, "workspace must be %zu-byte aligned", kAlign);
+    return SGQA_OK;
+}
+
+// Fill a launch table with sequences [first, first+count) that have queries
+// (or blocks to compress); returns the largest per-sequence extent `ext`.
+template <typename Extent>
+int64_t fill_table(sgqa::SeqTable& tab, const sgqa_seq* s, int32_t first, int32_t count,
+                   Extent ext) {
+    tab.n = 0;
+    tab.pad_ = 0;
+    int64_t mx = 0;
+    for (int32_t i = first; i < first + count; ++i) {
+        const int64_t e = ext(s[i]);
+        if (e <= 0) continue;
+        sgqa::DevSeq& d = tab.s[tab.n++];
+        d.q_offset = s[i].q_offset;
+        d.n_q = s[i].n_q;
+        d.pos0 = s[i].pos0;
+        d.kv_offset = s[i].kv_offset;
+        d.store_offset = s[i].store_offset;
+        mx = std::max(mx, e);
+    }
+    return mx;
+}
+
+// ---------------------------------------------------------------------------
+// the three steps (arguments already validated)
+// ---------------------------------------------------------------------------
+int run_compress(const sgqa_config* c, const sgqa_seq* s, int32_t n, const void* proxy_k,
+                 const float* logits, const void* ln_gamma, const void* ln_beta, void* store,
+                 hipStream_t st) {
+    sgqa::CompressArgs a;
+    a.proxy_k = (const uint16_t*)proxy_k;
+    a.logits = logits;
+    a.ln_gamma = (const uint16_t*)ln_gamma;
+    a.ln_beta = (const uint16_t*)ln_beta;
+    a.store = (uint16_t*)store;
+    a.block_size = c->block_size;
+    a.store_q8 = c->store_q8;
+    a.eps = c->eps_ln;
+    a.rope_base = c->rope_base;
+    const int B = c->block_size;
+    for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
+        const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
+        sgqa::SeqTable tab;
+        const int64_t mx = fill_table(tab, s, first, cnt, [B](const sgqa_seq& q) {
+            return q.cache_len / B - q.pos0 / B;
+        });
+        if (tab.n == 0) continue;
+        hipError_t e = sgqa::launch_compress(tab, mx, a, st);
+        if (e != hipSuccess) return hip_fail(e, "compress launch");
+    }
+    return SGQA_OK;
+}
+
+int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPlan& p,
+              const void* q_idx, const float* w, const void* rms_gamma, const void* store,
+              int32_t* sel, float* sel_scores, void* q_hat_out, void* ws, hipStream_t st) {
+    sgqa::IndexArgs a;
+    a.q_idx = (const uint16_t*)q_idx;
+    a.w = w;
+    a.rms_gamma = (const uint16_t*)rms_gamma;
+    a.store = (const uint16_t*)store;
+    a.sel = sel;
+    a.sel_scores = sel_scores;
+    a.q_hat_out = (uint16_t*)q_hat_out;
+    a.block_size = c->block_size;
+    a.topk = c->topk_blocks;
+    a.cap = p.cap;
+    a.n_split = p.n_split;
+    a.split_blocks = p.split_blocks;
+    a.eps = c->eps_rms;
+    a.rope_base = c->rope_base;
+    a.part_key = nullptr;
+    a.part_idx = nullptr;
+    a.part_cnt = nullptr;
+    if (p.n_split > 1) {
+        const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split;
+        char* base = (char*)ws;
+        a.part_key = (uint32_t*)base;
+        a.part_idx = (int32_t*)(base + align_up(parts * c->topk_blocks * 4));
+        a.part_cnt = (int32_t*)(base + 2 * align_up(parts * c->topk_blocks * 4));
+    }
+    for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
+        const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
+        sgqa::SeqTable tab;
+        const int64_t mx = fill_table(tab, s, first, cnt, [](const sgqa_seq& q) { return q.n_q; });
+        if (tab.n == 0) continue;
+        hipError_t e = sgqa::launch_index_topk(tab, mx, a, st);
+        if (e != hipSuccess) return hip_fail(e, "index_topk launch");
+        if (p.n_split > 1) {
+            sgqa::IndexMergeArgs ma;
+            ma.part_key = a.part_key;
+            ma.part_idx = a.part_idx;
+            ma.part_cnt = a.part_cnt;
+            ma.sel = sel;
+            ma.sel_scores = sel_scores;
+            ma.topk = c->topk_blocks;
+            ma.n_split = p.n_split;
+            e = sgqa::launch_index_merge(tab, mx, ma, st);
+            if (e != hipSuccess) return hip_fail(e, "index_merge launch");
+        }
+    }
+    return SGQA_OK;
+}
+
+int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan& p,
+             const void* q, const void* k_cache, const void* v_cache, const int32_t* sel,
+             void* out, float* lse, void* ws, hipStream_t st) {
+    sgqa::AttnArgs a;
+    a.q = (const uint16_t*)q;
+    a.k = (const uint16_t*)k_cache;
+    a.v = (const uint16_t*)v_cache;
+    a.sel = sel;
+    a.out = (uint16_t*)out;
+    a.lse = lse;
+    a.block_size = c->block_size;
+    a.topk = c->topk_blocks;
+    a.n_split = p.n_split;
+    a.chunks_per_split = p.chunks_per_split;
+    a.scale_log2 = c->softmax_scale * 1.4426950408889634f;
+    a.part_o = nullptr;
+    a.part_ml = nullptr;
+    if (p.n_split > 1) {
+        const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split * sgqa::kHeadsPerGroup;
+        a.part_o = (float*)ws;
+        a.part_ml = (float*)((char*)ws + align_up(parts * sgqa::kHeadDim * 4));
+    }
+    for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
+        const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
+        sgqa::SeqTable tab;
+        const int64_t mx = fill_table(tab, s, first, cnt, [](const sgqa_seq& qq) { return qq.n_q; });
+        if (tab.n == 0) continue;
+        hipError_t e = sgqa::launch_sparse_attn(tab, mx, a, st);
+        if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+        if (p.n_split > 1) {
+            sgqa::AttnMergeArgs ma;
+            ma.part_o = a.part_o;
+            ma.part_ml = a.part_ml;
+            ma.out = (uint16_t*)out;
+            ma.lse = lse;
+            ma.n_split = p.n_split;
+            e = sgqa::launch_attn_merge(tab, mx, ma, st);
+            if (e != hipSuccess) return hip_fail(e, "attn_merge launch");
+        }
+    }
+    return SGQA_OK;
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// extern "C" entry points
+// ---------------------------------------------------------------------------
+extern "C" {
+
+int32_t sgqa_abi_version(void) { return 1; }
+
+const char* sgqa_last_error(void) { return g_last_error.c_str(); }
+
+const char* sgqa_status_string(int status) {
+    switch (status) {
+        case SGQA_OK: return "SGQA_OK";
+        case SGQA_ERR_NULL: return "SGQA_ERR_NULL";
+        case SGQA_ERR_CONFIG: return "SGQA_ERR_CONFIG";
+        case SGQA_ERR_SHAPE: return "SGQA_ERR_SHAPE";
+        case SGQA_ERR_CAUSAL: return "SGQA_ERR_CAUSAL";
+        case SGQA_ERR_CAPACITY: return "SGQA_ERR_CAPACITY";
+        case SGQA_ERR_WORKSPACE: return "SGQA_ERR_WORKSPACE";
+        case SGQA_ERR_UNSUPPORTED: return "SGQA_ERR_UNSUPPORTED";
+        case SGQA_ERR_HIP: return "SGQA_ERR_HIP";
+        default: return "SGQA_UNKNOWN_STATUS";
+    }
+}
+
+size_t sgqa_workspace_size(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                           int32_t op) {
+    if (check_config(cfg) != SGQA_OK || check_seqs(cfg, seqs, n_seqs) != SGQA_OK) return 0;
+    switch (op) {
+        case SGQA_OP_COMPRESS: return 0;
+        case SGQA_OP_INDEX_TOPK: return plan_index(cfg, seqs, n_seqs).ws;
+        case SGQA_OP_SPARSE_ATTN: return plan_attn(cfg, seqs, n_seqs).ws;
+        case SGQA_OP_FORWARD:
+            return std::max(plan_index(cfg, seqs, n_seqs).ws, plan_attn(cfg, seqs, n_seqs).ws);
+        default: fail(SGQA_ERR_CONFIG, "unknown op %d", op); return 0;
+    }
+}
+
+int sgqa_compress(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                  const void* proxy_k, const float* comp_logits, const void* ln_gamma,
+                  const void* ln_beta, void* store, void* ws, size_t ws_bytes,
+                  void* hip_stream) {
+    (void)ws;
+    (void)ws_bytes;
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!proxy_k || !comp_logits || !store)
+        return fail(SGQA_ERR_NULL, "proxy_k, comp_logits and store are required");
+    return run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store,
+                        (hipStream_t)hip_stream);
+}
+
+int sgqa_index_topk(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                    const void* q_idx, const float* w, const void* rms_gamma,
+                    const void* store, int32_t* sel, float* sel_scores, void* q_hat_out,
+                    void* ws, size_t ws_bytes, void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!q_idx || !w || !store || !sel)
+        return fail(SGQA_ERR_NULL, "q_idx, w, store and sel are required");
+    const IndexPlan p = plan_index(cfg, seqs, n_seqs);
+    if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
+    return run_index(cfg, seqs, n_seqs, p, q_idx, w, rms_gamma, store, sel, sel_scores,
+                     q_hat_out, ws, (hipStream_t)hip_stream);
+}
+
+int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                     const void* q, const void* k_cache, const void* v_cache,
+                     const int32_t* sel, void* out, float* lse, void* ws, size_t ws_bytes,
+                     void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!q || !k_cache || !v_cache || !sel || !out)
+        return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel and out are required");
+    const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
+    if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
+    return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, sel, out, lse, ws,
+                    (hipStream_t)hip_stream);
+}
+
+int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                 const void* proxy_k, const float* comp_logits, const void* ln_gamma,
+                 const void* ln_beta, void* store, const void* q_idx, const float* w,
+                 const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
+                 const void* k_cache, const void* v_cache, void* out, float* lse, void* ws,
+                 size_t ws_bytes, void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!proxy_k || !comp_logits || !store || !q_idx || !w || !sel || !q || !k_cache ||
+        !v_cache || !out)
+        return fail(SGQA_ERR_NULL,
+                    "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache and out "
+                    "are required");
+    const IndexPlan ip = plan_index(cfg, seqs, n_seqs);
+    const AttnPlan ap = plan_attn(cfg, seqs, n_seqs);
+    if ((rc = check_ws(std::max(ip.ws, ap.ws), ws, ws_bytes))) return rc;
+    hipStream_t st = (hipStream_t)hip_stream;
+    if ((rc = run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, st)))
+        return rc;
+    if ((rc = run_index(cfg, seqs, n_seqs, ip, q_idx, w, rms_gamma, store, sel, sel_scores,
+                        nullptr, ws, st)))
+        return rc;
+    return run_attn(cfg, seqs, n_seqs, ap, q, k_cache, v_cache, sel, out, lse, ws, st);
+}
+
+}  // extern "C"

@@ -1,0 +1,225 @@
+// Internal declarations shared by the HIP kernels and the host dispatch of
+// libsgqa.so.  Nothing here is part of the public ABI (include/sgqa.h).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace sgqa {
+
+// ---------------------------------------------------------------------------
+// compiled shape set
+// ---------------------------------------------------------------------------
+constexpr int kHeads = 64;        // query heads
+constexpr int kGroups = 4;        // KV groups (16 heads each)
+constexpr int kHeadsPerGroup = 16;
+constexpr int kHeadDim = 192;     // main Q/K/V head dim
+constexpr int kIdxHeads = 4;      // indexer heads per group
+constexpr int kIdxDim = 128;      // indexer dim
+constexpr int kRopeDim = 32;      // indexer rotary span
+constexpr int kMaxTopK = 4096;
+constexpr int kMaxSeqsPerLaunch = 64;
+
+// Per-sequence descriptor as the kernels see it (passed by value in the
+// kernel arguments, up to kMaxSeqsPerLaunch per launch).
+struct DevSeq {
+    int64_t q_offset;
+    int64_t n_q;
+    int64_t pos0;
+    int64_t kv_offset;
+    int64_t store_offset;
+};
+
+struct SeqTable {
+    int32_t n;
+    int32_t pad_;
+    DevSeq s[kMaxSeqsPerLaunch];
+};
+
+// ---------------------------------------------------------------------------
+// launch parameter blocks (host-chosen, passed by value)
+// ---------------------------------------------------------------------------
+struct CompressArgs {
+    const uint16_t* proxy_k;
+    const float* logits;
+    const uint16_t* ln_gamma;  // may be null
+    const uint16_t* ln_beta;   // may be null
+    uint16_t* store;
+    int32_t block_size;
+    int32_t store_q8;
+    float eps;
+    float rope_base;
+};
+
+struct IndexArgs {
+    const uint16_t* q_idx;
+    const float* w;
+    const uint16_t* rms_gamma;  // may be null
+    const uint16_t* store;
+    int32_t* sel;               // final output (n_split == 1) or null
+    float* sel_scores;          // may be null
+    uint16_t* q_hat_out;        // may be null
+    uint32_t* part_key;         // split mode: [rows, G, n_split, K]
+    int32_t* part_idx;
+    int32_t* part_cnt;          // [rows, G, n_split]
+    int32_t block_size;
+    int32_t topk;               // K
+    int32_t cap;                // per-row LDS buffer capacity C
+    int32_t n_split;
+    int32_t split_blocks;       // candidate blocks per split (multiple of 16)
+    float eps;
+    float rope_base;
+};
+
+struct IndexMergeArgs {
+    const uint32_t* part_key;
+    const int32_t* part_idx;
+    const int32_t* part_cnt;
+    int32_t* sel;
+    float* sel_scores;
+    int32_t topk;
+    int32_t n_split;
+};
+
+struct AttnArgs {
+    const uint16_t* q;
+    const uint16_t* k;
+    const uint16_t* v;
+    const int32_t* sel;
+    uint16_t* out;
+    float* lse;            // may be null
+    float* part_o;         // split mode: [rows, G, n_split, 16, 192]
+    float* part_ml;        // split mode: [rows, G, n_split, 16, 2]
+    int32_t block_size;
+    int32_t topk;
+    int32_t n_split;
+    int32_t chunks_per_split;  // 16-token chunks per split
+    float scale_log2;          // softmax_scale * log2(e)
+};
+
+struct AttnMergeArgs {
+    const float* part_o;
+    const float* part_ml;
+    uint16_t* out;
+    float* lse;
+    int32_t n_split;
+};
+
+// ---------------------------------------------------------------------------
+// launchers (defined next to their kernels); return hipError_t of the launch
+// ---------------------------------------------------------------------------
+hipError_t launch_compress(const SeqTable& seqs, int64_t max_blocks, const CompressArgs& a,
+                           hipStream_t stream);
+size_t index_lds_bytes(int cap);
+hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
+                             hipStream_t stream);
+hipError_t launch_index_merge(const SeqTable& seqs, int64_t max_nq, const IndexMergeArgs& a,
+                              hipStream_t stream);
+hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
+                              hipStream_t stream);
+hipError_t launch_attn_merge(const SeqTable& seqs, int64_t max_nq, const AttnMergeArgs& a,
+                             hipStream_t stream);
+
+}  // namespace sgqa
+
+// ---------------------------------------------------------------------------
+// device helpers
+// ---------------------------------------------------------------------------
+#if defined(__HIPCC__)
+namespace sgqa {
+namespace dev {
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8;
+typedef __attribute__((ext_vector_type(4))) short i16x4;
+typedef __attribute__((ext_vector_type(4))) float f32x4;
+
+__device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// fp32 -> bf16 bits, round to nearest, ties to even (inputs are finite).
+__device__ __forceinline__ uint32_t f32_to_bf16(float f) {
+    uint32_t u = __float_as_uint(f);
+    u += 0x7FFFu + ((u >> 16) & 1u);
+    return u >> 16;
+}
+
+// bf16 value -> nearest OCP E4M3FN value (ties to even, saturating at 448),
+// returned as bf16 bits.  Exact: scaling by powers of two and rint.
+__device__ __forceinline__ uint32_t bf16_to_e4m3_as_bf16(uint32_t b) {
+    float x = bf16_to_f32(b);
+    float a = fabsf(x);
+    float r;
+    if (a < 0.015625f) {                         // below 2^-6: quantum 2^-9
+        r = rintf(a * 512.0f) * (1.0f / 512.0f);
+    } else {
+        int e = (int)((__float_as_uint(a) >> 23) & 0xFF) - 127;   // a in [2^e, 2^(e+1))
+        float up = __uint_as_float((uint32_t)(127 + 3 - e) << 23);   // 2^(3-e)
+        float dn = __uint_as_float((uint32_t)(127 - 3 + e) << 23);   // 2^(e-3)
+        r = rintf(a * up) * dn;
+    }
+    r = fminf(r, 448.0f);
+    r = copysignf(r, x);
+    return __float_as_uint(r) >> 16;             // exactly representable in bf16
+}
+
+// Order-preserving map of a score to uint32 (larger score -> larger key);
+// -0.0 is first folded into +0.0 so the two compare equal.
+__device__ __forceinline__ uint32_t score_key(float s) {
+    uint32_t u = __float_as_uint(s);
+    if (u == 0x80000000u) u = 0u;
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+    uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+    return __uint_as_float(u);
+}
+
+// number of set bits of `mask` at lanes below this one
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo((uint32_t)mask, 0u));
+}
+
+// make this wave's LDS writes visible to its other lanes
+__device__ __forceinline__ void wave_lds_sync() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+    return v;
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x32(bf16x8 a, bf16x8 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
+    return __builtin_amdgcn_mfma_f32_16x16x16bf16_1k(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
+__device__ __forceinline__ i16x4 as_i16x4(uint2 v) { return __builtin_bit_cast(i16x4, v); }
+
+// rotary frequency of pair j: base^(-2j/32), in fp64
+__device__ __forceinline__ double rope_theta(int j, float base) {
+    return pow((double)base, -2.0 * (double)j / (double)kRopeDim);
+}
+
+// cos / sin of the rotary angle pos * theta, evaluated in fp64 (an fp32
+// product would lose ~0.06 rad near position 1e6)
+__device__ __forceinline__ void rope_cos_sin(int64_t pos, double theta, float* c, float* s) {
+    double sd, cd;
+    sincos((double)pos * theta, &sd, &cd);
+    *c = (float)cd;
+    *s = (float)sd;
+}
+
+}  // namespace dev
+}  // namespace sgqa
+#endif

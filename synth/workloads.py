@@ -1,0 +1,206 @@
+"""The synthetic workloads: shapes, sequence layout and seeded contents.
+
+Input infrastructure shared by the tests, the smoke check and the benchmark.
+It holds none of the method's arithmetic: it only lays sequences out in the
+caches and fills tensors from the counter-based generator, on the device
+(:mod:`synth.device`) or, for any slice the CPU oracle needs, on the host.
+
+Workloads (one attention layer each, 64 heads / 4 KV groups / head_dim 192,
+indexer 4 heads x 128 per group with a 32-dim rotary span, seed 0):
+
+=====================  ==========================================  ======  =====
+name                   queries / cache                             B       K
+=====================  ==========================================  ======  =====
+tiny_prefill_256       prefill N=256                               8       16
+prefill_8k             prefill N=8,192                             8       512
+prefill_64k            prefill N=65,536                            8       512
+prefill_64k_b1         prefill N=65,536 (ablation)                 1       2,048
+decode_64x256k         64 sequences x 1 new token, lengths U[131072,262144],
+                       262,144-token allocation each               8       512
+chunk_1m               8,192 queries at 1,040,384..1,048,575 over a
+                       1,048,576-token cache                       8       512
+=====================  ==========================================  ======  =====
+
+Distributions: main Q and K bf16 unit normal then RMS-normalised per
+(token, head / group) row; V, indexer queries and proxy keys bf16 unit
+normal; compression logits fp32 unit normal; indexer weights fp32 normal with
+standard deviation 1/sqrt(512).  All i.i.d.; the draws are Irwin-Hall(4)
+(bounded tails, see :mod:`synth`).
+"""
+from __future__ import annotations
+
+from dataclasses import dataclass, field
+from typing import Dict, List
+
+import numpy as np
+
+from . import (C_W, TID_K, TID_LOGITS, TID_PROXY, TID_Q, TID_QIDX, TID_V, TID_W,
+               normal_bf16_bits, normal_f32, rms_rows_bf16_bits, seq_lengths)
+
+H, G, D, HI, DI = 64, 4, 192, 4, 128
+
+
+@dataclass
+class SeqLayout:
+    q_offset: int
+    n_q: int
+    pos0: int
+    kv_offset: int
+    kv_capacity: int
+    store_offset: int
+    store_capacity: int
+
+    @property
+    def cache_len(self) -> int:
+        return self.pos0 + self.n_q
+
+
+@dataclass
+class Workload:
+    name: str
+    block_size: int
+    topk: int
+    seqs: List[SeqLayout]
+    # store rows written before the measured step: (pos0=0, n_q=pos0) per seq
+    prebuilt: bool = False
+    store_q8: bool = True
+    seed: int = 0
+    notes: str = ""
+
+    @property
+    def n_q_total(self) -> int:
+        return sum(s.n_q for s in self.seqs)
+
+    @property
+    def q_rows(self) -> int:
+        return max(s.q_offset + s.n_q for s in self.seqs)
+
+    @property
+    def kv_rows(self) -> int:
+        return max(s.kv_offset + s.kv_capacity for s in self.seqs)
+
+    @property
+    def store_rows(self) -> int:
+        return max(s.store_offset + s.store_capacity for s in self.seqs)
+
+
+def _prefill(name, n, B, K, pos0=0, **kw) -> Workload:
+    T = pos0 + n
+    return Workload(name, B, K, [SeqLayout(0, n, pos0, 0, T, 0, T // B)], prebuilt=pos0 > 0, **kw)
+
+
+def _decode(name, n_seqs=64, lo=131072, hi=262144, cap=262144, B=8, K=512, seed=0) -> Workload:
+    L = seq_lengths(seed, n_seqs, lo, hi)
+    seqs = [SeqLayout(i, 1, int(L[i]) - 1, i * cap, cap, i * (cap // B), cap // B)
+            for i in range(n_seqs)]
+    return Workload(name, B, K, seqs, prebuilt=True, seed=seed)
+
+
+def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
+    if name == "tiny_prefill_256":
+        w = _prefill(name, 256, 8, 16)
+    elif name == "prefill_8k":
+        w = _prefill(name, 8192, 8, 512)
+    elif name == "prefill_64k":
+        w = _prefill(name, 65536, 8, 512)
+    elif name == "prefill_64k_b1":
+        w = _prefill(name, 65536, 1, 2048)
+    elif name == "decode_64x256k":
+        w = _decode(name, seed=seed)
+    elif name == "chunk_1m":
+        w = _prefill(name, 8192, 8, 512, pos0=1_040_384)
+    elif name.startswith("prefill_"):          # prefill_<n>[_b<B>_k<K>] for tests
+        parts = name.split("_")
+        n = int(parts[1])
+        B = int(parts[2][1:]) if len(parts) > 2 else 8
+        K = int(parts[3][1:]) if len(parts) > 3 else 512
+        w = _prefill(name, n, B, K)
+    else:
+        raise KeyError(name)
+    w.seed = seed
+    w.store_q8 = store_q8
+    return w
+
+
+NAMES = ["tiny_prefill_256", "prefill_8k", "prefill_64k", "prefill_64k_b1", "decode_64x256k",
+         "chunk_1m"]
+
+
+# ---------------------------------------------------------------------------
+# device tensors
+# ---------------------------------------------------------------------------
+
+@dataclass
+class DeviceInputs:
+    wl: Workload
+    t: Dict[str, "object"] = field(default_factory=dict)
+
+    def __getitem__(self, k):
+        return self.t[k]
+
+
+def device_inputs(wl: Workload, device="cuda") -> DeviceInputs:
+    """Allocate and fill every tensor of the workload on the device; outputs
+    (store, sel, sel_scores, q_hat, out, lse) are allocated and zero-filled."""
+    import torch
+
+    from . import device as dv
+
+    Nq, R, S = wl.q_rows, wl.kv_rows, wl.store_rows
+    bf, f32 = torch.bfloat16, torch.float32
+    t = {}
+    t["q"] = dv.fill_rms_rows(torch.empty((Nq, H, D), dtype=bf, device=device), wl.seed, TID_Q)
+    t["k"] = dv.fill_rms_rows(torch.empty((R, G, D), dtype=bf, device=device), wl.seed, TID_K)
+    t["v"] = dv.fill_bf16(torch.empty((R, G, D), dtype=bf, device=device), wl.seed, TID_V)
+    t["q_idx"] = dv.fill_bf16(torch.empty((Nq, G, HI, DI), dtype=bf, device=device), wl.seed, TID_QIDX)
+    t["w"] = dv.fill_f32(torch.empty((Nq, G, HI), dtype=f32, device=device), wl.seed, TID_W, scale=C_W)
+    t["proxy_k"] = dv.fill_bf16(torch.empty((R, DI), dtype=bf, device=device), wl.seed, TID_PROXY)
+    t["logits"] = dv.fill_f32(torch.empty((R, DI), dtype=f32, device=device), wl.seed, TID_LOGITS)
+    t["store"] = torch.zeros((S, DI), dtype=bf, device=device)
+    t["sel"] = torch.zeros((Nq, G, wl.topk), dtype=torch.int32, device=device)
+    t["sel_scores"] = torch.zeros((Nq, G, wl.topk), dtype=f32, device=device)
+    t["q_hat"] = torch.zeros((Nq, G, HI, DI), dtype=bf, device=device)
+    t["out"] = torch.zeros((Nq, H, D), dtype=bf, device=device)
+    t["lse"] = torch.zeros((Nq, H), dtype=f32, device=device)
+    return DeviceInputs(wl, t)
+
+
+# ---------------------------------------------------------------------------
+# host slices for the oracle (regenerated, never copied from the device)
+# ---------------------------------------------------------------------------
+
+def host_q(wl: Workload, qrows) -> np.ndarray:
+    qrows = np.asarray(qrows, dtype=np.int64).reshape(-1)
+    rows = (qrows[:, None] * H + np.arange(H)[None, :]).reshape(-1)
+    return rms_rows_bf16_bits(wl.seed, TID_Q, rows, D).reshape(-1, H, D)
+
+
+def host_k(wl: Workload, kv_rows) -> np.ndarray:
+    kv_rows = np.asarray(kv_rows, dtype=np.int64).reshape(-1)
+    rows = (kv_rows[:, None] * G + np.arange(G)[None, :]).reshape(-1)
+    return rms_rows_bf16_bits(wl.seed, TID_K, rows, D).reshape(-1, G, D)
+
+
+def _flat(rows, width):
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    return (rows[:, None] * width + np.arange(width)[None, :]).astype(np.uint64)
+
+
+def host_v(wl: Workload, kv_rows) -> np.ndarray:
+    return normal_bf16_bits(wl.seed, TID_V, _flat(kv_rows, G * D)).reshape(-1, G, D)
+
+
+def host_q_idx(wl: Workload, qrows) -> np.ndarray:
+    return normal_bf16_bits(wl.seed, TID_QIDX, _flat(qrows, G * HI * DI)).reshape(-1, G, HI, DI)
+
+
+def host_w(wl: Workload, qrows) -> np.ndarray:
+    return normal_f32(wl.seed, TID_W, _flat(qrows, G * HI), C_W).reshape(-1, G, HI)
+
+
+def host_proxy(wl: Workload, kv_rows) -> np.ndarray:
+    return normal_bf16_bits(wl.seed, TID_PROXY, _flat(kv_rows, DI)).reshape(-1, DI)
+
+
+def host_logits(wl: Workload, kv_rows) -> np.ndarray:
+    return normal_f32(wl.seed, TID_LOGITS, _flat(kv_rows, DI)).reshape(-1, DI)

@@ -1,0 +1,56 @@
+"""First GPU parity checks: generator twin, the tiny prefill in full, forward
+vs the three calls, determinism."""
+import numpy as np
+import pytest
+import torch
+
+import synth
+from synth import workloads as W
+
+from .gpu_checks import Checker, log, prepare, run_steps
+
+pytestmark = pytest.mark.gpu
+
+
+def test_device_generator_matches_host():
+    from synth import device as dv
+    n = 1 << 16
+    for tid, idx0 in [(synth.TID_V, 0), (synth.TID_QIDX, 12345), (synth.TID_V, (1 << 34) + 7)]:
+        t = dv.fill_bf16(torch.empty(n, dtype=torch.bfloat16, device="cuda"), 0, tid, idx0)
+        host = synth.normal_bf16_bits(0, tid, np.arange(idx0, idx0 + n, dtype=np.uint64))
+        assert np.array_equal(t.cpu().view(torch.int16).numpy().view(np.uint16), host)
+    f = dv.fill_f32(torch.empty(n, dtype=torch.float32, device="cuda"), 3, synth.TID_W, 99, synth.C_W)
+    assert np.array_equal(f.cpu().numpy(), synth.normal_f32(3, synth.TID_W, np.arange(99, 99 + n, dtype=np.uint64), synth.C_W))
+    r = dv.fill_rms_rows(torch.empty((512, 192), dtype=torch.bfloat16, device="cuda"), 0, synth.TID_K, 1000)
+    host = synth.rms_rows_bf16_bits(0, synth.TID_K, np.arange(1000, 1512), 192)
+    assert np.array_equal(r.cpu().view(torch.int16).numpy().view(np.uint16), host)
+
+
+def test_tiny_prefill_all_rows():
+    wl = W.make("tiny_prefill_256")
+    log("case", wl.name)
+    di, cfg = prepare(wl)
+    run_steps(wl, di, cfg)
+    ck = Checker(wl, di, cfg)
+    s = wl.seqs[0]
+    stored, exact = ck.oracle_store(s, s.cache_len // wl.block_size)
+    ck.check_store(s, stored, exact)
+    ck.check_seq(0, np.arange(s.n_q), store_exact=(stored, exact))
+    st = ck.finish()
+    log(st)
+    assert st["rows"] == 256
+
+
+def test_forward_equals_steps_and_is_deterministic():
+    wl = W.make("tiny_prefill_256")
+    di, cfg = prepare(wl)
+    run_steps(wl, di, cfg)
+    a = {k: di[k].clone() for k in ("store", "sel", "sel_scores", "out", "lse")}
+    for k in ("store", "sel", "sel_scores", "out", "lse"):
+        di[k].zero_()
+    run_steps(wl, di, cfg, use_forward=True)
+    for k, v in a.items():
+        assert torch.equal(di[k], v), k
+    run_steps(wl, di, cfg, use_forward=True)
+    for k, v in a.items():
+        assert torch.equal(di[k], v), k
