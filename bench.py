@@ -1,0 +1,271 @@
+#!/usr/bin/env python3
+"""Benchmark of the sparse GQA hot path on one MI355X.
+
+One step = one ``sgqa_forward`` (block merging -> indexer scores + causal
+top-k -> sparse GQA attention) of one attention layer over one batch of
+seeded synthetic input already resident in HBM.  Default workload: the
+single-layer prefill of 8,192 tokens (64 heads / 4 KV groups / head_dim 192,
+indexer 4 x 128 per group, B=8, k = 512 blocks = 4,096 tokens).
+
+Prints one JSON line with whole-step throughput, the roofline of the dominant
+kernel (its per-launch time measured with HIP events on the stream it runs
+on) and the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "sparse-GQA prefill tokens/s + decode queries/s on 1 GPU; % of HBM/MFMA peak"
+PEAK_BF16_FLOPS = 2.5e15      # MI355X dense bf16 MFMA
+PEAK_HBM_BPS = 8.0e12         # MI355X HBM3E
+H, G, D, HI, DI = 64, 4, 192, 4, 128
+
+
+# ---------------------------------------------------------------------------
+# algorithmic work of one step (what the method must compute / move)
+# ---------------------------------------------------------------------------
+
+def work_model(wl) -> dict:
+    B, K = wl.block_size, wl.topk
+    attn_pairs = 0          # sum over (t, g) of |U_t,g|
+    idx_pairs = 0           # sum over t of b(t) (per group)
+    comp_blocks = 0
+    store_bytes = 0
+    for s in wl.seqs:
+        t = np.arange(s.pos0, s.pos0 + s.n_q, dtype=np.int64)
+        b = t // B
+        u = np.minimum(b, K) * B + (t - b * B) + 1
+        attn_pairs += int(u.sum()) * G
+        idx_pairs += int(b.sum())
+        store_bytes += int(b.sum()) * DI * 2
+        comp_blocks += s.cache_len // B - s.pos0 // B
+    return {
+        "attn_flops": attn_pairs * (H // G) * 4 * D,        # QK^T + PV, 2 flop per MAC
+        "attn_gather_bytes": attn_pairs * 2 * D * 2,          # K and V rows, bf16
+        "index_flops": idx_pairs * G * HI * 2 * DI,
+        "index_store_bytes": store_bytes,                     # store read once per query
+        "compress_bytes": comp_blocks * (B * (DI * 2 + DI * 4) + DI * 2),
+        "queries": sum(s.n_q for s in wl.seqs),
+    }
+
+
+# ---------------------------------------------------------------------------
+# CPU oracle baseline on a bounded sample
+# ---------------------------------------------------------------------------
+
+def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
+    """The oracle, as written, on a bounded sample of the step: the merge of up
+    to 2,048 of the step's blocks plus uniformly drawn query rows through
+    scoring, top-k and attention until ``budget_s`` is spent, scaled to the
+    whole step by block and query counts."""
+    from oracle import numerics as nu
+    from oracle import sgqa as O
+    from synth import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:  # pragma: no cover
+        cores = 1
+    cfg = O.Config(block_size=wl.block_size, topk_blocks=wl.topk, store_q8=wl.store_q8)
+    rng = np.random.default_rng(0)
+    B = wl.block_size
+    total_q = sum(x.n_q for x in wl.seqs)
+    step_blocks = sum(x.cache_len // B - x.pos0 // B for x in wl.seqs)
+
+    def store_prefix(s, n_blocks):
+        rows = s.kv_offset + np.arange(B * n_blocks)
+        return O.compress(W.host_proxy(wl, rows), W.host_logits(wl, rows), np.arange(n_blocks), cfg)[0]
+
+    # (1) merge: the first min(step, 2048) blocks the step compresses
+    s0 = next(x for x in wl.seqs if x.cache_len // B > x.pos0 // B) if step_blocks else wl.seqs[0]
+    first, nb = s0.pos0 // B, min(max(s0.cache_len // B - s0.pos0 // B, 0), 2048)
+    rows = s0.kv_offset + np.arange(B * first, B * (first + nb))
+    kp = np.zeros((B * (first + nb), DI), dtype=np.uint16)
+    lg = np.zeros((B * (first + nb), DI), dtype=np.float32)
+    kp[B * first:] = W.host_proxy(wl, rows)
+    lg[B * first:] = W.host_logits(wl, rows)
+    t0 = time.perf_counter()
+    O.compress(kp, lg, np.arange(first, first + nb), cfg)
+    t_comp = (time.perf_counter() - t0) * step_blocks / max(nb, 1)
+    # (2) query rows through steps 2-4; the store they search is the real one
+    #     up to 8,192 blocks, repeated cyclically beyond (pace only)
+    prefix = {}
+    kv_full = None
+    if wl.kv_rows * G * D <= (1 << 26):          # small caches: regenerate once
+        kv_full = (W.host_k(wl, np.arange(wl.kv_rows)), W.host_v(wl, np.arange(wl.kv_rows)))
+    n_rows, t_rows = 0, 0.0
+    while t_rows < budget_s and n_rows < total_q:
+        si = int(rng.integers(0, len(wl.seqs)))
+        s = wl.seqs[si]
+        if s.n_q == 0:
+            continue
+        if si not in prefix:
+            prefix[si] = store_prefix(s, min((s.cache_len - 1) // B, 8192))
+        qi = int(rng.integers(0, s.n_q))
+        t = s.pos0 + qi
+        b = t // B
+        st = prefix[si]
+        store = st[np.arange(b) % max(st.shape[0], 1)] if b > st.shape[0] else st[:b]
+        qrow = s.q_offset + qi
+        qi_bits, w_row, q_bits = W.host_q_idx(wl, [qrow]), W.host_w(wl, [qrow])[0], W.host_q(wl, [qrow])[0]
+        t1 = time.perf_counter()
+        qh = O.index_queries(qi_bits, [t], cfg)[0]
+        w = w_row.astype(np.float64)
+        q = nu.bf16_bits_to_f64(q_bits)
+        sels = []
+        for g in range(G):
+            sc = O.block_scores(qh[g], w[g], store)
+            sels.append(O.token_set(O.select_blocks(sc, wl.topk), t, B))
+        toks = np.unique(np.concatenate(sels))
+        t_rows += time.perf_counter() - t1
+        if kv_full is not None:
+            k_bits, v_bits = kv_full[0][s.kv_offset + toks], kv_full[1][s.kv_offset + toks]
+        else:
+            k_bits, v_bits = W.host_k(wl, s.kv_offset + toks), W.host_v(wl, s.kv_offset + toks)
+        t1 = time.perf_counter()
+        kk, vv = nu.bf16_bits_to_f64(k_bits), nu.bf16_bits_to_f64(v_bits)
+        for g in range(G):
+            u = np.searchsorted(toks, sels[g])
+            O.attend(q[16 * g:16 * g + 16], kk[u, g], vv[u, g], cfg.softmax_scale)
+        t_rows += time.perf_counter() - t1
+        n_rows += 1
+    est = t_comp + t_rows / max(n_rows, 1) * total_q
+    unit = "queries/s" if wl.name.startswith("decode") else "tokens/s"
+    return {"value": total_q / est, "unit": unit, "cores": int(cores), "kind": "oracle",
+            "sample": f"{n_rows} uniformly drawn query rows through scoring, top-k and attention "
+                      f"({t_rows:.1f} s, input regeneration excluded) plus the merge of {nb} "
+                      f"blocks, scaled to {total_q} queries and {step_blocks} blocks; "
+                      f"est. {est:.2f} s per step"}
+
+
+# ---------------------------------------------------------------------------
+# GPU timing
+# ---------------------------------------------------------------------------
+
+def event_time_ms(fn, stream, reps: int) -> float:
+    import torch
+    start = torch.cuda.Event(enable_timing=True)
+    end = torch.cuda.Event(enable_timing=True)
+    with torch.cuda.stream(stream):
+        start.record(stream)
+        for _ in range(reps):
+            fn()
+        end.record(stream)
+    end.synchronize()
+    return start.elapsed_time(end) / reps
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="prefill_8k")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=20)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU part); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+
+    import torch
+
+    import sparse_long_context_block_amd as sg
+    from synth import workloads as W
+    from tests.gpu_checks import lib_seqs, prepare
+
+    wl = W.make(args.workload)
+    print(f"[bench] workload {wl.name}: preparing inputs", file=sys.stderr, flush=True)
+    di, cfg = prepare(wl)
+    seqs = lib_seqs(wl)
+    stream = torch.cuda.current_stream()
+    ws_n = sg.workspace_size(cfg, seqs, sg.OP_FORWARD)
+    ws = torch.empty(max(ws_n, 1) + 256, dtype=torch.uint8, device="cuda")
+    ws_view = ws[(-ws.data_ptr()) % 256:][:max(ws_n, 1)]
+
+    def step():
+        sg.forward(cfg, seqs, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
+                   di["sel"], di["q"], di["k"], di["v"], di["out"], lse=di["lse"],
+                   ws=ws_view, stream=stream)
+
+    def op_compress():
+        sg.compress(cfg, seqs, di["proxy_k"], di["logits"], di["store"], stream=stream)
+
+    def op_index():
+        sg.index_topk(cfg, seqs, di["q_idx"], di["w"], di["store"], di["sel"],
+                      ws=ws_view, stream=stream)
+
+    def op_attn():
+        sg.sparse_attn(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"],
+                       lse=di["lse"], ws=ws_view, stream=stream)
+
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
+          flush=True)
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    ms_step = wall * 1e3 / args.steps
+
+    reps = args.kernel_reps
+    k_ms = {
+        "compress": event_time_ms(op_compress, stream, reps),
+        "index_topk": event_time_ms(op_index, stream, reps),
+        "sparse_attn": event_time_ms(op_attn, stream, reps),
+    }
+    print(f"[bench] per-op ms {k_ms}", file=sys.stderr, flush=True)
+
+    wm = work_model(wl)
+    decode = wl.name.startswith("decode")
+    if decode:
+        # HBM-bound: store stream + K/V gather over the step
+        bytes_alg = wm["index_store_bytes"] + wm["attn_gather_bytes"]
+        achieved = bytes_alg / (ms_step * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                "frac": achieved / (PEAK_HBM_BPS / 1e9), "traffic": None,
+                "kernel": "index_topk + sparse_attn (whole step)"}
+        value, unit = wm["queries"] / (ms_step * 1e-3), "queries/s"
+    else:
+        achieved = wm["attn_flops"] / (k_ms["sparse_attn"] * 1e-3) / 1e12
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16_FLOPS / 1e12), "traffic": None,
+                "kernel": "sparse_attn_kernel",
+                "algorithmic_flops_per_launch": wm["attn_flops"],
+                "launch_ms": k_ms["sparse_attn"]}
+        value, unit = wm["queries"] / (ms_step * 1e-3), "tokens/s"
+
+    res = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name, "queries": wm["queries"], "block_size": wl.block_size,
+                   "topk_blocks": wl.topk, "store_q8": wl.store_q8,
+                   "heads": H, "kv_groups": G, "head_dim": D},
+        "per_op_ms": k_ms,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        res["cpu_baseline"] = cpu_baseline(wl)
+    print(json.dumps(res), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -148,11 +148,21 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     return p;
 }
 
+// Queries of a sequence [0, n_dense) whose selection covers at least a
+// quarter of their candidates (floor(t/B) <= 4K) take the tiled kernel when
+// the sequence brings enough queries to fill its workgroups; the rest take
+// the gather kernel.
+int64_t dense_queries(const sgqa_config* c, const sgqa_seq& q) {
+    if (q.n_q < 64) return 0;
+    const int64_t limit = 4 * (int64_t)c->topk_blocks * c->block_size;   // t < limit
+    return std::max<int64_t>(0, std::min<int64_t>(q.n_q, limit - q.pos0));
+}
+
 AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     AttnPlan p;
     p.rows = packed_rows(s, n);
     int64_t total_q = 0;
-    for (int32_t i = 0; i < n; ++i) total_q += s[i].n_q;
+    for (int32_t i = 0; i < n; ++i) total_q += s[i].n_q - dense_queries(c, s[i]);
     const int64_t max_chunks =
         ((int64_t)c->topk_blocks * c->block_size + c->block_size + 15) / 16;
     const int64_t units = total_q * sgqa::kGroups;
@@ -314,10 +324,45 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
     }
     for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
         const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
-        sgqa::SeqTable tab;
-        const int64_t mx = fill_table(tab, s, first, cnt, [](const sgqa_seq& qq) { return qq.n_q; });
-        if (tab.n == 0) continue;
-        hipError_t e = sgqa::launch_sparse_attn(tab, mx, a, st);
+        // dense-ish leading queries -> tiled kernel
+        sgqa::SeqTable ut;
+        ut.n = 0;
+        ut.pad_ = 0;
+        int64_t umax = 0, ublk = 0;
+        sgqa::SeqTable gt;
+        gt.n = 0;
+        gt.pad_ = 0;
+        int64_t gmax = 0;
+        for (int32_t i = first; i < first + cnt; ++i) {
+            const sgqa_seq& q = s[i];
+            const int64_t nd = dense_queries(c, q);
+            if (nd > 0) {
+                sgqa::DevSeq& d = ut.s[ut.n++];
+                d.q_offset = q.q_offset;
+                d.n_q = nd;
+                d.pos0 = q.pos0;
+                d.kv_offset = q.kv_offset;
+                d.store_offset = q.store_offset;
+                umax = std::max(umax, nd);
+                ublk = std::max(ublk, (q.pos0 + nd - 1) / c->block_size);
+            }
+            if (q.n_q - nd > 0) {
+                sgqa::DevSeq& d = gt.s[gt.n++];
+                d.q_offset = q.q_offset + nd;
+                d.n_q = q.n_q - nd;
+                d.pos0 = q.pos0 + nd;
+                d.kv_offset = q.kv_offset;
+                d.store_offset = q.store_offset;
+                gmax = std::max(gmax, q.n_q - nd);
+            }
+        }
+        if (ut.n > 0) {
+            const int words = (int)(ublk / 32 + 1);
+            hipError_t e = sgqa::launch_attn_union(ut, umax, a, words, st);
+            if (e != hipSuccess) return hip_fail(e, "sparse_attn (tiled) launch");
+        }
+        if (gt.n == 0) continue;
+        hipError_t e = sgqa::launch_sparse_attn(gt, gmax, a, st);
         if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
         if (p.n_split > 1) {
             sgqa::AttnMergeArgs ma;
@@ -326,7 +371,7 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
             ma.out = (uint16_t*)out;
             ma.lse = lse;
             ma.n_split = p.n_split;
-            e = sgqa::launch_attn_merge(tab, mx, ma, st);
+            e = sgqa::launch_attn_merge(gt, gmax, ma, st);
             if (e != hipSuccess) return hip_fail(e, "attn_merge launch");
         }
     }

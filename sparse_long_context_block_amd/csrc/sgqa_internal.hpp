@@ -119,6 +119,12 @@ hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnAr
                               hipStream_t stream);
 hipError_t launch_attn_merge(const SeqTable& seqs, int64_t max_nq, const AttnMergeArgs& a,
                              hipStream_t stream);
+// tiled kernel for dense-ish selections; `words` = 32-bit words per query
+// bitmap (>= floor(t_max/B)/32 + 1 over the launch)
+constexpr int kUnionWaves = 8;
+int union_queries_per_block();
+hipError_t launch_attn_union(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a, int words,
+                             hipStream_t stream);
 
 }  // namespace sgqa
 

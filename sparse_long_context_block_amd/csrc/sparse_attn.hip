@@ -211,6 +211,233 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
     }
 }
 
+// ---------------------------------------------------------------------------
+// Tiled kernel for dense-ish selections (selected share of the candidates
+// >= 1/4, e.g. every query of an 8K prefill at k = 512 blocks).
+//
+// One workgroup = 2*NW consecutive queries x one group; wavefront w owns two
+// queries x 16 heads = 32 columns.  The workgroup walks the causal range in
+// contiguous 32-token tiles: K (row-major) and V (transposed) go through LDS
+// once and serve 32*NW (query, head) columns; a per-query bitmap of selected
+// blocks (plus the current block, positions <= t) masks the scores, so every
+// query still attends over exactly its own token set.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K tile (LDS), B = Q^T (regs)
+//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T tile (LDS), B = P^T: the
+//                 exponentiated S^T result layout, token order permuted
+//                 identically in A and B, so P never leaves registers.
+// Each lane holds one (query, head) column, so the running max / sum are
+// per lane; the max is rescaled lazily (only when it grows by more than
+// 2^8), which keeps O exact because O and the sum share the reference max.
+// ---------------------------------------------------------------------------
+typedef __attribute__((ext_vector_type(16))) float f32x16;
+
+constexpr int kTileTok = 32;
+constexpr int kKStride = kHeadDim + 8;       // bf16 per K row in LDS (400 B)
+constexpr int kVtStrideU = kTileTok + 4;     // bf16 per V^T row in LDS (72 B)
+constexpr int kChunksPerTile = kTileTok * kHeadDim / 8;   // 16-byte chunks of one K (or V) tile
+constexpr float kLazyRescale = 8.0f;         // log2 units
+
+__device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int NW, int LOG2B>
+__global__ __launch_bounds__(NW * 64) void attn_union_kernel(SeqTable seqs, AttnArgs a, int words) {
+    constexpr int TQ = 2 * NW;
+    constexpr int NT = NW * 64;
+    constexpr int kPer = (kChunksPerTile + NT - 1) / NT;
+    extern __shared__ uint32_t bitmap[];                         // [TQ][words]
+    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileTok * kKStride];
+    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][kHeadDim * kVtStrideU];
+    __shared__ int s_nsel[TQ];
+
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int g = blockIdx.x & 3;
+    const int64_t n_qt = (sq.n_q + TQ - 1) / TQ;
+    const int64_t rank = blockIdx.x >> 2;
+    if (rank >= n_qt) return;
+    const int64_t q0 = (n_qt - 1 - rank) * TQ;                  // longest tiles first
+    const int n_valid = (int)(sq.n_q - q0 < TQ ? sq.n_q - q0 : TQ);
+    const int64_t t0 = sq.pos0 + q0;
+    const int64_t t_last = t0 + n_valid - 1;
+    const int nwords = (int)((t_last >> LOG2B) >> 5) + 1;
+    const int tid = threadIdx.x;
+    const int K = a.topk;
+
+    // ---- per-query bitmaps of the selected blocks and the current block ----
+    for (int i = tid; i < TQ * nwords; i += NT) bitmap[(i / nwords) * words + i % nwords] = 0u;
+    if (tid < TQ) s_nsel[tid] = K;
+    __syncthreads();
+    const int32_t* selbase = a.sel + ((sq.q_offset + q0) * kGroups + g) * (int64_t)K;
+    for (int i = tid; i < n_valid * K; i += NT) {
+        const int q = i / K, j = i - q * K;
+        if (selbase[(int64_t)q * kGroups * K + j] < 0) atomicMin(&s_nsel[q], j);
+    }
+    __syncthreads();
+    for (int i = tid; i < n_valid * K; i += NT) {
+        const int q = i / K, j = i - q * K;
+        if (j >= s_nsel[q]) continue;
+        const int32_t v = selbase[(int64_t)q * kGroups * K + j];
+        const int64_t nb = (t0 + q) >> LOG2B;
+        if (v >= 0 && v < nb) atomicOr(&bitmap[q * words + (v >> 5)], 1u << (v & 31));
+    }
+    if (tid < n_valid) {
+        const int64_t cb = (t0 + tid) >> LOG2B;
+        atomicOr(&bitmap[tid * words + (int)(cb >> 5)], 1u << (int)(cb & 31));
+    }
+
+    // ---- this lane's column: query qw (2 per wave), head ----
+    const int wave = tid >> 6, lane = tid & 63, hgrp = lane >> 5, col = lane & 31;
+    const int qw = 2 * wave + (col >> 4);
+    const int head = col & 15;
+    const bool q_ok = qw < n_valid;
+    const int64_t tq = t0 + qw;
+    const int64_t qrow = sq.q_offset + q0 + (q_ok ? qw : 0);
+    bf16x8 qf[12];
+    {
+        const uint16_t* qp = a.q + (qrow * kHeads + g * kHeadsPerGroup + head) * kHeadDim + 8 * hgrp;
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) qf[kk] = as_bf16x8(*(const uint4*)(qp + 16 * kk));
+    }
+    const uint32_t* mybits = bitmap + (q_ok ? qw : 0) * words;
+
+    f32x16 o[6];
+#pragma unroll
+    for (int dt = 0; dt < 6; ++dt)
+#pragma unroll
+        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
+    float m_use = -INFINITY, lsum = 0.f;
+    const float sl2 = a.scale_log2;
+
+    // ---- cooperative tile loads ----
+    constexpr int64_t kRowStride = (int64_t)kGroups * kHeadDim;
+    const uint16_t* kb = a.k + (sq.kv_offset * kGroups + g) * kHeadDim;
+    const uint16_t* vb = a.v + (sq.kv_offset * kGroups + g) * kHeadDim;
+    uint4 kreg[kPer], vreg[kPer];
+    auto gload = [&](int tile) {
+#pragma unroll
+        for (int p = 0; p < kPer; ++p) {
+            const int c = tid + p * NT;
+            if (c < kChunksPerTile) {
+                const int tok = c / 24, d8 = (c - tok * 24) * 8;
+                int64_t pos = (int64_t)tile * kTileTok + tok;
+                pos = pos > t_last ? t_last : pos;
+                kreg[p] = *(const uint4*)(kb + pos * kRowStride + d8);
+                vreg[p] = *(const uint4*)(vb + pos * kRowStride + d8);
+            }
+        }
+    };
+    auto lstore = [&](int buf) {
+#pragma unroll
+        for (int p = 0; p < kPer; ++p) {
+            const int c = tid + p * NT;
+            if (c < kChunksPerTile) {
+                const int tok = c / 24, d8 = (c - tok * 24) * 8;
+                *(uint4*)(&k_lds[buf][tok * kKStride + d8]) = kreg[p];
+                const uint32_t w4[4] = {vreg[p].x, vreg[p].y, vreg[p].z, vreg[p].w};
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    vt_lds[buf][(d8 + 2 * e) * kVtStrideU + tok] = (uint16_t)(w4[e] & 0xFFFFu);
+                    vt_lds[buf][(d8 + 2 * e + 1) * kVtStrideU + tok] = (uint16_t)(w4[e] >> 16);
+                }
+            }
+        }
+    };
+
+    const int n_tiles = (int)(t_last / kTileTok) + 1;
+    gload(0);
+    lstore(0);
+    __syncthreads();
+    for (int i = 0; i < n_tiles; ++i) {
+        const int buf = i & 1;
+        if (i + 1 < n_tiles) gload(i + 1);
+
+        // S^T = K Q^T for this lane's column
+        f32x16 s;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) s[r] = 0.f;
+        const uint16_t* kl = &k_lds[buf][col * kKStride + 8 * hgrp];
+#pragma unroll
+        for (int kk = 0; kk < 12; ++kk) s = mfma_32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * kk)), qf[kk], s);
+
+        // mask: selected block of this query, and positions <= t
+        const int64_t tok0 = (int64_t)i * kTileTok;
+        const int blk0 = (int)(tok0 >> LOG2B);
+        const uint32_t word = mybits[blk0 >> 5];
+        const uint32_t tb = LOG2B == 0 ? word : (word >> (blk0 & 31));
+        float x[16];
+        float tmax = -INFINITY;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int mm = 8 * (r >> 2) + 4 * hgrp + (r & 3);
+            const bool valid = q_ok && ((tb >> (mm >> LOG2B)) & 1u) && (tok0 + mm <= tq);
+            x[r] = valid ? s[r] : -INFINITY;
+            tmax = fmaxf(tmax, x[r]);
+        }
+        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+        const float ts = tmax * sl2;
+        float ms = m_use * sl2;
+        const bool need = ts > ms + kLazyRescale;
+        if (__ballot(need)) {
+            const float alpha = need ? exp2f(ms - ts) : 1.0f;
+#pragma unroll
+            for (int dt = 0; dt < 6; ++dt) o[dt] *= alpha;
+            lsum *= alpha;
+            if (need) m_use = tmax;
+            ms = m_use * sl2;
+        }
+        const float msub = m_use == -INFINITY ? 0.0f : ms;
+        float p[16], psum = 0.f;
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            p[r] = exp2f(x[r] * sl2 - msub);
+            psum += p[r];
+        }
+        psum += __shfl_xor(psum, 32, 64);
+        lsum += psum;
+        bf16x8 pb[2];
+#pragma unroll
+        for (int sgi = 0; sgi < 2; ++sgi) {
+            uint4 pk;
+            pk.x = f32_to_bf16(p[8 * sgi + 0]) | (f32_to_bf16(p[8 * sgi + 1]) << 16);
+            pk.y = f32_to_bf16(p[8 * sgi + 2]) | (f32_to_bf16(p[8 * sgi + 3]) << 16);
+            pk.z = f32_to_bf16(p[8 * sgi + 4]) | (f32_to_bf16(p[8 * sgi + 5]) << 16);
+            pk.w = f32_to_bf16(p[8 * sgi + 6]) | (f32_to_bf16(p[8 * sgi + 7]) << 16);
+            pb[sgi] = as_bf16x8(pk);
+        }
+        // O^T += V^T P^T; k index 8*hgrp+e <-> token 16*sgi + 4*hgrp + (e&3) + 8*(e>>2)
+#pragma unroll
+        for (int dt = 0; dt < 6; ++dt) {
+#pragma unroll
+            for (int sgi = 0; sgi < 2; ++sgi) {
+                const uint16_t* vr = &vt_lds[buf][(32 * dt + col) * kVtStrideU + 16 * sgi + 4 * hgrp];
+                const uint2 lo = *(const uint2*)vr;
+                const uint2 hi = *(const uint2*)(vr + 8);
+                o[dt] = mfma_32x32x16(as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y}), pb[sgi], o[dt]);
+            }
+        }
+        if (i + 1 < n_tiles) lstore((i + 1) & 1);
+        __syncthreads();
+    }
+
+    // ---- epilogue: lane holds O^T[d][col] for d = 32dt + 8j + 4hgrp + i ----
+    if (q_ok) {
+        const float inv = 1.0f / lsum;
+        uint16_t* op = a.out + (qrow * kHeads + g * kHeadsPerGroup + head) * kHeadDim;
+#pragma unroll
+        for (int dt = 0; dt < 6; ++dt)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                uint2 pk;
+                pk.x = f32_to_bf16(o[dt][4 * j] * inv) | (f32_to_bf16(o[dt][4 * j + 1] * inv) << 16);
+                pk.y = f32_to_bf16(o[dt][4 * j + 2] * inv) | (f32_to_bf16(o[dt][4 * j + 3] * inv) << 16);
+                *(uint2*)(op + 32 * dt + 8 * j + 4 * hgrp) = pk;
+            }
+        if (hgrp == 0 && a.lse)
+            a.lse[qrow * kHeads + g * kHeadsPerGroup + head] = (m_use * sl2 + log2f(lsum)) * kLn2;
+    }
+}
+
 // Combine the splits' partial softmax states of one (query, group).
 __global__ __launch_bounds__(256) void attn_merge_kernel(SeqTable seqs, AttnMergeArgs a) {
     const DevSeq sq = seqs.s[blockIdx.y];
@@ -251,6 +478,35 @@ hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnAr
     dim3 grid((unsigned)(max_nq * kGroups * a.n_split), (unsigned)seqs.n);
     hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(256), lds, stream, seqs, a);
     return hipGetLastError();
+}
+
+template <int NW, int LOG2B>
+static hipError_t launch_union_t(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
+                                 int words, hipStream_t stream) {
+    const size_t lds = (size_t)(2 * NW) * words * sizeof(uint32_t);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_union_kernel<NW, LOG2B>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    const int64_t n_qt = (max_nq + 2 * NW - 1) / (2 * NW);
+    dim3 grid((unsigned)(n_qt * kGroups), (unsigned)seqs.n);
+    hipLaunchKernelGGL((attn_union_kernel<NW, LOG2B>), grid, dim3(NW * 64), lds, stream, seqs, a,
+                       words);
+    return hipGetLastError();
+}
+
+int union_queries_per_block() { return 2 * kUnionWaves; }
+
+hipError_t launch_attn_union(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
+                             int words, hipStream_t stream) {
+    if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
+    switch (a.block_size) {
+        case 1: return launch_union_t<kUnionWaves, 0>(seqs, max_nq, a, words, stream);
+        case 2: return launch_union_t<kUnionWaves, 1>(seqs, max_nq, a, words, stream);
+        case 4: return launch_union_t<kUnionWaves, 2>(seqs, max_nq, a, words, stream);
+        case 8: return launch_union_t<kUnionWaves, 3>(seqs, max_nq, a, words, stream);
+        case 16: return launch_union_t<kUnionWaves, 4>(seqs, max_nq, a, words, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 hipError_t launch_attn_merge(const SeqTable& seqs, int64_t max_nq, const AttnMergeArgs& a,

@@ -109,6 +109,14 @@ def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
         w = _decode(name, seed=seed)
     elif name == "chunk_1m":
         w = _prefill(name, 8192, 8, 512, pos0=1_040_384)
+    elif name == "decode_small":                 # 8 sequences, split paths (tests)
+        w = _decode(name, n_seqs=8, lo=8192, hi=40000, cap=40960, seed=seed)
+    elif name.startswith("chunk_"):              # chunk_<pos0>_<n>[_b<B>_k<K>] (tests)
+        parts = name.split("_")
+        pos0, n = int(parts[1]), int(parts[2])
+        B = int(parts[3][1:]) if len(parts) > 3 else 8
+        K = int(parts[4][1:]) if len(parts) > 4 else 512
+        w = _prefill(name, n, B, K, pos0=pos0)
     elif name.startswith("prefill_"):          # prefill_<n>[_b<B>_k<K>] for tests
         parts = name.split("_")
         n = int(parts[1])

@@ -129,7 +129,10 @@ class Checker:
         blocks = np.arange(n) if blocks is None else np.asarray(blocks)
         gpu = P.bits_to_f64(self.store[s.store_offset + blocks])
         st = P.check_rounded(gpu, exact[blocks], self.wl.store_q8, P.REL_STORE, "store")
-        self.stats["store"] = st
+        prev = self.stats["store"] or {"n": 0, "boundary_cases": 0, "max_abs": 0.0}
+        self.stats["store"] = {"n": prev["n"] + st["n"],
+                               "boundary_cases": prev["boundary_cases"] + st["boundary_cases"],
+                               "max_abs": max(prev["max_abs"], st["max_abs"])}
         return st
 
     # -- one sequence ----------------------------------------------------------
@@ -153,7 +156,11 @@ class Checker:
         qh = nu.round_bf16(qh_exact)
         # q_hat parity (admissible rounding)
         qh_gpu = P.bits_to_f64(self.q_hat[qrows])
-        self.stats["q_hat"] = P.check_rounded(qh_gpu, qh_exact, False, P.REL_QHAT, "q_hat")
+        st = P.check_rounded(qh_gpu, qh_exact, False, P.REL_QHAT, "q_hat")
+        prev = self.stats["q_hat"] or {"n": 0, "boundary_cases": 0, "max_abs": 0.0}
+        self.stats["q_hat"] = {"n": prev["n"] + st["n"],
+                               "boundary_cases": prev["boundary_cases"] + st["boundary_cases"],
+                               "max_abs": max(prev["max_abs"], st["max_abs"])}
         q_lo, q_hi = P.rounding_interval(qh_exact, False, P.REL_QHAT)
         q_main = W.host_q(wl, qrows) if check_attn else None
         for n_i, (qi, t) in enumerate(zip(qs, t_all)):

@@ -1,0 +1,62 @@
+"""GPU parity against the oracle across block sizes, top-k sizes, ragged
+tails, chunked prefill on an existing cache and the split (decode) paths."""
+import numpy as np
+import pytest
+import torch
+
+from synth import workloads as W
+
+from .gpu_checks import Checker, log, prepare, run_steps
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_and_check(name, n_rows=64, store_q8=True, check_all_store=True, seed_rows=0):
+    wl = W.make(name, store_q8=store_q8)
+    log("case", wl.name, "q8" if store_q8 else "bf16")
+    di, cfg = prepare(wl)
+    run_steps(wl, di, cfg)
+    ck = Checker(wl, di, cfg)
+    rng = np.random.default_rng(seed_rows)
+    from .gpu_checks import stratified_rows
+    for si, s in enumerate(wl.seqs):
+        qs = stratified_rows(s, wl.block_size, wl.topk, n_rows, rng)
+        b_need = max((s.cache_len - 1) // wl.block_size, s.cache_len // wl.block_size)
+        stored, exact = ck.oracle_store(s, s.cache_len // wl.block_size)
+        if check_all_store:
+            ck.check_store(s, stored, exact)
+        ck.check_seq(si, qs, store_exact=(stored, exact))
+    st = ck.finish()
+    log(st)
+    return st
+
+
+def test_topk_compaction_heavy():
+    # K=16 over up to 499 candidates: the streaming buffer compacts many times
+    _run_and_check("prefill_4000_b8_k16", n_rows=96)
+
+
+def test_prefill_8k_stratified():
+    _run_and_check("prefill_8k", n_rows=64)
+
+
+def test_block_size_one():
+    _run_and_check("prefill_2000_b1_k64", n_rows=64)
+
+
+def test_block_size_sixteen_ragged():
+    _run_and_check("prefill_1003_b16_k8", n_rows=64)
+
+
+def test_bf16_store():
+    _run_and_check("prefill_1000_b8_k32", n_rows=64, store_q8=False)
+
+
+def test_chunk_on_existing_cache_unaligned():
+    # pos0 = 1003 is inside block 125: the block mixes earlier and new tokens
+    _run_and_check("chunk_1003_997_b8_k64", n_rows=64)
+
+
+def test_decode_split_paths():
+    st = _run_and_check("decode_small", n_rows=1, check_all_store=True)
+    assert st["rows"] == 8
