@@ -1,0 +1,178 @@
+"""The C ABI without a GPU: every symbol include/sgqa.h declares is exported,
+and every rejected call returns its status before any HIP call.
+
+Every call here is invalid by construction (a NULL or inconsistent argument
+that validation rejects first), so none of them can reach a kernel launch.
+"""
+import ctypes
+import math
+import os
+import re
+
+import pytest
+
+import sparse_long_context_block_amd as sg
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "sgqa.h")
+
+OK, E_NULL, E_CONFIG, E_SHAPE, E_CAUSAL, E_CAPACITY, E_WS, E_UNSUP, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8
+FAKE = 0x100000          # a non-NULL pointer value; never dereferenced (calls fail validation)
+
+
+@pytest.fixture(scope="module")
+def L():
+    return sg.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(sgqa_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_symbols_exported(L):
+    names = declared_functions()
+    assert set(names) >= {"sgqa_compress", "sgqa_index_topk", "sgqa_sparse_attn", "sgqa_forward",
+                          "sgqa_workspace_size", "sgqa_status_string", "sgqa_last_error",
+                          "sgqa_abi_version"}
+    for n in names:
+        assert hasattr(L, n), f"{n} not exported by libsgqa.so"
+
+
+def test_version_and_status_strings(L):
+    assert L.sgqa_abi_version() == 1
+    for code, name in [(OK, b"SGQA_OK"), (E_NULL, b"SGQA_ERR_NULL"), (E_CONFIG, b"SGQA_ERR_CONFIG"),
+                       (E_SHAPE, b"SGQA_ERR_SHAPE"), (E_CAUSAL, b"SGQA_ERR_CAUSAL"),
+                       (E_CAPACITY, b"SGQA_ERR_CAPACITY"), (E_WS, b"SGQA_ERR_WORKSPACE"),
+                       (E_UNSUP, b"SGQA_ERR_UNSUPPORTED"), (E_HIP, b"SGQA_ERR_HIP")]:
+        assert L.sgqa_status_string(code) == name
+    assert L.sgqa_status_string(12345) == b"SGQA_UNKNOWN_STATUS"
+
+
+def _seqs(*seqs):
+    arr = (sg.Seq * len(seqs))(*seqs)
+    return arr, len(seqs)
+
+
+def _call_attn(L, cfg, seqs, n=None, q=None, k=None, v=None, sel=None, out=None, ws=None, ws_bytes=0):
+    arr, m = _seqs(*seqs) if seqs else (None, 0)
+    return L.sgqa_sparse_attn(ctypes.byref(cfg) if cfg is not None else None, arr,
+                              m if n is None else n, q, k, v, sel, out, None, ws, ws_bytes, None)
+
+
+def _good_seq(n_q=8, pos0=0):
+    return sg.seq(n_q, pos0=pos0)
+
+
+# config and sequence errors are reported before pointers are looked at, so
+# all tensor pointers below are NULL
+
+@pytest.mark.parametrize("field,value,code", [
+    ("num_q_heads", 0, E_CONFIG), ("num_q_heads", 65, E_CONFIG), ("rope_dim", 31, E_CONFIG),
+    ("rope_dim", 256, E_CONFIG), ("store_q8", 2, E_CONFIG), ("softmax_scale", math.nan, E_CONFIG),
+    ("softmax_scale", -1.0, E_CONFIG), ("eps_rms", -1.0, E_CONFIG), ("rope_base", 0.0, E_CONFIG),
+    ("topk_blocks", 0, E_CONFIG), ("block_size", 0, E_CONFIG),
+    ("head_dim", 128, E_UNSUP), ("idx_dim", 64, E_UNSUP), ("num_kv_groups", 8, E_UNSUP),
+    ("idx_heads", 2, E_UNSUP), ("rope_dim", 64, E_UNSUP), ("block_size", 3, E_UNSUP),
+    ("block_size", 32, E_UNSUP), ("topk_blocks", 4097, E_UNSUP),
+])
+def test_config_errors(L, field, value, code):
+    cfg = sg.config()
+    setattr(cfg, field, value)
+    assert _call_attn(L, cfg, [_good_seq()]) == code
+    assert field.split("_")[0] in L.sgqa_last_error().decode() or code in (E_UNSUP, E_CONFIG)
+
+
+def test_null_config_and_seqs(L):
+    assert _call_attn(L, None, [_good_seq()]) == E_NULL
+    cfg = sg.config()
+    assert L.sgqa_sparse_attn(ctypes.byref(cfg), None, 1, None, None, None, None, None, None,
+                              None, 0, None) == E_NULL
+    assert _call_attn(L, cfg, [_good_seq()], n=0) == E_SHAPE
+
+
+@pytest.mark.parametrize("mutate,code", [
+    (lambda s: setattr(s, "n_q", -1), E_SHAPE),
+    (lambda s: setattr(s, "kv_offset", -5), E_SHAPE),
+    (lambda s: setattr(s, "q_offset", 1 << 41), E_SHAPE),
+    (lambda s: setattr(s, "cache_len", s.cache_len + 1), E_CAUSAL),
+    (lambda s: setattr(s, "kv_capacity", s.cache_len - 1), E_CAPACITY),
+    (lambda s: setattr(s, "store_capacity", s.cache_len // 8 - 1), E_CAPACITY),
+])
+def test_sequence_errors(L, mutate, code):
+    s = sg.seq(64, pos0=100)
+    mutate(s)
+    assert _call_attn(L, sg.config(), [sg.seq(8), s]) == code
+    assert "seqs[1]" in L.sgqa_last_error().decode()
+
+
+def test_null_tensors(L):
+    cfg = sg.config()
+    arr, n = _seqs(_good_seq())
+    P = ctypes.c_void_p(FAKE)
+    # compress: proxy_k, comp_logits, store required
+    assert L.sgqa_compress(ctypes.byref(cfg), arr, n, None, P, None, None, P, None, 0, None) == E_NULL
+    assert L.sgqa_compress(ctypes.byref(cfg), arr, n, P, None, None, None, P, None, 0, None) == E_NULL
+    assert L.sgqa_compress(ctypes.byref(cfg), arr, n, P, P, None, None, None, None, 0, None) == E_NULL
+    # index_topk: q_idx, w, store, sel required
+    for missing in range(4):
+        a = [P, P, P, P]
+        a[missing] = None
+        assert L.sgqa_index_topk(ctypes.byref(cfg), arr, n, a[0], a[1], None, a[2], a[3], None,
+                                 None, None, 0, None) == E_NULL
+    # sparse_attn: q, k, v, sel, out required
+    for missing in range(5):
+        a = [P] * 5
+        a[missing] = None
+        assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, *a, None, None, 0, None) == E_NULL
+    # forward: ten required pointers
+    req = [3, 4, 7, 8, 9, 11, 13, 14, 15, 16]     # proxy_k, logits, store, q_idx, w, sel, q, k, v, out
+    for missing in req:
+        args = [ctypes.byref(cfg), arr, n] + [None] * 18
+        for i in req:
+            args[i] = P
+        args[19] = 0                              # ws_bytes
+        args[missing] = None
+        assert L.sgqa_forward(*args) == E_NULL
+
+
+def test_workspace_errors(L):
+    # one decode query over a long cache needs split workspace
+    cfg = sg.config()
+    seqs = [sg.seq(1, pos0=200_000)]
+    need = sg.workspace_size(cfg, seqs, sg.OP_SPARSE_ATTN)
+    need_i = sg.workspace_size(cfg, seqs, sg.OP_INDEX_TOPK)
+    need_f = sg.workspace_size(cfg, seqs, sg.OP_FORWARD)
+    assert need > 0 and need_i > 0 and need_f >= max(need, need_i)
+    P = ctypes.c_void_p(FAKE)
+    arr, n = _seqs(*seqs)
+    assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, P, P, P, P, P, None, None, need, None) == E_WS
+    assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, P, P, P, P, P, None, P, need - 1, None) == E_WS
+    assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, P, P, P, P, P, None,
+                              ctypes.c_void_p(FAKE + 8), need, None) == E_WS
+    assert L.sgqa_index_topk(ctypes.byref(cfg), arr, n, P, P, None, P, P, None, None, P, need_i - 1,
+                             None) == E_WS
+    assert "workspace" in L.sgqa_last_error().decode()
+
+
+def test_workspace_size_invalid_args_is_zero(L):
+    cfg = sg.config(block_size=3)
+    assert sg.workspace_size(cfg, [_good_seq()], sg.OP_FORWARD) == 0
+    assert "block_size" in L.sgqa_last_error().decode()
+    assert sg.workspace_size(sg.config(), [_good_seq()], 7) == 0
+
+
+def test_prefill_needs_no_workspace(L):
+    # large prefills run unsplit: no scratch memory
+    cfg = sg.config()
+    assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_FORWARD) == 0
+    assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_COMPRESS) == 0
+
+
+def test_binding_rejects_wrong_tensors():
+    import torch
+    cfg = sg.config()
+    with pytest.raises((TypeError, ValueError)):
+        sg.sparse_attn(cfg, [_good_seq()], torch.zeros(4), torch.zeros(4), torch.zeros(4),
+                       torch.zeros(4, dtype=torch.int32), torch.zeros(4))
