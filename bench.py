@@ -174,6 +174,8 @@ def main() -> int:
     ap.add_argument("--workload", default="prefill_8k")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--kernel-reps", type=int, default=20)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 512 MiB device-to-device copy (HBM byte-counter scale)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); "
@@ -230,6 +232,13 @@ def main() -> int:
         "sparse_attn": event_time_ms(op_attn, stream, reps),
     }
     print(f"[bench] per-op ms {k_ms}", file=sys.stderr, flush=True)
+
+    if args.calibrate_copy:
+        src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
 
     wm = work_model(wl)
     decode = wl.name.startswith("decode")

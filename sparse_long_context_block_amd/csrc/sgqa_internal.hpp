@@ -121,7 +121,6 @@ hipError_t launch_attn_merge(const SeqTable& seqs, int64_t max_nq, const AttnMer
                              hipStream_t stream);
 // tiled kernel for dense-ish selections; `words` = 32-bit words per query
 // bitmap (>= floor(t_max/B)/32 + 1 over the launch)
-constexpr int kUnionWaves = 8;
 int union_queries_per_block();
 hipError_t launch_attn_union(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a, int words,
                              hipStream_t stream);

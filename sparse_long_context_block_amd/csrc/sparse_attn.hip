@@ -217,39 +217,222 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
 //
 // One workgroup = 2*NW consecutive queries x one group; wavefront w owns two
 // queries x 16 heads = 32 columns.  The workgroup walks the causal range in
-// contiguous 32-token tiles: K (row-major) and V (transposed) go through LDS
-// once and serve 32*NW (query, head) columns; a per-query bitmap of selected
-// blocks (plus the current block, positions <= t) masks the scores, so every
-// query still attends over exactly its own token set.
-//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K tile (LDS), B = Q^T (regs)
-//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T tile (LDS), B = P^T: the
-//                 exponentiated S^T result layout, token order permuted
-//                 identically in A and B, so P never leaves registers.
+// contiguous 32-token tiles; K and V rows go through LDS once (row-major,
+// padded) and serve 32*NW (query, head) columns.  A per-query bitmap of the
+// selected blocks (plus the current block, positions <= t) masks the scores,
+// so every query still attends over exactly its own token set.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128),
+//                 B = Q^T (registers)
+//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T read from the row-major
+//                 V tile with ds_read_b64_tr_b16 (each 16-lane group gets a
+//                 4-token x 16-dim block transposed), B = P^T: the
+//                 exponentiated S^T result layout with the token order
+//                 permuted identically in A and B, so P never leaves
+//                 registers.
 // Each lane holds one (query, head) column, so the running max / sum are
 // per lane; the max is rescaled lazily (only when it grows by more than
 // 2^8), which keeps O exact because O and the sum share the reference max.
+// Global loads run two tiles ahead through registers (3 x 16 B per thread
+// per tile), LDS is double-buffered.
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(16))) float f32x16;
+typedef __attribute__((ext_vector_type(4))) short i16x4v;
+typedef __attribute__((ext_vector_type(8))) short i16x8v;
 
 constexpr int kTileTok = 32;
-constexpr int kKStride = kHeadDim + 8;       // bf16 per K row in LDS (400 B)
-constexpr int kVtStrideU = kTileTok + 4;     // bf16 per V^T row in LDS (72 B)
-constexpr int kChunksPerTile = kTileTok * kHeadDim / 8;   // 16-byte chunks of one K (or V) tile
-constexpr float kLazyRescale = 8.0f;         // log2 units
+constexpr int kKStrideU = kHeadDim + 8;       // bf16 per K row in LDS (400 B: b128 reads conflict-free)
+constexpr int kVStrideU = kHeadDim + 32;      // bf16 per V row in LDS (448 B: transposed reads conflict-free)
+constexpr int kKTileElems = kTileTok * kKStrideU;
+constexpr int kVTileElems = kTileTok * kVStrideU;
+constexpr int kBufElems = kKTileElems + kVTileElems;
+constexpr int kHalfChunks = kTileTok * kHeadDim / 8;       // 16-byte chunks of one K (or V) tile
+constexpr int kOutStride = kHeadDim + 8;      // bf16 per staged output row (400 B)
+constexpr float kLazyRescale = 8.0f;          // log2 units
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int NW, int LOG2B>
-__global__ __launch_bounds__(NW * 64) void attn_union_kernel(SeqTable seqs, AttnArgs a, int words) {
-    constexpr int TQ = 2 * NW;
-    constexpr int NT = NW * 64;
-    constexpr int kPer = (kChunksPerTile + NT - 1) / NT;
+__device__ __forceinline__ i16x4v lds_read_tr16(const uint16_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+        (__attribute__((address_space(3))) i16x4v*)(p));
+}
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// three 16-byte chunks per thread per tile (512 threads x 3 = 2 x 768 chunks)
+struct KVStage {
+    uint4 c0, c1, c2;
+};
+
+struct UnionCtx {
+    const uint16_t* kb;
+    const uint16_t* vb;
+    int64_t t_last;
+    int tid;
+};
+
+__device__ __forceinline__ uint4 load_chunk(const UnionCtx& u, int tile, int c) {
+    const bool is_v = c >= kHalfChunks;
+    const int cc = is_v ? c - kHalfChunks : c;
+    const int tok = cc / 24, d8 = (cc - tok * 24) * 8;
+    int64_t pos = (int64_t)tile * kTileTok + tok;
+    pos = pos > u.t_last ? u.t_last : pos;
+    return *(const uint4*)((is_v ? u.vb : u.kb) + pos * ((int64_t)kGroups * kHeadDim) + d8);
+}
+
+__device__ __forceinline__ void store_chunk(uint16_t* buf, int c, uint4 v) {
+    const bool is_v = c >= kHalfChunks;
+    const int cc = is_v ? c - kHalfChunks : c;
+    const int tok = cc / 24, d8 = (cc - tok * 24) * 8;
+    *(uint4*)(buf + (is_v ? kKTileElems + tok * kVStrideU : tok * kKStrideU) + d8) = v;
+}
+
+__device__ __forceinline__ void gload(const UnionCtx& u, int tile, KVStage& r) {
+    r.c0 = load_chunk(u, tile, u.tid);
+    r.c1 = load_chunk(u, tile, u.tid + 512);
+    r.c2 = load_chunk(u, tile, u.tid + 1024);
+}
+
+__device__ __forceinline__ void lstore(uint16_t* buf, int tid, const KVStage& r) {
+    store_chunk(buf, tid, r.c0);
+    store_chunk(buf, tid + 512, r.c1);
+    store_chunk(buf, tid + 1024, r.c2);
+}
+
+// state of one lane's (query, head) column
+struct ColState {
+    f32x16 o[6];
+    float m_use, lsum;
+};
+
+template <int LOG2B>
+__device__ __forceinline__ void union_tile(ColState& st, const bf16x8 (&qf)[12], const uint16_t* buf,
+                                           int i, uint32_t word, int64_t tq, bool q_ok, int lane,
+                                           float sl2) {
+    const int hgrp = lane >> 5, col = lane & 31;
+    const uint16_t* kt = buf;
+    const uint16_t* vt = buf + kKTileElems;
+    // S^T = K Q^T for this lane's column
+    f32x16 s;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) s[r] = 0.f;
+    const uint16_t* kl = kt + col * kKStrideU + 8 * hgrp;
+#pragma unroll
+    for (int kk = 0; kk < 12; ++kk) s = mfma_32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * kk)), qf[kk], s);
+
+    // mask: this query's selected blocks, and positions <= t
+    const int64_t tok0 = (int64_t)i * kTileTok;
+    const int blk0 = (int)(tok0 >> LOG2B);
+    constexpr uint32_t kTileBits = LOG2B == 0 ? 0xFFFFFFFFu : ((1u << (kTileTok >> LOG2B)) - 1u);
+    const uint32_t tb = (LOG2B == 0 ? word : (word >> (blk0 & 31))) & kTileBits;
+    const int64_t lim64 = tq - tok0;                       // last visible offset in the tile
+    const int lim = lim64 > 64 ? 64 : (int)lim64;          // (negative: nothing visible)
+    const bool full = q_ok && tb == kTileBits && lim >= kTileTok - 1;
+    float x[16];
+    if (__ballot(!full) == 0) {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) x[r] = s[r];
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int mm = 8 * (r >> 2) + 4 * hgrp + (r & 3);
+            const bool valid = q_ok && ((tb >> (mm >> LOG2B)) & 1u) && mm <= lim;
+            x[r] = valid ? s[r] : -INFINITY;
+        }
+    }
+    float tmax = x[0];
+#pragma unroll
+    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
+    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    const float ts = tmax * sl2;
+    float ms = st.m_use * sl2;
+    const bool need = ts > ms + kLazyRescale;
+    if (__ballot(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(ms - ts) : 1.0f;
+#pragma unroll
+        for (int dt = 0; dt < 6; ++dt) st.o[dt] *= alpha;
+        st.lsum *= alpha;
+        if (need) st.m_use = tmax;
+        ms = st.m_use * sl2;
+    }
+    const float msub = st.m_use == -INFINITY ? 0.0f : ms;
+    float p[16], psum = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) {
+        p[r] = __builtin_amdgcn_exp2f(x[r] * sl2 - msub);
+        psum += p[r];
+    }
+    psum += __shfl_xor(psum, 32, 64);
+    st.lsum += psum;
+    bf16x8 pb[2];
+#pragma unroll
+    for (int sgi = 0; sgi < 2; ++sgi) {
+        uint4 pk;
+        pk.x = pack_bf16(p[8 * sgi + 0], p[8 * sgi + 1]);
+        pk.y = pack_bf16(p[8 * sgi + 2], p[8 * sgi + 3]);
+        pk.z = pack_bf16(p[8 * sgi + 4], p[8 * sgi + 5]);
+        pk.w = pack_bf16(p[8 * sgi + 6], p[8 * sgi + 7]);
+        pb[sgi] = as_bf16x8(pk);
+    }
+    // O^T += V^T P^T; k index 8*hgrp+e <-> token 16*sgi + 4*hgrp + (e&3) + 8*(e>>2).
+    // Transposed read: this lane supplies row tr_row (+16 sgi, +8), column
+    // tr_col + 32 dt; its 16-lane group receives a 4-token x 16-dim block.
+    const int tr_grp = lane >> 4;
+    const int tr_row = 4 * (tr_grp >> 1) + ((lane >> 2) & 3);
+    const int tr_col = 16 * (tr_grp & 1) + 4 * (lane & 3);
+#pragma unroll
+    for (int dt = 0; dt < 6; ++dt) {
+#pragma unroll
+        for (int sgi = 0; sgi < 2; ++sgi) {
+            const uint16_t* vr = vt + (16 * sgi + tr_row) * kVStrideU + 32 * dt + tr_col;
+            const i16x4v lo = lds_read_tr16(vr);
+            const i16x4v hi = lds_read_tr16(vr + 8 * kVStrideU);
+            const i16x8v av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
+            st.o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), pb[sgi], st.o[dt]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Tiled kernel for dense-ish selections (selected share of the candidates
+// >= 1/4, e.g. every query of an 8K prefill at k = 512 blocks).
+//
+// One workgroup = 16 consecutive queries x one group on 8 wavefronts;
+// wavefront w owns two queries x 16 heads = 32 columns.  The workgroup walks
+// the causal range in contiguous 32-token tiles; K and V rows go through LDS
+// once (row-major, padded) and serve 256 (query, head) columns.  A per-query
+// bitmap of the selected blocks (plus the current block, positions <= t)
+// masks the scores, so every query still attends over exactly its own token
+// set.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128),
+//                 B = Q^T (registers)
+//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T read from the row-major
+//                 V tile with ds_read_b64_tr_b16 (each 16-lane group gets a
+//                 4-token x 16-dim block transposed), B = P^T: the
+//                 exponentiated S^T result layout with the token order
+//                 permuted identically in A and B, so P never leaves
+//                 registers.
+// Each lane holds one (query, head) column, so the running max / sum are
+// per lane; the max is rescaled lazily (only when it grows by more than
+// 2^8), which keeps O exact because O and the sum share the reference max.
+// Global loads run two tiles ahead through registers (3 x 16 B per thread
+// per tile), LDS is double-buffered, and the output is staged through LDS so
+// each query's 16 heads leave as one contiguous 6 KB row block.
+// ---------------------------------------------------------------------------
+template <int LOG2B>
+__global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs a, int words) {
+    constexpr int NW = 8, TQ = 16, NT = 512;
     extern __shared__ uint32_t bitmap[];                         // [TQ][words]
-    __shared__ __attribute__((aligned(16))) uint16_t k_lds[2][kTileTok * kKStride];
-    __shared__ __attribute__((aligned(16))) uint16_t vt_lds[2][kHeadDim * kVtStrideU];
+    __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2 * kBufElems];
     __shared__ int s_nsel[TQ];
+    static_assert(2 * kBufElems >= NW * 16 * kOutStride, "output staging fits the tile buffers");
 
     const DevSeq sq = seqs.s[blockIdx.y];
     const int g = blockIdx.x & 3;
@@ -263,6 +446,16 @@ __global__ __launch_bounds__(NW * 64) void attn_union_kernel(SeqTable seqs, Attn
     const int nwords = (int)((t_last >> LOG2B) >> 5) + 1;
     const int tid = threadIdx.x;
     const int K = a.topk;
+
+    UnionCtx u;
+    u.kb = a.k + (sq.kv_offset * kGroups + g) * kHeadDim;
+    u.vb = a.v + (sq.kv_offset * kGroups + g) * kHeadDim;
+    u.t_last = t_last;
+    u.tid = tid;
+    const int n_tiles = (int)(t_last / kTileTok) + 1;
+    KVStage ra, rb;
+    gload(u, 0, ra);
+    if (n_tiles > 1) gload(u, 1, rb);
 
     // ---- per-query bitmaps of the selected blocks and the current block ----
     for (int i = tid; i < TQ * nwords; i += NT) bitmap[(i / nwords) * words + i % nwords] = 0u;
@@ -301,140 +494,71 @@ __global__ __launch_bounds__(NW * 64) void attn_union_kernel(SeqTable seqs, Attn
     }
     const uint32_t* mybits = bitmap + (q_ok ? qw : 0) * words;
 
-    f32x16 o[6];
+    ColState st;
 #pragma unroll
     for (int dt = 0; dt < 6; ++dt)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) o[dt][r] = 0.f;
-    float m_use = -INFINITY, lsum = 0.f;
+        for (int r = 0; r < 16; ++r) st.o[dt][r] = 0.f;
+    st.m_use = -INFINITY;
+    st.lsum = 0.f;
     const float sl2 = a.scale_log2;
 
-    // ---- cooperative tile loads ----
-    constexpr int64_t kRowStride = (int64_t)kGroups * kHeadDim;
-    const uint16_t* kb = a.k + (sq.kv_offset * kGroups + g) * kHeadDim;
-    const uint16_t* vb = a.v + (sq.kv_offset * kGroups + g) * kHeadDim;
-    uint4 kreg[kPer], vreg[kPer];
-    auto gload = [&](int tile) {
-#pragma unroll
-        for (int p = 0; p < kPer; ++p) {
-            const int c = tid + p * NT;
-            if (c < kChunksPerTile) {
-                const int tok = c / 24, d8 = (c - tok * 24) * 8;
-                int64_t pos = (int64_t)tile * kTileTok + tok;
-                pos = pos > t_last ? t_last : pos;
-                kreg[p] = *(const uint4*)(kb + pos * kRowStride + d8);
-                vreg[p] = *(const uint4*)(vb + pos * kRowStride + d8);
-            }
-        }
-    };
-    auto lstore = [&](int buf) {
-#pragma unroll
-        for (int p = 0; p < kPer; ++p) {
-            const int c = tid + p * NT;
-            if (c < kChunksPerTile) {
-                const int tok = c / 24, d8 = (c - tok * 24) * 8;
-                *(uint4*)(&k_lds[buf][tok * kKStride + d8]) = kreg[p];
-                const uint32_t w4[4] = {vreg[p].x, vreg[p].y, vreg[p].z, vreg[p].w};
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    vt_lds[buf][(d8 + 2 * e) * kVtStrideU + tok] = (uint16_t)(w4[e] & 0xFFFFu);
-                    vt_lds[buf][(d8 + 2 * e + 1) * kVtStrideU + tok] = (uint16_t)(w4[e] >> 16);
-                }
-            }
-        }
-    };
-
-    const int n_tiles = (int)(t_last / kTileTok) + 1;
-    gload(0);
-    lstore(0);
+    lstore(kv_lds, tid, ra);
     __syncthreads();
-    for (int i = 0; i < n_tiles; ++i) {
-        const int buf = i & 1;
-        if (i + 1 < n_tiles) gload(i + 1);
-
-        // S^T = K Q^T for this lane's column
-        f32x16 s;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) s[r] = 0.f;
-        const uint16_t* kl = &k_lds[buf][col * kKStride + 8 * hgrp];
-#pragma unroll
-        for (int kk = 0; kk < 12; ++kk) s = mfma_32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * kk)), qf[kk], s);
-
-        // mask: selected block of this query, and positions <= t
-        const int64_t tok0 = (int64_t)i * kTileTok;
-        const int blk0 = (int)(tok0 >> LOG2B);
-        const uint32_t word = mybits[blk0 >> 5];
-        const uint32_t tb = LOG2B == 0 ? word : (word >> (blk0 & 31));
-        float x[16];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int mm = 8 * (r >> 2) + 4 * hgrp + (r & 3);
-            const bool valid = q_ok && ((tb >> (mm >> LOG2B)) & 1u) && (tok0 + mm <= tq);
-            x[r] = valid ? s[r] : -INFINITY;
-            tmax = fmaxf(tmax, x[r]);
-        }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float ts = tmax * sl2;
-        float ms = m_use * sl2;
-        const bool need = ts > ms + kLazyRescale;
-        if (__ballot(need)) {
-            const float alpha = need ? exp2f(ms - ts) : 1.0f;
-#pragma unroll
-            for (int dt = 0; dt < 6; ++dt) o[dt] *= alpha;
-            lsum *= alpha;
-            if (need) m_use = tmax;
-            ms = m_use * sl2;
-        }
-        const float msub = m_use == -INFINITY ? 0.0f : ms;
-        float p[16], psum = 0.f;
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            p[r] = exp2f(x[r] * sl2 - msub);
-            psum += p[r];
-        }
-        psum += __shfl_xor(psum, 32, 64);
-        lsum += psum;
-        bf16x8 pb[2];
-#pragma unroll
-        for (int sgi = 0; sgi < 2; ++sgi) {
-            uint4 pk;
-            pk.x = f32_to_bf16(p[8 * sgi + 0]) | (f32_to_bf16(p[8 * sgi + 1]) << 16);
-            pk.y = f32_to_bf16(p[8 * sgi + 2]) | (f32_to_bf16(p[8 * sgi + 3]) << 16);
-            pk.z = f32_to_bf16(p[8 * sgi + 4]) | (f32_to_bf16(p[8 * sgi + 5]) << 16);
-            pk.w = f32_to_bf16(p[8 * sgi + 6]) | (f32_to_bf16(p[8 * sgi + 7]) << 16);
-            pb[sgi] = as_bf16x8(pk);
-        }
-        // O^T += V^T P^T; k index 8*hgrp+e <-> token 16*sgi + 4*hgrp + (e&3) + 8*(e>>2)
-#pragma unroll
-        for (int dt = 0; dt < 6; ++dt) {
-#pragma unroll
-            for (int sgi = 0; sgi < 2; ++sgi) {
-                const uint16_t* vr = &vt_lds[buf][(32 * dt + col) * kVtStrideU + 16 * sgi + 4 * hgrp];
-                const uint2 lo = *(const uint2*)vr;
-                const uint2 hi = *(const uint2*)(vr + 8);
-                o[dt] = mfma_32x32x16(as_bf16x8(uint4{lo.x, lo.y, hi.x, hi.y}), pb[sgi], o[dt]);
-            }
-        }
-        if (i + 1 < n_tiles) lstore((i + 1) & 1);
+    // tile i: compute from buffer i&1; registers of tile i+1 go to the other
+    // buffer afterwards; tile i+2 is loaded into the registers just freed
+    int i = 0;
+    for (; i + 1 < n_tiles; i += 2) {
+        if (i + 2 < n_tiles) gload(u, i + 2, ra);
+        union_tile<LOG2B>(st, qf, kv_lds, i, mybits[(int)((i * kTileTok) >> LOG2B) >> 5], tq, q_ok,
+                          lane, sl2);
+        lstore(kv_lds + kBufElems, tid, rb);
+        __syncthreads();
+        if (i + 3 < n_tiles) gload(u, i + 3, rb);
+        union_tile<LOG2B>(st, qf, kv_lds + kBufElems, i + 1,
+                          mybits[(int)(((i + 1) * kTileTok) >> LOG2B) >> 5], tq, q_ok, lane, sl2);
+        if (i + 2 < n_tiles) lstore(kv_lds, tid, ra);
+        __syncthreads();
+    }
+    if (i < n_tiles) {
+        union_tile<LOG2B>(st, qf, kv_lds, i, mybits[(int)((i * kTileTok) >> LOG2B) >> 5], tq, q_ok,
+                          lane, sl2);
         __syncthreads();
     }
 
-    // ---- epilogue: lane holds O^T[d][col] for d = 32dt + 8j + 4hgrp + i ----
-    if (q_ok) {
-        const float inv = 1.0f / lsum;
-        uint16_t* op = a.out + (qrow * kHeads + g * kHeadsPerGroup + head) * kHeadDim;
+    // ---- epilogue: O^T[d][col] for d = 32dt + 8j + 4hgrp + i, normalised,
+    //      staged per query in LDS, then written as contiguous 6 KB rows ----
+    const float inv = 1.0f / st.lsum;
+    if (hgrp == 0 && q_ok && a.lse)
+        a.lse[qrow * kHeads + g * kHeadsPerGroup + head] = (st.m_use * sl2 + log2f(st.lsum)) * kLn2;
 #pragma unroll
-        for (int dt = 0; dt < 6; ++dt)
+    for (int phase = 0; phase < 2; ++phase) {
+        if ((col >> 4) == phase) {
+            uint16_t* orow = kv_lds + (wave * 16 + head) * kOutStride;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                uint2 pk;
-                pk.x = f32_to_bf16(o[dt][4 * j] * inv) | (f32_to_bf16(o[dt][4 * j + 1] * inv) << 16);
-                pk.y = f32_to_bf16(o[dt][4 * j + 2] * inv) | (f32_to_bf16(o[dt][4 * j + 3] * inv) << 16);
-                *(uint2*)(op + 32 * dt + 8 * j + 4 * hgrp) = pk;
+            for (int dt = 0; dt < 6; ++dt)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    uint2 pk;
+                    pk.x = pack_bf16(st.o[dt][4 * j] * inv, st.o[dt][4 * j + 1] * inv);
+                    pk.y = pack_bf16(st.o[dt][4 * j + 2] * inv, st.o[dt][4 * j + 3] * inv);
+                    *(uint2*)(orow + 32 * dt + 8 * j + 4 * hgrp) = pk;
+                }
+        }
+        __syncthreads();
+        // 8 queries x 16 heads x 24 chunks of 16 B
+        for (int c = tid; c < NW * 16 * 24; c += NT) {
+            const int w = c / (16 * 24);
+            const int rem = c - w * 16 * 24;
+            const int h = rem / 24, c16 = rem - h * 24;
+            const int q = 2 * w + phase;
+            if (q < n_valid) {
+                const int64_t row = sq.q_offset + q0 + q;
+                *(uint4*)(a.out + (row * kHeads + g * kHeadsPerGroup + h) * kHeadDim + 8 * c16) =
+                    *(const uint4*)(kv_lds + (w * 16 + h) * kOutStride + 8 * c16);
             }
-        if (hgrp == 0 && a.lse)
-            a.lse[qrow * kHeads + g * kHeadsPerGroup + head] = (m_use * sl2 + log2f(lsum)) * kLn2;
+        }
+        __syncthreads();
     }
 }
 
@@ -480,31 +604,30 @@ hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnAr
     return hipGetLastError();
 }
 
-template <int NW, int LOG2B>
+template <int LOG2B>
 static hipError_t launch_union_t(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                                  int words, hipStream_t stream) {
-    const size_t lds = (size_t)(2 * NW) * words * sizeof(uint32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)attn_union_kernel<NW, LOG2B>,
+    const size_t lds = (size_t)16 * words * sizeof(uint32_t);
+    hipError_t e = hipFuncSetAttribute((const void*)attn_union_kernel<LOG2B>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
-    const int64_t n_qt = (max_nq + 2 * NW - 1) / (2 * NW);
+    const int64_t n_qt = (max_nq + 15) / 16;
     dim3 grid((unsigned)(n_qt * kGroups), (unsigned)seqs.n);
-    hipLaunchKernelGGL((attn_union_kernel<NW, LOG2B>), grid, dim3(NW * 64), lds, stream, seqs, a,
-                       words);
+    hipLaunchKernelGGL((attn_union_kernel<LOG2B>), grid, dim3(512), lds, stream, seqs, a, words);
     return hipGetLastError();
 }
 
-int union_queries_per_block() { return 2 * kUnionWaves; }
+int union_queries_per_block() { return 16; }
 
 hipError_t launch_attn_union(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                              int words, hipStream_t stream) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
     switch (a.block_size) {
-        case 1: return launch_union_t<kUnionWaves, 0>(seqs, max_nq, a, words, stream);
-        case 2: return launch_union_t<kUnionWaves, 1>(seqs, max_nq, a, words, stream);
-        case 4: return launch_union_t<kUnionWaves, 2>(seqs, max_nq, a, words, stream);
-        case 8: return launch_union_t<kUnionWaves, 3>(seqs, max_nq, a, words, stream);
-        case 16: return launch_union_t<kUnionWaves, 4>(seqs, max_nq, a, words, stream);
+        case 1: return launch_union_t<0>(seqs, max_nq, a, words, stream);
+        case 2: return launch_union_t<1>(seqs, max_nq, a, words, stream);
+        case 4: return launch_union_t<2>(seqs, max_nq, a, words, stream);
+        case 8: return launch_union_t<3>(seqs, max_nq, a, words, stream);
+        case 16: return launch_union_t<4>(seqs, max_nq, a, words, stream);
         default: return hipErrorInvalidValue;
     }
 }
