@@ -78,7 +78,7 @@ typedef enum sgqa_status {
  * state"): num_q_heads 64 in num_kv_groups 4 (16 heads per group), head_dim
  * 192, idx_heads 4 indexer heads per group of idx_dim 128, rope_dim 32 (even,
  * <= idx_dim).  block_size B is 1, 2, 4, 8 or 16 (8 on the page; 1 in the
- * architecture blog's ablation); topk_blocks K is 1..4096 (512 on the page:
+ * architecture blog's ablation); topk_blocks K is 1..3072 (512 on the page:
  * 4,096 tokens at B=8).  Other values are SGQA_ERR_UNSUPPORTED.
  */
 typedef struct sgqa_config {

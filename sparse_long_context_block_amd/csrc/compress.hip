@@ -52,8 +52,8 @@ __global__ __launch_bounds__(256) void compress_kernel(SeqTable seqs, CompressAr
     const bool in_rope = d0 < kRopeDim;
     const int pair_j = first_half ? d0 : d0 - kHalf;
     const int partner = first_half ? lane + kHalf / 2 : lane - kHalf / 2;
-    const double th0 = rope_theta(pair_j, a.rope_base);
-    const double th1 = rope_theta(pair_j + 1, a.rope_base);
+    const double th0 = in_rope ? a.theta[pair_j] : 0.0;
+    const double th1 = in_rope ? a.theta[pair_j + 1] : 0.0;
 
     float k0[B], k1[B], c0[B], c1[B];
 #pragma unroll

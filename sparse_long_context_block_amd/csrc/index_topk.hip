@@ -12,20 +12,19 @@
 // leaves the wavefront that computed it unless it may still be selected.
 //
 // Mapping (one wavefront per query and candidate split):
-//   * the 4 groups x 4 heads of one query's indexer queries are exactly the
-//     16 rows of a v_mfma_f32_16x16x32_bf16 A operand, so the four groups
-//     share every summary tile the wave streams (4x reuse of the store);
+//   * the query's 4 groups x 4 heads of q_hat are exactly the 16 rows of a
+//     v_mfma_f32_16x16x32_bf16 A operand, so the four groups share every
+//     store row the wavefront reads;
 //   * a 16-block tile of the store is the B operand, read straight from HBM /
-//     L2 into registers (16 B per lane per 32-wide k step, double-buffered);
+//     L2 into registers (16 B per lane per 32-wide k step), two tiles ahead;
 //   * the result layout puts all 4 heads of (group, block) in one lane, so
 //     the weighted ReLU sum is in-lane;
-//   * each group's selection is a streaming top-k: a per-group LDS buffer of
-//     `cap` (key, block) entries in ascending block order, an acceptance
-//     threshold (the current k-th key), and a radix-select compaction back to
-//     k entries when the buffer is nearly full.  Keys are order-preserving
-//     uint32 images of the fp32 scores (-0 folded into +0); ties keep the
-//     earlier entry, which is the lower block id because blocks arrive in
-//     ascending order.
+//   * each group's selection is a streaming top-k: an LDS buffer of `cap`
+//     (key, block) entries in ascending block order, an acceptance threshold
+//     (the current k-th key) and a radix-select compaction back to k entries
+//     when the buffer is nearly full.  Keys are order-preserving uint32 images
+//     of the fp32 scores (-0 folded into +0); ties keep the earlier entry,
+//     which is the lower block id because blocks arrive in ascending order.
 // A decode-sized call (few queries) splits each query's candidates over
 // several wavefronts; index_merge_kernel then selects from their lists.
 #include "sgqa_internal.hpp"
@@ -35,55 +34,80 @@ namespace {
 
 using namespace dev;
 
+
+__device__ __forceinline__ uint32_t wave_or(uint32_t v) {
+#pragma unroll
+    for (int o = 32; o > 0; o >>= 1) v |= __shfl_xor(v, o, 64);
+    return v;
+}
+
 // Keep the k entries with the largest keys among (key, idx)[0..n), n > k,
 // preferring earlier entries among equal keys, in their original order.
-// Runs on one wavefront; `hist` is 256 words of LDS.  Returns the k-th key.
+// Runs on one wavefront; `hist` is 256 words of LDS owned by it.  Radix
+// select with 8-bit digits starting at the highest bit in which the keys
+// differ (all-equal rows, e.g. rows of zero scores, need no histogram).
+// Returns the smallest kept key: the acceptance threshold for later,
+// higher-numbered candidates.
 __device__ uint32_t compact_topk(uint32_t* key, int32_t* idx, int n, int k, uint32_t* hist) {
     const int lane = lane_id();
-    uint32_t prefix = 0, pmask = 0;
+    const uint32_t k0 = key[0];
+    uint32_t diff = 0;
+    for (int i = lane; i < n; i += 64) diff |= key[i] ^ k0;
+    diff = wave_or(diff);
+    uint32_t prefix = k0;
     int krem = k;
+    if (diff != 0) {
+        const int hb = 31 - __builtin_clz(diff);
+        uint32_t pmask = hb == 31 ? 0u : (0xFFFFFFFFu << (hb + 1));
+        prefix = k0 & pmask;
 #pragma unroll 1
-    for (int shift = 24; shift >= 0; shift -= 8) {
-        for (int b = lane; b < 256; b += 64) hist[b] = 0u;
-        wave_lds_sync();
-        for (int i = lane; i < n; i += 64) {
-            uint32_t kk = key[i];
-            if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> shift) & 255u], 1u);
-        }
-        wave_lds_sync();
-        // lane L owns digits 255-4L down to 252-4L
-        uint32_t h[4];
-        uint32_t tot = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            h[j] = hist[255 - 4 * lane - j];
-            tot += h[j];
-        }
-        uint32_t incl = tot;
-#pragma unroll
-        for (int o = 1; o < 64; o <<= 1) {
-            uint32_t up = __shfl_up(incl, o, 64);
-            if (lane >= o) incl += up;
-        }
-        uint32_t above = incl - tot;   // entries with a larger digit
-        int found = -1;
-        uint32_t above_found = 0;
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            if (found < 0 && above + h[j] >= (uint32_t)krem) {
-                found = 255 - 4 * lane - j;
-                above_found = above;
+        for (int hi = hb; hi >= 0;) {
+            const int lo = hi >= 7 ? hi - 7 : 0;
+            const int nbins = 1 << (hi - lo + 1);
+            const uint32_t dmask = (uint32_t)nbins - 1u;
+            for (int b = lane; b < 256; b += 64) hist[b] = 0u;
+            wave_lds_sync();
+            for (int i = lane; i < n; i += 64) {
+                const uint32_t kk = key[i];
+                if ((kk & pmask) == prefix) atomicAdd(&hist[(kk >> lo) & dmask], 1u);
             }
-            above += h[j];
+            wave_lds_sync();
+            // lane L owns digits nbins-1-4L down to nbins-4-4L
+            uint32_t h[4];
+            uint32_t tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = nbins - 1 - 4 * lane - j;
+                h[j] = d >= 0 ? hist[d] : 0u;
+                tot += h[j];
+            }
+            uint32_t incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t up = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += up;
+            }
+            uint32_t above = incl - tot;   // entries with a larger digit
+            int found = -1;
+            uint32_t above_found = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (found < 0 && h[j] > 0 && above + h[j] >= (uint32_t)krem) {
+                    found = nbins - 1 - 4 * lane - j;
+                    above_found = above;
+                }
+                above += h[j];
+            }
+            const uint64_t fm = __ballot(found >= 0);
+            const int src = (int)__builtin_ctzll(fm);
+            const int digit = __shfl(found, src, 64);
+            const uint32_t ab = __shfl(above_found, src, 64);
+            prefix |= (uint32_t)digit << lo;
+            pmask |= dmask << lo;
+            krem -= (int)ab;
+            wave_lds_sync();
+            hi = lo - 1;
         }
-        const uint64_t fm = __ballot(found >= 0);
-        const int src = (int)__builtin_ctzll(fm);
-        const int digit = __shfl(found, src, 64);
-        const uint32_t ab = __shfl(above_found, src, 64);
-        prefix |= (uint32_t)digit << shift;
-        pmask |= 0xFFu << shift;
-        krem -= (int)ab;
-        wave_lds_sync();
     }
     // stable in-place compaction: all keys > v, and the first krem keys == v
     const uint32_t v = prefix;
@@ -116,23 +140,12 @@ __device__ uint32_t compact_topk(uint32_t* key, int32_t* idx, int n, int k, uint
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *(const uint4*)p; }
 
-__global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs a) {
-    extern __shared__ uint32_t lds[];
-    const int cap = a.cap;
-    uint32_t* keys = lds;                               // [4][cap]
-    int32_t* idxs = (int32_t*)(lds + 4 * cap);          // [4][cap]
-    uint32_t* hist = lds + 8 * cap;                     // [256]
-
-    const DevSeq sq = seqs.s[blockIdx.y];
-    const int64_t qi = blockIdx.x / a.n_split;
-    const int split = blockIdx.x % a.n_split;
-    if (qi >= sq.n_q) return;
-    const int64_t t = sq.pos0 + qi;
-    const int64_t row = sq.q_offset + qi;
-    const int lane = lane_id();
-    const int qq = lane >> 4;     // operand k-chunk; result group
-    const int m = lane & 15;      // operand row (4*group + head); result column
-
+// Indexer query of (row, t): RMSNorm, rotary span at position t, bf16; the
+// lane's A-operand fragments (row m = 4*group + head, k-chunk qq).  Writes
+// q_hat when asked.
+__device__ __forceinline__ void index_query_fragments(const IndexArgs& a, int64_t row, int64_t t,
+                                                      int qq, int m, bool write_qhat,
+                                                      bf16x8 (&afrag)[4]) {
     // ---- indexer query: RMSNorm, rotary span, bf16 (A operand rows) ----
     const uint16_t* qrow = a.q_idx + (row * (kGroups * kIdxHeads) + m) * kIdxDim + 8 * qq;
     float x[4][8];
@@ -181,13 +194,11 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
         for (int e = 0; e < 8; ++e) p[e] = __shfl_xor(x[0][e], 32, 64);
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-            const int j = 8 * (qq & 1) + e;
             float c, s;
-            rope_cos_sin(t, rope_theta(j, a.rope_base), &c, &s);
+            rope_cos_sin(t, a.theta[8 * (qq & 1) + e], &c, &s);
             x[0][e] = first ? (x[0][e] * c - p[e] * s) : (p[e] * s + x[0][e] * c);
         }
     }
-    bf16x8 afrag[4];
 #pragma unroll
     for (int kk = 0; kk < 4; ++kk) {
         uint4 packed;
@@ -196,10 +207,31 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
         packed.z = f32_to_bf16(x[kk][4]) | (f32_to_bf16(x[kk][5]) << 16);
         packed.w = f32_to_bf16(x[kk][6]) | (f32_to_bf16(x[kk][7]) << 16);
         afrag[kk] = as_bf16x8(packed);
-        if (a.q_hat_out && split == 0)
+        if (a.q_hat_out && write_qhat)
             *(uint4*)(a.q_hat_out + (row * (kGroups * kIdxHeads) + m) * kIdxDim + 32 * kk + 8 * qq) =
                 packed;
     }
+
+}
+
+__global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs a) {
+    extern __shared__ uint32_t lds[];
+    const int cap = a.cap;
+    uint32_t* keys = lds;                               // [4][cap]
+    int32_t* idxs = (int32_t*)(lds + 4 * cap);          // [4][cap]
+    uint32_t* hist = lds + 8 * cap;                     // [256]
+
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = blockIdx.x / a.n_split;
+    const int split = blockIdx.x % a.n_split;
+    if (qi >= sq.n_q) return;
+    const int64_t t = sq.pos0 + qi;
+    const int64_t row = sq.q_offset + qi;
+    const int lane = lane_id();
+    const int qq = lane >> 4;     // operand k-chunk; result group
+    const int m = lane & 15;      // operand row (4*group + head); result column
+    bf16x8 afrag[4];
+    index_query_fragments(a, row, t, qq, m, true, afrag);
 
     // this lane's results belong to group qq, heads 0..3
     const float4 wv = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
@@ -215,22 +247,31 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
     uint32_t* const mykeys = keys + qq * cap;
     int32_t* const myidx = idxs + qq * cap;
 
-    uint4 bcur[4], bnxt[4];
+    // B operand of tile r0: lane holds store[r0 + m][32kk + 8qq .. +7]
+    uint4 b0[4], b1[4];
+    auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * kIdxDim; };
     if (r_lo < r_hi) {
-        const int64_t rr = r_lo + m < r_hi ? r_lo + m : r_lo;
+        const int64_t o = row_of(r_lo);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) bcur[kk] = load16(store + rr * kIdxDim + 32 * kk);
+        for (int kk = 0; kk < 4; ++kk) b0[kk] = load16(store + o + 32 * kk);
+    }
+    if (r_lo + 16 < r_hi) {
+        const int64_t o = row_of(r_lo + 16);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
     }
     for (int64_t r0 = r_lo; r0 < r_hi; r0 += 16) {
-        const int64_t rn = r0 + 16;
-        if (rn < r_hi) {
-            const int64_t rr = rn + m < r_hi ? rn + m : rn;
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) bnxt[kk] = load16(store + rr * kIdxDim + 32 * kk);
-        }
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], as_bf16x8(bcur[kk]), acc);
+        for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], as_bf16x8(b0[kk]), acc);
+        // rotate the two-tile register pipeline: tile r0+32 goes in flight
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b0[kk] = b1[kk];
+        if (r0 + 32 < r_hi) {
+            const int64_t o = row_of(r0 + 32);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
+        }
         float s = wv.x * fmaxf(acc[0], 0.f);
         s += wv.y * fmaxf(acc[1], 0.f);
         s += wv.z * fmaxf(acc[2], 0.f);
@@ -239,6 +280,7 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
         const uint32_t key = score_key(s);
         const bool take = (rr < r_hi) && key > thr;
         const uint64_t am = __ballot(take);
+        if (am == 0) continue;                    // the common case once the threshold is up
         const uint32_t seg = (uint32_t)(am >> (16 * qq)) & 0xFFFFu;
         const int mycnt = qq == 0 ? cnt0 : qq == 1 ? cnt1 : qq == 2 ? cnt2 : cnt3;
         if (take) {
@@ -250,32 +292,28 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
         cnt1 += __popc((uint32_t)(am >> 16) & 0xFFFFu);
         cnt2 += __popc((uint32_t)(am >> 32) & 0xFFFFu);
         cnt3 += __popc((uint32_t)(am >> 48) & 0xFFFFu);
-        if (cnt0 > a.cap - 16 || cnt1 > a.cap - 16 || cnt2 > a.cap - 16 || cnt3 > a.cap - 16) {
+        if (cnt0 > cap - 16 || cnt1 > cap - 16 || cnt2 > cap - 16 || cnt3 > cap - 16) {
             wave_lds_sync();
-            if (cnt0 > a.cap - 16) {
-                uint32_t v = compact_topk(keys, idxs, cnt0, a.topk, hist);
+            if (cnt0 > cap - 16) {
+                const uint32_t v = compact_topk(keys, idxs, cnt0, a.topk, hist);
                 cnt0 = a.topk;
                 if (qq == 0) thr = v;
             }
-            if (cnt1 > a.cap - 16) {
-                uint32_t v = compact_topk(keys + cap, idxs + cap, cnt1, a.topk, hist);
+            if (cnt1 > cap - 16) {
+                const uint32_t v = compact_topk(keys + cap, idxs + cap, cnt1, a.topk, hist);
                 cnt1 = a.topk;
                 if (qq == 1) thr = v;
             }
-            if (cnt2 > a.cap - 16) {
-                uint32_t v = compact_topk(keys + 2 * cap, idxs + 2 * cap, cnt2, a.topk, hist);
+            if (cnt2 > cap - 16) {
+                const uint32_t v = compact_topk(keys + 2 * cap, idxs + 2 * cap, cnt2, a.topk, hist);
                 cnt2 = a.topk;
                 if (qq == 2) thr = v;
             }
-            if (cnt3 > a.cap - 16) {
-                uint32_t v = compact_topk(keys + 3 * cap, idxs + 3 * cap, cnt3, a.topk, hist);
+            if (cnt3 > cap - 16) {
+                const uint32_t v = compact_topk(keys + 3 * cap, idxs + 3 * cap, cnt3, a.topk, hist);
                 cnt3 = a.topk;
                 if (qq == 3) thr = v;
             }
-        }
-        if (rn < r_hi) {
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) bcur[kk] = bnxt[kk];
         }
     }
     wave_lds_sync();
@@ -290,62 +328,216 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
             c = a.topk;
         }
         const int64_t rg = row * kGroups + g;
-        if (a.n_split == 1) {
-            int32_t* sel = a.sel + rg * a.topk;
-            float* ssc = a.sel_scores ? a.sel_scores + rg * a.topk : nullptr;
-            for (int j = lane; j < a.topk; j += 64) {
-                const bool in = j < c;
-                sel[j] = in ? idxs[g * cap + j] : -1;
-                if (ssc) ssc[j] = in ? key_score(keys[g * cap + j]) : 0.0f;
-            }
-        } else {
-            const int64_t part = rg * a.n_split + split;
-            for (int j = lane; j < c; j += 64) {
-                a.part_key[part * a.topk + j] = keys[g * cap + j];
-                a.part_idx[part * a.topk + j] = idxs[g * cap + j];
-            }
-            if (lane == 0) a.part_cnt[part] = c;
+        int32_t* sel = a.sel + rg * a.topk;
+        float* ssc = a.sel_scores ? a.sel_scores + rg * a.topk : nullptr;
+        for (int j = lane; j < a.topk; j += 64) {
+            const bool in = j < c;
+            sel[j] = in ? idxs[g * cap + j] : -1;
+            if (ssc) ssc[j] = in ? key_score(keys[g * cap + j]) : 0.0f;
         }
     }
 }
 
-// Final selection of a split call: concatenate the splits' lists (ascending
-// block order), keep the k best.  One wavefront per (query, group).
-__global__ __launch_bounds__(64) void index_merge_kernel(SeqTable seqs, IndexMergeArgs a) {
-    extern __shared__ uint32_t lds[];
-    const int capm = a.n_split * a.topk;
-    uint32_t* keys = lds;
-    int32_t* idxs = (int32_t*)(lds + capm);
-    uint32_t* hist = lds + 2 * capm;
+// ---------------------------------------------------------------------------
+// Decode-sized calls (few queries, long histories): the candidates of each
+// query are spread over many wavefronts that only score (same MFMA mapping as
+// above) and write the order-preserving score keys to the workspace at their
+// block ids; one workgroup per (query, group) then selects.  Keys cost 4 B
+// per (query, group, candidate): 33 MB for 64 sequences of 256K tokens.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArgs a) {
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = blockIdx.x / a.n_split;
+    const int split = blockIdx.x % a.n_split;
+    if (qi >= sq.n_q) return;
+    const int64_t t = sq.pos0 + qi;
+    const int64_t row = sq.q_offset + qi;
+    const int64_t nb = t / a.block_size;
+    const int64_t r_lo = (int64_t)split * a.split_blocks;
+    const int64_t r_hi = nb < r_lo + a.split_blocks ? nb : r_lo + a.split_blocks;
+    if (r_lo >= r_hi && !(split == 0 && a.q_hat_out)) return;
+    const int lane = lane_id();
+    const int qq = lane >> 4;
+    const int m = lane & 15;
+    bf16x8 afrag[4];
+    index_query_fragments(a, row, t, qq, m, split == 0, afrag);
+    if (r_lo >= r_hi) return;
+    const float4 wv = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
+    const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
+    uint32_t* keys = a.part_key + (row * kGroups + qq) * a.key_stride;
+    uint4 b0[4], b1[4];
+    auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * kIdxDim; };
+    {
+        const int64_t o = row_of(r_lo);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b0[kk] = load16(store + o + 32 * kk);
+    }
+    if (r_lo + 16 < r_hi) {
+        const int64_t o = row_of(r_lo + 16);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
+    }
+    for (int64_t r0 = r_lo; r0 < r_hi; r0 += 16) {
+        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], as_bf16x8(b0[kk]), acc);
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b0[kk] = b1[kk];
+        if (r0 + 32 < r_hi) {
+            const int64_t o = row_of(r0 + 32);
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
+        }
+        float s = wv.x * fmaxf(acc[0], 0.f);
+        s += wv.y * fmaxf(acc[1], 0.f);
+        s += wv.z * fmaxf(acc[2], 0.f);
+        s += wv.w * fmaxf(acc[3], 0.f);
+        if (r0 + m < r_hi) keys[r0 + m] = score_key(s);
+    }
+}
 
+// Top-k of one (query, group) from its score keys: the k largest, equal keys
+// to the lower block id, output in ascending block id.  Four wavefronts:
+// keys staged in LDS when they fit, one histogram per wavefront per radix
+// digit (summed by wavefront 0), and the ordered output written from four
+// contiguous segments whose offsets come from one exchange.
+constexpr int kSelectLdsKeys = 36864;
+
+__global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexArgs a) {
+    extern __shared__ uint32_t skeys[];
+    __shared__ uint32_t hist[4][256];
+    __shared__ uint32_t red[4];
+    __shared__ int s_cnt[2][4];
+    __shared__ int s_digit, s_above;
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = blockIdx.x / kGroups;
     const int g = blockIdx.x % kGroups;
     if (qi >= sq.n_q) return;
-    const int lane = lane_id();
+    const int64_t t = sq.pos0 + qi;
     const int64_t rg = (sq.q_offset + qi) * kGroups + g;
+    const int n = (int)(t / a.block_size);
+    const int K = a.topk;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const uint32_t* gkeys = a.part_key + rg * a.key_stride;
+    const bool in_lds = n <= kSelectLdsKeys;
+    if (in_lds)
+        for (int i = tid; i < n; i += 256) skeys[i] = gkeys[i];
+    const uint32_t* keys = in_lds ? skeys : gkeys;
+    int32_t* sel = a.sel + rg * K;
+    float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
+    __syncthreads();
 
-    int n = 0;
-    for (int s = 0; s < a.n_split; ++s) {
-        const int64_t part = rg * a.n_split + s;
-        const int c = a.part_cnt[part];
-        for (int j = lane; j < c; j += 64) {
-            keys[n + j] = a.part_key[part * a.topk + j];
-            idxs[n + j] = a.part_idx[part * a.topk + j];
+    // selection rule: an entry is kept iff (key & pmask) > prefix, or
+    // (key & pmask) == prefix and fewer than krem such entries precede it
+    uint32_t prefix = 0, pmask = 0;   // n <= K: pmask 0 keeps everything
+    int krem = K;
+    if (n > K) {
+        const uint32_t k0 = keys[0];
+        uint32_t diff = 0;
+        for (int i = tid; i < n; i += 256) diff |= keys[i] ^ k0;
+        diff = wave_or(diff);
+        if (lane == 0) red[w] = diff;
+        __syncthreads();
+        diff = red[0] | red[1] | red[2] | red[3];
+        prefix = k0;
+        pmask = 0xFFFFFFFFu;
+        if (diff != 0) {
+            const int hb = 31 - __builtin_clz(diff);
+            pmask = hb == 31 ? 0u : (0xFFFFFFFFu << (hb + 1));
+            prefix = k0 & pmask;
+            for (int hi = hb; hi >= 0;) {
+                const int lo = hi >= 7 ? hi - 7 : 0;
+                const int nbins = 1 << (hi - lo + 1);
+                const uint32_t dmask = (uint32_t)nbins - 1u;
+                for (int b = lane; b < 256; b += 64) hist[w][b] = 0u;
+                __syncthreads();
+                for (int i = tid; i < n; i += 256) {
+                    const uint32_t kk = keys[i];
+                    if ((kk & pmask) == prefix) atomicAdd(&hist[w][(kk >> lo) & dmask], 1u);
+                }
+                __syncthreads();
+                if (w == 0) {
+                    uint32_t h[4], tot = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const int d = nbins - 1 - 4 * lane - j;
+                        h[j] = d >= 0 ? hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d] : 0u;
+                        tot += h[j];
+                    }
+                    uint32_t incl = tot;
+#pragma unroll
+                    for (int o = 1; o < 64; o <<= 1) {
+                        const uint32_t up = __shfl_up(incl, o, 64);
+                        if (lane >= o) incl += up;
+                    }
+                    uint32_t above = incl - tot;
+                    int found = -1;
+                    uint32_t above_found = 0;
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        if (found < 0 && h[j] > 0 && above + h[j] >= (uint32_t)krem) {
+                            found = nbins - 1 - 4 * lane - j;
+                            above_found = above;
+                        }
+                        above += h[j];
+                    }
+                    const uint64_t fm = __ballot(found >= 0);
+                    if (lane == (int)__builtin_ctzll(fm)) {
+                        s_digit = found;
+                        s_above = (int)above_found;
+                    }
+                }
+                __syncthreads();
+                prefix |= (uint32_t)s_digit << lo;
+                pmask |= dmask << lo;
+                krem -= s_above;
+                hi = lo - 1;
+            }
         }
-        n += c;
     }
-    wave_lds_sync();
-    if (n > a.topk) {
-        compact_topk(keys, idxs, n, a.topk, hist);
-        n = a.topk;
+    // ordered output: wavefront w owns entries [w*seg, (w+1)*seg)
+    const int seg = (n + 255) / 256 * 64;
+    const int b0 = w * seg;
+    const int b1 = b0 + seg < n ? b0 + seg : n;
+    int n_gt = 0, n_eq = 0;
+    for (int base = b0; base < b1; base += 64) {
+        const int i = base + lane;
+        const uint32_t kk = i < b1 ? keys[i] & pmask : 0u;
+        n_gt += __popcll(__ballot(i < b1 && kk > prefix));
+        n_eq += __popcll(__ballot(i < b1 && kk == prefix));
     }
-    int32_t* sel = a.sel + rg * a.topk;
-    float* ssc = a.sel_scores ? a.sel_scores + rg * a.topk : nullptr;
-    for (int j = lane; j < a.topk; j += 64) {
-        const bool in = j < n;
-        sel[j] = in ? idxs[j] : -1;
-        if (ssc) ssc[j] = in ? key_score(keys[j]) : 0.0f;
+    if (lane == 0) {
+        s_cnt[0][w] = n_gt;
+        s_cnt[1][w] = n_eq;
+    }
+    __syncthreads();
+    // kept before this segment: every larger masked key, min(krem, equal ones)
+    int out = 0, eq_seen = 0;
+    for (int j = 0; j < w; ++j) {
+        out += s_cnt[0][j];
+        eq_seen += s_cnt[1][j];
+    }
+    out += eq_seen < krem ? eq_seen : krem;
+    for (int base = b0; base < b1; base += 64) {
+        const int i = base + lane;
+        const uint32_t kk = i < b1 ? keys[i] : 0u;
+        const bool eq = i < b1 && (kk & pmask) == prefix;
+        const uint64_t em = __ballot(eq);
+        const int er = eq_seen + (int)lanes_below(em);
+        const bool keep = i < b1 && ((kk & pmask) > prefix || (eq && er < krem));
+        const uint64_t km = __ballot(keep);
+        if (keep) {
+            const int pos = out + (int)lanes_below(km);
+            sel[pos] = i;
+            if (ssc) ssc[pos] = key_score(kk);
+        }
+        out += __popcll(km);
+        eq_seen += __popcll(em);
+    }
+    const int total = n <= K ? n : K;
+    for (int j = total + tid; j < K; j += 256) {
+        sel[j] = -1;
+        if (ssc) ssc[j] = 0.0f;
     }
 }
 
@@ -365,15 +557,20 @@ hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexAr
     return hipGetLastError();
 }
 
-hipError_t launch_index_merge(const SeqTable& seqs, int64_t max_nq, const IndexMergeArgs& a,
+hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
                               hipStream_t stream) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
-    const size_t lds = (size_t)a.n_split * a.topk * 8u + 1024u;
-    hipError_t e = hipFuncSetAttribute((const void*)index_merge_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    dim3 grid((unsigned)(max_nq * a.n_split), (unsigned)seqs.n);
+    hipLaunchKernelGGL(index_score_kernel, grid, dim3(64), 0, stream, seqs, a);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
-    hipLaunchKernelGGL(index_merge_kernel, grid, dim3(64), lds, stream, seqs, a);
+    const int64_t max_b = a.key_stride;
+    const size_t lds = (size_t)(max_b < kSelectLdsKeys ? max_b : kSelectLdsKeys) * sizeof(uint32_t);
+    e = hipFuncSetAttribute((const void*)index_select_kernel,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid2((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
+    hipLaunchKernelGGL(index_select_kernel, grid2, dim3(256), lds, stream, seqs, a);
     return hipGetLastError();
 }
 

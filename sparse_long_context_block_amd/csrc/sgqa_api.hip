@@ -98,6 +98,7 @@ struct IndexPlan {
     int n_split = 1;
     int split_blocks = 0;
     int cap = 0;
+    int64_t key_stride = 0;
     int64_t rows = 0;           // packed query rows spanned (max q_offset + n_q)
     size_t ws = 0;
 };
@@ -116,36 +117,39 @@ int64_t packed_rows(const sgqa_seq* s, int32_t n) {
     return r;
 }
 
+// Large query counts run the fused streaming kernel (one wavefront per
+// query); small ones (decode) spread each query's candidates over score
+// wavefronts and select from the score keys in the workspace.
 IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     IndexPlan p;
     const int K = c->topk_blocks;
     p.cap = (K + 256 + 63) / 64 * 64;
+    while (p.cap > K + 64 && sgqa::index_lds_bytes(p.cap) > sgqa::kMaxLds) p.cap -= 64;
     p.rows = packed_rows(s, n);
     int64_t total_q = 0, max_b = 0;
     for (int32_t i = 0; i < n; ++i) {
         total_q += s[i].n_q;
         if (s[i].n_q > 0) max_b = std::max(max_b, (s[i].cache_len - 1) / c->block_size);
     }
-    const int64_t max_split_lds = std::max<int64_t>(1, 16384 / K);
-    int64_t want = total_q > 0 ? (2048 + total_q - 1) / total_q : 1;
-    int64_t split = std::min<int64_t>({want, max_split_lds, std::max<int64_t>(1, max_b / 256)});
-    if (split <= 1 || max_b <= 0) {
-        p.n_split = 1;
-        p.split_blocks = 0x7FFFFFF0;
-        return p;
-    }
+    p.n_split = 1;
+    p.split_blocks = 0x7FFFFFF0;
+    p.key_stride = 0;
+    const int64_t stride = (max_b + 15) / 16 * 16;
+    const size_t key_bytes = (size_t)p.rows * sgqa::kGroups * stride * 4;
+    if (total_q == 0 || total_q >= 1024 || max_b <= K || key_bytes > ((size_t)1 << 30)) return p;
+    int64_t split = std::min<int64_t>((4096 + total_q - 1) / total_q, std::max<int64_t>(1, max_b / 256));
     int64_t per = (max_b + split - 1) / split;
     per = (per + 15) / 16 * 16;
     p.split_blocks = (int)per;
     p.n_split = (int)((max_b + per - 1) / per);
-    if (p.n_split <= 1) {
-        p.n_split = 1;
-        p.split_blocks = 0x7FFFFFF0;
-        return p;
-    }
-    const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split;
-    p.ws = align_up(parts * K * 4) * 2 + align_up(parts * 4);
+    p.key_stride = stride;
+    p.ws = align_up(key_bytes);
     return p;
+}
+
+void rope_table(const sgqa_config* c, double* theta) {
+    for (int j = 0; j < sgqa::kRopeDim / 2; ++j)
+        theta[j] = pow((double)c->rope_base, -2.0 * j / (double)sgqa::kRopeDim);
 }
 
 // Queries of a sequence [0, n_dense) whose selection covers at least a
@@ -167,7 +171,8 @@ AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
         ((int64_t)c->topk_blocks * c->block_size + c->block_size + 15) / 16;
     const int64_t units = total_q * sgqa::kGroups;
     int64_t want = units > 0 ? (1024 + units - 1) / units : 1;
-    int64_t split = std::min<int64_t>(want, std::max<int64_t>(1, max_chunks / 8));
+    int64_t split = std::min<int64_t>({want, std::max<int64_t>(1, max_chunks / 8),
+                                       (int64_t)sgqa::kMaxAttnSplits});
     if (split <= 1) {
         p.n_split = 1;
         p.chunks_per_split = (int)std::min<int64_t>(max_chunks + 4, 0x7FFFFFF0);
@@ -234,7 +239,7 @@ int run_compress(const sgqa_config* c, const sgqa_seq* s, int32_t n, const void*
     a.block_size = c->block_size;
     a.store_q8 = c->store_q8;
     a.eps = c->eps_ln;
-    a.rope_base = c->rope_base;
+    rope_table(c, a.theta);
     const int B = c->block_size;
     for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
         const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
@@ -266,36 +271,18 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     a.n_split = p.n_split;
     a.split_blocks = p.split_blocks;
     a.eps = c->eps_rms;
-    a.rope_base = c->rope_base;
+    rope_table(c, a.theta);
     a.part_key = nullptr;
-    a.part_idx = nullptr;
-    a.part_cnt = nullptr;
-    if (p.n_split > 1) {
-        const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split;
-        char* base = (char*)ws;
-        a.part_key = (uint32_t*)base;
-        a.part_idx = (int32_t*)(base + align_up(parts * c->topk_blocks * 4));
-        a.part_cnt = (int32_t*)(base + 2 * align_up(parts * c->topk_blocks * 4));
-    }
+    a.key_stride = p.key_stride;
+    if (p.key_stride > 0) a.part_key = (uint32_t*)ws;
     for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
         const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
         sgqa::SeqTable tab;
         const int64_t mx = fill_table(tab, s, first, cnt, [](const sgqa_seq& q) { return q.n_q; });
         if (tab.n == 0) continue;
-        hipError_t e = sgqa::launch_index_topk(tab, mx, a, st);
+        hipError_t e = p.key_stride > 0 ? sgqa::launch_index_split(tab, mx, a, st)
+                                        : sgqa::launch_index_topk(tab, mx, a, st);
         if (e != hipSuccess) return hip_fail(e, "index_topk launch");
-        if (p.n_split > 1) {
-            sgqa::IndexMergeArgs ma;
-            ma.part_key = a.part_key;
-            ma.part_idx = a.part_idx;
-            ma.part_cnt = a.part_cnt;
-            ma.sel = sel;
-            ma.sel_scores = sel_scores;
-            ma.topk = c->topk_blocks;
-            ma.n_split = p.n_split;
-            e = sgqa::launch_index_merge(tab, mx, ma, st);
-            if (e != hipSuccess) return hip_fail(e, "index_merge launch");
-        }
     }
     return SGQA_OK;
 }

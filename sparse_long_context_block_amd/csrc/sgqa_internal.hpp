@@ -17,8 +17,9 @@ constexpr int kHeadDim = 192;     // main Q/K/V head dim
 constexpr int kIdxHeads = 4;      // indexer heads per group
 constexpr int kIdxDim = 128;      // indexer dim
 constexpr int kRopeDim = 32;      // indexer rotary span
-constexpr int kMaxTopK = 4096;
+constexpr int kMaxTopK = 3072;
 constexpr int kMaxSeqsPerLaunch = 64;
+constexpr int kMaxAttnSplits = 64;
 
 // Per-sequence descriptor as the kernels see it (passed by value in the
 // kernel arguments, up to kMaxSeqsPerLaunch per launch).
@@ -48,7 +49,7 @@ struct CompressArgs {
     int32_t block_size;
     int32_t store_q8;
     float eps;
-    float rope_base;
+    double theta[kRopeDim / 2]; // rotary frequencies base^(-2j/32)
 };
 
 struct IndexArgs {
@@ -56,29 +57,18 @@ struct IndexArgs {
     const float* w;
     const uint16_t* rms_gamma;  // may be null
     const uint16_t* store;
-    int32_t* sel;               // final output (n_split == 1) or null
+    int32_t* sel;
     float* sel_scores;          // may be null
     uint16_t* q_hat_out;        // may be null
-    uint32_t* part_key;         // split mode: [rows, G, n_split, K]
-    int32_t* part_idx;
-    int32_t* part_cnt;          // [rows, G, n_split]
+    uint32_t* part_key;         // split calls: score keys [rows, G, key_stride]
+    int64_t key_stride;
     int32_t block_size;
     int32_t topk;               // K
-    int32_t cap;                // per-row LDS buffer capacity C
+    int32_t cap;                // per-row LDS buffer capacity C (fused kernel)
     int32_t n_split;
     int32_t split_blocks;       // candidate blocks per split (multiple of 16)
     float eps;
-    float rope_base;
-};
-
-struct IndexMergeArgs {
-    const uint32_t* part_key;
-    const int32_t* part_idx;
-    const int32_t* part_cnt;
-    int32_t* sel;
-    float* sel_scores;
-    int32_t topk;
-    int32_t n_split;
+    double theta[kRopeDim / 2]; // rotary frequencies base^(-2j/32)
 };
 
 struct AttnArgs {
@@ -111,9 +101,12 @@ struct AttnMergeArgs {
 hipError_t launch_compress(const SeqTable& seqs, int64_t max_blocks, const CompressArgs& a,
                            hipStream_t stream);
 size_t index_lds_bytes(int cap);
+constexpr size_t kMaxLds = 160 * 1024;
 hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
                              hipStream_t stream);
-hipError_t launch_index_merge(const SeqTable& seqs, int64_t max_nq, const IndexMergeArgs& a,
+// decode-sized calls: score wavefronts over candidate splits, then one
+// select workgroup per (query, group)
+hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
                               hipStream_t stream);
 hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                               hipStream_t stream);
@@ -211,18 +204,16 @@ __device__ __forceinline__ f32x4 mfma_16x16x16(i16x4 a, i16x4 b, f32x4 c) {
 __device__ __forceinline__ bf16x8 as_bf16x8(uint4 v) { return __builtin_bit_cast(bf16x8, v); }
 __device__ __forceinline__ i16x4 as_i16x4(uint2 v) { return __builtin_bit_cast(i16x4, v); }
 
-// rotary frequency of pair j: base^(-2j/32), in fp64
-__device__ __forceinline__ double rope_theta(int j, float base) {
-    return pow((double)base, -2.0 * (double)j / (double)kRopeDim);
-}
-
-// cos / sin of the rotary angle pos * theta, evaluated in fp64 (an fp32
-// product would lose ~0.06 rad near position 1e6)
+// cos / sin of the rotary angle pos * theta.  The angle is reduced modulo
+// 2*pi in fp64 (an fp32 product would lose ~0.06 rad near position 1e6),
+// then evaluated in fp32 on the reduced argument.
 __device__ __forceinline__ void rope_cos_sin(int64_t pos, double theta, float* c, float* s) {
-    double sd, cd;
-    sincos((double)pos * theta, &sd, &cd);
-    *c = (float)cd;
-    *s = (float)sd;
+    const double kTwoPiHi = 6.283185307179586;
+    const double kTwoPiLo = 2.4492935982947064e-16;
+    const double phi = (double)pos * theta;
+    const double k = rint(phi * 0.15915494309189535);
+    const double r = (phi - k * kTwoPiHi) - k * kTwoPiLo;
+    sincosf((float)r, s, c);
 }
 
 }  // namespace dev

@@ -562,31 +562,42 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
     }
 }
 
-// Combine the splits' partial softmax states of one (query, group).
+// Combine the splits' partial softmax states of one (query, group): each
+// split's (max, sum) becomes one weight per head, then every output element
+// is a weighted sum of the splits' partial outputs.
 __global__ __launch_bounds__(256) void attn_merge_kernel(SeqTable seqs, AttnMergeArgs a) {
+    __shared__ float wsc[kMaxAttnSplits][kHeadsPerGroup];
     const DevSeq sq = seqs.s[blockIdx.y];
     const int g = blockIdx.x % kGroups;
     const int64_t qi = blockIdx.x / kGroups;
     if (qi >= sq.n_q) return;
     const int64_t row = sq.q_offset + qi;
     const int64_t rg = row * kGroups + g;
-    for (int e = threadIdx.x; e < kHeadsPerGroup * kHeadDim; e += 256) {
-        const int head = e / kHeadDim;
-        const int d = e - head * kHeadDim;
+    const int tid = threadIdx.x;
+    if (tid < kHeadsPerGroup) {
+        const int head = tid;
         float M = -INFINITY;
         for (int s = 0; s < a.n_split; ++s)
             M = fmaxf(M, a.part_ml[((rg * a.n_split + s) * kHeadsPerGroup + head) * 2]);
-        float L = 0.f, O = 0.f;
+        float L = 0.f;
         for (int s = 0; s < a.n_split; ++s) {
-            const int64_t part = rg * a.n_split + s;
-            const float ms = a.part_ml[(part * kHeadsPerGroup + head) * 2];
-            if (ms == -INFINITY) continue;
-            const float sc = exp2f(ms - M);
-            L += a.part_ml[(part * kHeadsPerGroup + head) * 2 + 1] * sc;
-            O += a.part_o[(part * kHeadsPerGroup + head) * kHeadDim + d] * sc;
+            const int64_t pi = ((rg * a.n_split + s) * kHeadsPerGroup + head) * 2;
+            const float ms = a.part_ml[pi];
+            const float sc = ms == -INFINITY ? 0.0f : exp2f(ms - M);
+            wsc[s][head] = sc;
+            L += a.part_ml[pi + 1] * sc;
         }
-        a.out[(row * kHeads + g * kHeadsPerGroup + head) * kHeadDim + d] = (uint16_t)f32_to_bf16(O / L);
-        if (a.lse && d == 0) a.lse[row * kHeads + g * kHeadsPerGroup + head] = (M + log2f(L)) * kLn2;
+        const float inv = 1.0f / L;
+        for (int s = 0; s < a.n_split; ++s) wsc[s][head] *= inv;
+        if (a.lse) a.lse[row * kHeads + g * kHeadsPerGroup + head] = (M + log2f(L)) * kLn2;
+    }
+    __syncthreads();
+    for (int e = tid; e < kHeadsPerGroup * kHeadDim; e += 256) {
+        const int head = e / kHeadDim;
+        float O = 0.f;
+        for (int s = 0; s < a.n_split; ++s)
+            O += wsc[s][head] * a.part_o[((rg * a.n_split + s) * kHeadsPerGroup) * kHeadDim + e];
+        a.out[(row * kHeads + g * kHeadsPerGroup) * kHeadDim + e] = (uint16_t)f32_to_bf16(O);
     }
 }
 

@@ -75,7 +75,7 @@ def _good_seq(n_q=8, pos0=0):
     ("topk_blocks", 0, E_CONFIG), ("block_size", 0, E_CONFIG),
     ("head_dim", 128, E_UNSUP), ("idx_dim", 64, E_UNSUP), ("num_kv_groups", 8, E_UNSUP),
     ("idx_heads", 2, E_UNSUP), ("rope_dim", 64, E_UNSUP), ("block_size", 3, E_UNSUP),
-    ("block_size", 32, E_UNSUP), ("topk_blocks", 4097, E_UNSUP),
+    ("block_size", 32, E_UNSUP), ("topk_blocks", 3073, E_UNSUP),
 ])
 def test_config_errors(L, field, value, code):
     cfg = sg.config()
