@@ -212,50 +212,22 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
 }
 
 // ---------------------------------------------------------------------------
-// Tiled kernel for dense-ish selections (selected share of the candidates
-// >= 1/4, e.g. every query of an 8K prefill at k = 512 blocks).
-//
-// One workgroup = 2*NW consecutive queries x one group; wavefront w owns two
-// queries x 16 heads = 32 columns.  The workgroup walks the causal range in
-// contiguous 32-token tiles; K and V rows go through LDS once (row-major,
-// padded) and serve 32*NW (query, head) columns.  A per-query bitmap of the
-// selected blocks (plus the current block, positions <= t) masks the scores,
-// so every query still attends over exactly its own token set.
-//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128),
-//                 B = Q^T (registers)
-//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T read from the row-major
-//                 V tile with ds_read_b64_tr_b16 (each 16-lane group gets a
-//                 4-token x 16-dim block transposed), B = P^T: the
-//                 exponentiated S^T result layout with the token order
-//                 permuted identically in A and B, so P never leaves
-//                 registers.
-// Each lane holds one (query, head) column, so the running max / sum are
-// per lane; the max is rescaled lazily (only when it grows by more than
-// 2^8), which keeps O exact because O and the sum share the reference max.
-// Global loads run two tiles ahead through registers (3 x 16 B per thread
-// per tile), LDS is double-buffered.
+// Tiled kernel for dense-ish selections: tile constants and helpers
 // ---------------------------------------------------------------------------
 typedef __attribute__((ext_vector_type(16))) float f32x16;
-typedef __attribute__((ext_vector_type(4))) short i16x4v;
-typedef __attribute__((ext_vector_type(8))) short i16x8v;
 
 constexpr int kTileTok = 32;
-constexpr int kKStrideU = kHeadDim + 8;       // bf16 per K row in LDS (400 B: b128 reads conflict-free)
-constexpr int kVStrideU = kHeadDim + 32;      // bf16 per V row in LDS (448 B: transposed reads conflict-free)
+constexpr int kKStrideU = kHeadDim + 8;       // bf16 per K row in LDS (100 dwords = 4 x odd: b128 reads conflict-free)
+constexpr int kVtStrideU = kTileTok + 8;      // bf16 per V^T row (one dim, 32 tokens) in LDS (20 dwords = 4 x odd)
 constexpr int kKTileElems = kTileTok * kKStrideU;
-constexpr int kVTileElems = kTileTok * kVStrideU;
+constexpr int kVTileElems = kHeadDim * kVtStrideU;
 constexpr int kBufElems = kKTileElems + kVTileElems;
-constexpr int kHalfChunks = kTileTok * kHeadDim / 8;       // 16-byte chunks of one K (or V) tile
+constexpr int kVSlots = (kHeadDim / 2) * (kTileTok / 8);   // (dim pair, token octet) slots of one V tile
 constexpr int kOutStride = kHeadDim + 8;      // bf16 per staged output row (400 B)
 constexpr float kLazyRescale = 8.0f;          // log2 units
 
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
-}
-
-__device__ __forceinline__ i16x4v lds_read_tr16(const uint16_t* p) {
-    return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-        (__attribute__((address_space(3))) i16x4v*)(p));
 }
 
 __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
@@ -266,91 +238,190 @@ __device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
     return __builtin_bit_cast(uint32_t, v);
 }
 
-// three 16-byte chunks per thread per tile (512 threads x 3 = 2 x 768 chunks)
+// Staging of one 32-token tile (12 dwords per thread).  Threads below
+// kVSlots each carry one V slot -- one dim pair of eight tokens, loaded as
+// dwords and transposed with byte permutes into two V^T row pieces -- and
+// one K chunk; the remaining threads carry three K chunks.  The eight
+// tokens of V slot octet o are the ones the O^T MFMA takes as k = 8o..8o+7:
+// 16(o>>1) + 4(o&1) + {0,1,2,3,8,9,10,11}, the token order of the
+// exponentiated scores a lane holds.
 struct KVStage {
-    uint4 c0, c1, c2;
+    uint4 a, b, c;
 };
 
 struct UnionCtx {
     const uint16_t* kb;
     const uint16_t* vb;
     int64_t t_last;
-    int tid;
+    bool vwave;        // this wavefront carries V slots (wave-uniform)
+    int o, pr;         // V slot: token octet, dim pair
+    int kc[3];         // K chunks carried (one for V wavefronts, three otherwise)
+    uint32_t voff;     // byte offset of the V slot's first token within a tile
+    uint32_t koff[3];  // byte offsets of the K chunks within a tile
 };
 
-__device__ __forceinline__ uint4 load_chunk(const UnionCtx& u, int tile, int c) {
-    const bool is_v = c >= kHalfChunks;
-    const int cc = is_v ? c - kHalfChunks : c;
-    const int tok = cc / 24, d8 = (cc - tok * 24) * 8;
-    int64_t pos = (int64_t)tile * kTileTok + tok;
-    pos = pos > u.t_last ? u.t_last : pos;
-    return *(const uint4*)((is_v ? u.vb : u.kb) + pos * ((int64_t)kGroups * kHeadDim) + d8);
+constexpr int64_t kRowElems = (int64_t)kGroups * kHeadDim;   // cache row stride in bf16
+constexpr int kRowBytes = (int)kRowElems * 2;
+
+__device__ __forceinline__ constexpr int octet_token(int o, int e) {
+    return 16 * (o >> 1) + 4 * (o & 1) + (e & 3) + 8 * (e >> 2);
 }
 
-__device__ __forceinline__ void store_chunk(uint16_t* buf, int c, uint4 v) {
-    const bool is_v = c >= kHalfChunks;
-    const int cc = is_v ? c - kHalfChunks : c;
-    const int tok = cc / 24, d8 = (cc - tok * 24) * 8;
-    *(uint4*)(buf + (is_v ? kKTileElems + tok * kVStrideU : tok * kKStrideU) + d8) = v;
+__device__ __forceinline__ uint32_t k_chunk_bytes(int c) {
+    const int tok = c / 24;
+    return (uint32_t)(tok * kRowBytes + (c - tok * 24) * 16);
+}
+
+__device__ __forceinline__ void union_ctx_init(UnionCtx& u, int tid) {
+    // readfirstlane makes the V/K split a scalar branch: the split falls on a
+    // wavefront boundary (kVSlots is a multiple of 64)
+    static_assert(kVSlots % 64 == 0, "V slots fill whole wavefronts");
+    u.vwave = __builtin_amdgcn_readfirstlane(tid) < kVSlots;
+    u.o = tid / 96;
+    u.pr = tid - u.o * 96;
+    u.kc[0] = tid;                 // V wavefronts: chunks 0..383; others: 384..767 in three strides
+    u.kc[1] = tid + 128;
+    u.kc[2] = tid + 256;
+    u.voff = (uint32_t)(octet_token(u.o, 0) * kRowBytes + 4 * u.pr);
+#pragma unroll
+    for (int j = 0; j < 3; ++j) u.koff[j] = k_chunk_bytes(u.kc[j]);
+}
+
+// Buffer resource over the tile's rows of one group: records end after the
+// group's slice of row t_last, so rows past the last query read as zeros
+// (finite, and masked out of the softmax) without any clamping.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base, int64_t tile0, int64_t t_last) {
+    const int64_t rows = t_last - tile0 + 1;
+    const int nrec = rows >= kTileTok ? kTileTok * kRowBytes : (int)(rows - 1) * kRowBytes + kHeadDim * 2;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tile0 * kRowElems), (short)0, nrec, 0x00020000);
 }
 
 __device__ __forceinline__ void gload(const UnionCtx& u, int tile, KVStage& r) {
-    r.c0 = load_chunk(u, tile, u.tid);
-    r.c1 = load_chunk(u, tile, u.tid + 512);
-    r.c2 = load_chunk(u, tile, u.tid + 1024);
+    const int64_t tile0 = (int64_t)tile * kTileTok;
+    const __amdgpu_buffer_rsrc_t kr = tile_rsrc(u.kb, tile0, u.t_last);
+    if (u.vwave) {
+        const __amdgpu_buffer_rsrc_t vr = tile_rsrc(u.vb, tile0, u.t_last);
+        uint32_t d[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e)
+            d[e] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)(u.voff + octet_token(0, e) * kRowBytes), 0, 0);
+        r.a = make_uint4(d[0], d[1], d[2], d[3]);
+        r.b = make_uint4(d[4], d[5], d[6], d[7]);
+        r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)u.koff[0], 0, 0));
+    } else {
+        r.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)u.koff[0], 0, 0));
+        r.b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)u.koff[1], 0, 0));
+        r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)u.koff[2], 0, 0));
+    }
 }
 
-__device__ __forceinline__ void lstore(uint16_t* buf, int tid, const KVStage& r) {
-    store_chunk(buf, tid, r.c0);
-    store_chunk(buf, tid + 512, r.c1);
-    store_chunk(buf, tid + 1024, r.c2);
+__device__ __forceinline__ void store_k_chunk(uint16_t* buf, int c, uint4 v) {
+    const int tok = c / 24, d8 = (c - tok * 24) * 8;
+    *(uint4*)(buf + tok * kKStrideU + d8) = v;
 }
 
-// state of one lane's (query, head) column
-struct ColState {
-    f32x16 o[6];
-    float m_use, lsum;
-};
+__device__ __forceinline__ void lstore(uint16_t* buf, const UnionCtx& u, const KVStage& r) {
+    if (u.vwave) {
+        // dims 2pr (low halves) and 2pr+1 (high halves) of the eight tokens
+        uint4 lo, hi;
+        lo.x = __builtin_amdgcn_perm(r.a.y, r.a.x, 0x05040100u);
+        lo.y = __builtin_amdgcn_perm(r.a.w, r.a.z, 0x05040100u);
+        lo.z = __builtin_amdgcn_perm(r.b.y, r.b.x, 0x05040100u);
+        lo.w = __builtin_amdgcn_perm(r.b.w, r.b.z, 0x05040100u);
+        hi.x = __builtin_amdgcn_perm(r.a.y, r.a.x, 0x07060302u);
+        hi.y = __builtin_amdgcn_perm(r.a.w, r.a.z, 0x07060302u);
+        hi.z = __builtin_amdgcn_perm(r.b.y, r.b.x, 0x07060302u);
+        hi.w = __builtin_amdgcn_perm(r.b.w, r.b.z, 0x07060302u);
+        uint16_t* vt = buf + kKTileElems + (2 * u.pr) * kVtStrideU + 8 * u.o;
+        *(uint4*)vt = lo;
+        *(uint4*)(vt + kVtStrideU) = hi;
+        store_k_chunk(buf, u.kc[0], r.c);
+    } else {
+        store_k_chunk(buf, u.kc[0], r.a);
+        store_k_chunk(buf, u.kc[1], r.b);
+        store_k_chunk(buf, u.kc[2], r.c);
+    }
+}
 
-template <int LOG2B>
-__device__ __forceinline__ void union_tile(ColState& st, const bf16x8 (&qf)[12], const uint16_t* buf,
-                                           int i, uint32_t word, int64_t tq, bool q_ok, int lane,
-                                           float sl2) {
+// S^T = K Q^T for this lane's column over one 32-token tile
+__device__ __forceinline__ f32x16 tile_scores(const uint16_t* buf, const bf16x8 (&qf)[12], int lane) {
     const int hgrp = lane >> 5, col = lane & 31;
-    const uint16_t* kt = buf;
-    const uint16_t* vt = buf + kKTileElems;
-    // S^T = K Q^T for this lane's column
     f32x16 s;
 #pragma unroll
     for (int r = 0; r < 16; ++r) s[r] = 0.f;
-    const uint16_t* kl = kt + col * kKStrideU + 8 * hgrp;
+    const uint16_t* kl = buf + col * kKStrideU + 8 * hgrp;
 #pragma unroll
     for (int kk = 0; kk < 12; ++kk) s = mfma_32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * kk)), qf[kk], s);
+    return s;
+}
 
-    // mask: this query's selected blocks, and positions <= t
-    const int64_t tok0 = (int64_t)i * kTileTok;
-    const int blk0 = (int)(tok0 >> LOG2B);
-    constexpr uint32_t kTileBits = LOG2B == 0 ? 0xFFFFFFFFu : ((1u << (kTileTok >> LOG2B)) - 1u);
-    const uint32_t tb = (LOG2B == 0 ? word : (word >> (blk0 & 31))) & kTileBits;
-    const int64_t lim64 = tq - tok0;                       // last visible offset in the tile
-    const int lim = lim64 > 64 ? 64 : (int)lim64;          // (negative: nothing visible)
-    const bool full = q_ok && tb == kTileBits && lim >= kTileTok - 1;
-    float x[16];
-    if (__ballot(!full) == 0) {
+// Reductions across the two 32-lane halves of a wavefront through
+// v_permlane32_swap (a VALU op: no LDS round trip as with ds_bpermute).
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+struct UnionState {
+    f32x16 o[6];       // O^T accumulators, 192 dims x this lane's column
+    f32x16 s;          // newest scores S^T
+    bf16x8 pb[2];      // exponentiated scores of the current tile, packed
+    float m_use, lsum; // reference max (raw score units) and running sum
+};
+
+struct UnionLane {
+    const uint32_t* mybits;
+    int64_t tq;
+    bool q_ok;
+    int lane, hgrp, col;
+    float sl2;
+};
+
+// Matrix work of a tile step: O^T += V^T P^T with the tile's exponentiated
+// scores, then S^T = K Q^T for the next tile.  k index
+// 8*hgrp+e of half sgi is V^T column 16*sgi + 8*hgrp + e, i.e. token
+// 16*sgi + 4*hgrp + (e&3) + 8*(e>>2), the token of S^T register 8*sgi + e.
+__device__ __forceinline__ void union_matrix(UnionState& st, const bf16x8 (&qf)[12], const uint16_t* kbuf,
+                                             const uint16_t* vbuf, const UnionLane& ln) {
+    const uint16_t* vt = vbuf + kKTileElems + ln.col * kVtStrideU + 8 * ln.hgrp;
 #pragma unroll
-        for (int r = 0; r < 16; ++r) x[r] = s[r];
-    } else {
+    for (int sgi = 0; sgi < 2; ++sgi)
 #pragma unroll
-        for (int r = 0; r < 16; ++r) {
-            const int mm = 8 * (r >> 2) + 4 * hgrp + (r & 3);
-            const bool valid = q_ok && ((tb >> (mm >> LOG2B)) & 1u) && mm <= lim;
-            x[r] = valid ? s[r] : -INFINITY;
+        for (int dt = 0; dt < 6; ++dt) {
+            const bf16x8 av = as_bf16x8(*(const uint4*)(vt + 32 * dt * kVtStrideU + 16 * sgi));
+            st.o[dt] = mfma_32x32x16(av, st.pb[sgi], st.o[dt]);
         }
-    }
-    float tmax = x[0];
+    st.s = tile_scores(kbuf, qf, ln.lane);
+}
+
+// Vector work of a tile step: mask the scores of tile ti (every score when
+// ti is not a tile of the range), update the lazily rescaled max and the
+// sum, and pack the exponentiated scores for the matrix work.
+template <int LOG2B>
+__device__ __forceinline__ void union_vector(UnionState& st, int ti, int n_tiles, const UnionLane& ln) {
+    constexpr uint32_t kTileBits = LOG2B == 0 ? 0xFFFFFFFFu : ((1u << (kTileTok >> LOG2B)) - 1u);
+    const bool live = ti >= 0 && ti < n_tiles;
+    const int64_t tok0 = (int64_t)(live ? ti : 0) * kTileTok;
+    const int blk0 = (int)(tok0 >> LOG2B);
+    const uint32_t word = ln.mybits[blk0 >> 5];
+    const uint32_t tb = (LOG2B == 0 ? word : (word >> (blk0 & 31))) & kTileBits;
+    const int64_t lim64 = ln.tq - tok0;
+    const int lim = ln.q_ok && live ? (lim64 > 64 ? 64 : (int)lim64) : -1;
+    float tmax = -INFINITY;
 #pragma unroll
-    for (int r = 1; r < 16; ++r) tmax = fmaxf(tmax, x[r]);
-    tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
+    for (int r = 0; r < 16; ++r) {
+        const int mm = 8 * (r >> 2) + 4 * ln.hgrp + (r & 3);
+        const bool valid = ((tb >> (mm >> LOG2B)) & 1u) && mm <= lim;
+        st.s[r] = valid ? st.s[r] : -INFINITY;
+        tmax = fmaxf(tmax, st.s[r]);
+    }
+    tmax = xor32_max(tmax);
+    const float sl2 = ln.sl2;
     const float ts = tmax * sl2;
     float ms = st.m_use * sl2;
     const bool need = ts > ms + kLazyRescale;
@@ -363,41 +434,24 @@ __device__ __forceinline__ void union_tile(ColState& st, const bf16x8 (&qf)[12],
         ms = st.m_use * sl2;
     }
     const float msub = st.m_use == -INFINITY ? 0.0f : ms;
-    float p[16], psum = 0.f;
-#pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        p[r] = __builtin_amdgcn_exp2f(x[r] * sl2 - msub);
-        psum += p[r];
-    }
-    psum += __shfl_xor(psum, 32, 64);
-    st.lsum += psum;
-    bf16x8 pb[2];
+    float psum = 0.f;
 #pragma unroll
     for (int sgi = 0; sgi < 2; ++sgi) {
-        uint4 pk;
-        pk.x = pack_bf16(p[8 * sgi + 0], p[8 * sgi + 1]);
-        pk.y = pack_bf16(p[8 * sgi + 2], p[8 * sgi + 3]);
-        pk.z = pack_bf16(p[8 * sgi + 4], p[8 * sgi + 5]);
-        pk.w = pack_bf16(p[8 * sgi + 6], p[8 * sgi + 7]);
-        pb[sgi] = as_bf16x8(pk);
-    }
-    // O^T += V^T P^T; k index 8*hgrp+e <-> token 16*sgi + 4*hgrp + (e&3) + 8*(e>>2).
-    // Transposed read: this lane supplies row tr_row (+16 sgi, +8), column
-    // tr_col + 32 dt; its 16-lane group receives a 4-token x 16-dim block.
-    const int tr_grp = lane >> 4;
-    const int tr_row = 4 * (tr_grp >> 1) + ((lane >> 2) & 3);
-    const int tr_col = 16 * (tr_grp & 1) + 4 * (lane & 3);
+        float p[8];
 #pragma unroll
-    for (int dt = 0; dt < 6; ++dt) {
-#pragma unroll
-        for (int sgi = 0; sgi < 2; ++sgi) {
-            const uint16_t* vr = vt + (16 * sgi + tr_row) * kVStrideU + 32 * dt + tr_col;
-            const i16x4v lo = lds_read_tr16(vr);
-            const i16x4v hi = lds_read_tr16(vr + 8 * kVStrideU);
-            const i16x8v av = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            st.o[dt] = mfma_32x32x16(__builtin_bit_cast(bf16x8, av), pb[sgi], st.o[dt]);
+        for (int e = 0; e < 8; ++e) {
+            p[e] = __builtin_amdgcn_exp2f(st.s[8 * sgi + e] * sl2 - msub);
+            psum += p[e];
         }
+        uint4 pk;
+        pk.x = pack_bf16(p[0], p[1]);
+        pk.y = pack_bf16(p[2], p[3]);
+        pk.z = pack_bf16(p[4], p[5]);
+        pk.w = pack_bf16(p[6], p[7]);
+        st.pb[sgi] = as_bf16x8(pk);
     }
+    psum = xor32_sum(psum);
+    st.lsum += psum;
 }
 
 // ---------------------------------------------------------------------------
@@ -407,32 +461,35 @@ __device__ __forceinline__ void union_tile(ColState& st, const bf16x8 (&qf)[12],
 // One workgroup = 16 consecutive queries x one group on 8 wavefronts;
 // wavefront w owns two queries x 16 heads = 32 columns.  The workgroup walks
 // the causal range in contiguous 32-token tiles; K and V rows go through LDS
-// once (row-major, padded) and serve 256 (query, head) columns.  A per-query
-// bitmap of the selected blocks (plus the current block, positions <= t)
-// masks the scores, so every query still attends over exactly its own token
-// set.
-//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128),
+// once and serve 256 (query, head) columns.  A per-query bitmap of the
+// selected blocks (plus the current block, positions <= t) masks the
+// scores, so every query still attends over exactly its own token set.
+//   S^T = K Q^T   v_mfma_f32_32x32x16_bf16, A = K rows (ds_read_b128 from a
+//                 row-major tile padded to 100 dwords per row),
 //                 B = Q^T (registers)
-//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T read from the row-major
-//                 V tile with ds_read_b64_tr_b16 (each 16-lane group gets a
-//                 4-token x 16-dim block transposed), B = P^T: the
-//                 exponentiated S^T result layout with the token order
-//                 permuted identically in A and B, so P never leaves
-//                 registers.
+//   O^T = V^T P^T v_mfma_f32_32x32x16_bf16, A = V^T rows (ds_read_b128)
+//                 from a dim-major V tile written with its tokens in the
+//                 order of the S^T result layout, B = P^T: the
+//                 exponentiated S^T registers, so P never leaves registers.
+//                 (Transposing on the way into LDS costs eight byte
+//                 permutes per thread per tile; transposed LDS reads run at
+//                 about a third of the b128 rate.)
 // Each lane holds one (query, head) column, so the running max / sum are
 // per lane; the max is rescaled lazily (only when it grows by more than
 // 2^8), which keeps O exact because O and the sum share the reference max.
-// Global loads run two tiles ahead through registers (3 x 16 B per thread
-// per tile), LDS is double-buffered, and the output is staged through LDS so
+// K/V tiles circulate through a ring of three LDS buffers with one barrier
+// per tile: tile i+2 is fetched with buffer loads at the top of step i (a
+// per-tile buffer resource ends at row t_last, so rows past the last query
+// read as zeros) and stored at its end.  The output is staged through LDS so
 // each query's 16 heads leave as one contiguous 6 KB row block.
 // ---------------------------------------------------------------------------
 template <int LOG2B>
 __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs a, int words) {
     constexpr int NW = 8, TQ = 16, NT = 512;
     extern __shared__ uint32_t bitmap[];                         // [TQ][words]
-    __shared__ __attribute__((aligned(16))) uint16_t kv_lds[2 * kBufElems];
+    __shared__ __attribute__((aligned(16))) uint16_t kv_lds[3 * kBufElems];
     __shared__ int s_nsel[TQ];
-    static_assert(2 * kBufElems >= NW * 16 * kOutStride, "output staging fits the tile buffers");
+    static_assert(3 * kBufElems >= NW * 16 * kOutStride, "output staging fits the tile buffers");
 
     const DevSeq sq = seqs.s[blockIdx.y];
     const int g = blockIdx.x & 3;
@@ -451,11 +508,10 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
     u.kb = a.k + (sq.kv_offset * kGroups + g) * kHeadDim;
     u.vb = a.v + (sq.kv_offset * kGroups + g) * kHeadDim;
     u.t_last = t_last;
-    u.tid = tid;
+    union_ctx_init(u, tid);
     const int n_tiles = (int)(t_last / kTileTok) + 1;
-    KVStage ra, rb;
-    gload(u, 0, ra);
-    if (n_tiles > 1) gload(u, 1, rb);
+    KVStage rs;
+    gload(u, 0, rs);
 
     // ---- per-query bitmaps of the selected blocks and the current block ----
     for (int i = tid; i < TQ * nwords; i += NT) bitmap[(i / nwords) * words + i % nwords] = 0u;
@@ -493,44 +549,56 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
         for (int kk = 0; kk < 12; ++kk) qf[kk] = as_bf16x8(*(const uint4*)(qp + 16 * kk));
     }
     const uint32_t* mybits = bitmap + (q_ok ? qw : 0) * words;
-
-    ColState st;
+    UnionState st;
 #pragma unroll
     for (int dt = 0; dt < 6; ++dt)
 #pragma unroll
         for (int r = 0; r < 16; ++r) st.o[dt][r] = 0.f;
+#pragma unroll
+    for (int r = 0; r < 16; ++r) st.s[r] = 0.f;
+    st.pb[0] = as_bf16x8(make_uint4(0u, 0u, 0u, 0u));
+    st.pb[1] = st.pb[0];
     st.m_use = -INFINITY;
     st.lsum = 0.f;
+    UnionLane ln;
+    ln.mybits = mybits;
+    ln.tq = tq;
+    ln.q_ok = q_ok;
+    ln.lane = lane;
+    ln.hgrp = hgrp;
+    ln.col = col;
+    ln.sl2 = a.scale_log2;
     const float sl2 = a.scale_log2;
 
-    lstore(kv_lds, tid, ra);
+    // ---- tile loop: the scores of tile i+1 are issued in the same straight
+    //      line as the softmax of tile i and the O update with it; tile i+2
+    //      is loaded at the top and stored into the third buffer at the end
+    //      (past the end the last tile is fetched again into a buffer no
+    //      longer read, which keeps loads and stores unconditional) ----
+    lstore(kv_lds, u, rs);
+    gload(u, n_tiles > 1 ? 1 : 0, rs);
+    lstore(kv_lds + kBufElems, u, rs);
     __syncthreads();
-    // tile i: compute from buffer i&1; registers of tile i+1 go to the other
-    // buffer afterwards; tile i+2 is loaded into the registers just freed
-    int i = 0;
-    for (; i + 1 < n_tiles; i += 2) {
-        if (i + 2 < n_tiles) gload(u, i + 2, ra);
-        union_tile<LOG2B>(st, qf, kv_lds, i, mybits[(int)((i * kTileTok) >> LOG2B) >> 5], tq, q_ok,
-                          lane, sl2);
-        lstore(kv_lds + kBufElems, tid, rb);
+    st.s = tile_scores(kv_lds, qf, lane);
+    int b_cur = 0;
+    for (int i = 0; i < n_tiles; ++i) {
+        const int b_nxt = b_cur == 2 ? 0 : b_cur + 1;
+        const int b_new = b_nxt == 2 ? 0 : b_nxt + 1;
+        gload(u, i + 2 < n_tiles ? i + 2 : n_tiles - 1, rs);
+        union_vector<LOG2B>(st, i, n_tiles, ln);
+        union_matrix(st, qf, kv_lds + b_nxt * kBufElems, kv_lds + b_cur * kBufElems, ln);
+        lstore(kv_lds + b_new * kBufElems, u, rs);
         __syncthreads();
-        if (i + 3 < n_tiles) gload(u, i + 3, rb);
-        union_tile<LOG2B>(st, qf, kv_lds + kBufElems, i + 1,
-                          mybits[(int)(((i + 1) * kTileTok) >> LOG2B) >> 5], tq, q_ok, lane, sl2);
-        if (i + 2 < n_tiles) lstore(kv_lds, tid, ra);
-        __syncthreads();
+        b_cur = b_nxt;
     }
-    if (i < n_tiles) {
-        union_tile<LOG2B>(st, qf, kv_lds, i, mybits[(int)((i * kTileTok) >> LOG2B) >> 5], tq, q_ok,
-                          lane, sl2);
-        __syncthreads();
-    }
+    f32x16 (&o)[6] = st.o;
+    const float m_use = st.m_use, lsum = st.lsum;
 
     // ---- epilogue: O^T[d][col] for d = 32dt + 8j + 4hgrp + i, normalised,
     //      staged per query in LDS, then written as contiguous 6 KB rows ----
-    const float inv = 1.0f / st.lsum;
+    const float inv = 1.0f / lsum;
     if (hgrp == 0 && q_ok && a.lse)
-        a.lse[qrow * kHeads + g * kHeadsPerGroup + head] = (st.m_use * sl2 + log2f(st.lsum)) * kLn2;
+        a.lse[qrow * kHeads + g * kHeadsPerGroup + head] = (m_use * sl2 + log2f(lsum)) * kLn2;
 #pragma unroll
     for (int phase = 0; phase < 2; ++phase) {
         if ((col >> 4) == phase) {
@@ -540,8 +608,8 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
                     uint2 pk;
-                    pk.x = pack_bf16(st.o[dt][4 * j] * inv, st.o[dt][4 * j + 1] * inv);
-                    pk.y = pack_bf16(st.o[dt][4 * j + 2] * inv, st.o[dt][4 * j + 3] * inv);
+                    pk.x = pack_bf16(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv);
+                    pk.y = pack_bf16(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
                     *(uint2*)(orow + 32 * dt + 8 * j + 4 * hgrp) = pk;
                 }
         }
