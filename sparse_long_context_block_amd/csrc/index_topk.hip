@@ -364,7 +364,7 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
     if (r_lo >= r_hi) return;
     const float4 wv = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
     const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
-    uint32_t* keys = a.part_key + (row * kGroups + qq) * a.key_stride;
+    uint32_t* keys = a.part_key + ((row - a.key_row0) * kGroups + qq) * a.key_stride;
     uint4 b0[4], b1[4];
     auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * kIdxDim; };
     {
@@ -396,106 +396,226 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
     }
 }
 
-// Top-k of one (query, group) from its score keys: the k largest, equal keys
-// to the lower block id, output in ascending block id.  Four wavefronts:
-// keys staged in LDS when they fit, one histogram per wavefront per radix
-// digit (summed by wavefront 0), and the ordered output written from four
-// contiguous segments whose offsets come from one exchange.
-constexpr int kSelectLdsKeys = 36864;
+// ---------------------------------------------------------------------------
+// Prefill-sized calls: a workgroup of four wavefronts scores 16 consecutive
+// queries (four per wavefront) against one range of candidate blocks.  The
+// range streams through LDS in tiles of 64 store rows (double-buffered, rows
+// padded to 68 dwords so the 16 rows a B-operand read touches hit distinct
+// banks); every B fragment a wavefront reads serves the MFMAs of its four
+// queries, so the store is read once per 16 queries instead of once per
+// query.  Keys go to the workspace exactly as in the decode-sized path.
+// ---------------------------------------------------------------------------
+constexpr int kStoreTile = 64;
+constexpr int kStoreStrideU = kIdxDim + 8;    // bf16 per LDS store row (68 dwords = 4 x 17)
 
-__global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexArgs a) {
-    extern __shared__ uint32_t skeys[];
-    __shared__ uint32_t hist[4][256];
-    __shared__ uint32_t red[4];
-    __shared__ int s_cnt[2][4];
-    __shared__ int s_digit, s_above;
+__global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, IndexArgs a) {
+    __shared__ __attribute__((aligned(16))) uint16_t tiles[2][kStoreTile * kStoreStrideU];
     const DevSeq sq = seqs.s[blockIdx.y];
-    const int64_t qi = blockIdx.x / kGroups;
-    const int g = blockIdx.x % kGroups;
-    if (qi >= sq.n_q) return;
-    const int64_t t = sq.pos0 + qi;
-    const int64_t rg = (sq.q_offset + qi) * kGroups + g;
-    const int n = (int)(t / a.block_size);
-    const int K = a.topk;
-    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const uint32_t* gkeys = a.part_key + rg * a.key_stride;
-    const bool in_lds = n <= kSelectLdsKeys;
-    if (in_lds)
-        for (int i = tid; i < n; i += 256) skeys[i] = gkeys[i];
-    const uint32_t* keys = in_lds ? skeys : gkeys;
-    int32_t* sel = a.sel + rg * K;
-    float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
-    __syncthreads();
+    const int64_t n_qt = (sq.n_q + kScoreTileQueries - 1) / kScoreTileQueries;
+    const int64_t qt = blockIdx.x / a.n_split;
+    const int split = blockIdx.x % a.n_split;
+    if (qt >= n_qt) return;
+    const int64_t q0 = qt * kScoreTileQueries;
+    const int n_valid = (int)(sq.n_q - q0 < kScoreTileQueries ? sq.n_q - q0 : kScoreTileQueries);
+    const int64_t nb_max = (sq.pos0 + q0 + n_valid - 1) / a.block_size;
+    const int64_t r_lo = (int64_t)split * a.split_blocks;
+    const int64_t r_hi = nb_max < r_lo + a.split_blocks ? nb_max : r_lo + a.split_blocks;
+    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int qq = lane >> 4;     // operand k-chunk; result group
+    const int m = lane & 15;      // operand row (4*group + head); result column
 
-    // selection rule: an entry is kept iff (key & pmask) > prefix, or
-    // (key & pmask) == prefix and fewer than krem such entries precede it
-    uint32_t prefix = 0, pmask = 0;   // n <= K: pmask 0 keeps everything
-    int krem = K;
-    if (n > K) {
-        const uint32_t k0 = keys[0];
-        uint32_t diff = 0;
-        for (int i = tid; i < n; i += 256) diff |= keys[i] ^ k0;
-        diff = wave_or(diff);
-        if (lane == 0) red[w] = diff;
+    // ---- the wavefront's four queries: A fragments, weights, candidates ----
+    bf16x8 af[4][4];
+    float4 wv[4];
+    int64_t nbq[4];
+    uint32_t* keys[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int qo = 4 * wave + j;
+        const bool ok = qo < n_valid;
+        const int64_t qi = q0 + (ok ? qo : 0);
+        const int64_t row = sq.q_offset + qi;
+        const int64_t t = sq.pos0 + qi;
+        index_query_fragments(a, row, t, qq, m, ok && split == 0, af[j]);
+        wv[j] = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
+        nbq[j] = ok ? t / a.block_size : 0;
+        keys[j] = a.part_key + ((row - a.key_row0) * kGroups + qq) * a.key_stride;
+    }
+    if (r_lo >= r_hi) return;                       // workgroup-uniform
+
+    // ---- store tiles: 64 rows x 16 chunks of 16 B, four chunks per thread
+    //      (rows past the range repeat its last row; their scores are not
+    //      written) ----
+    const uint16_t* store = a.store + sq.store_offset * kIdxDim;
+    auto gload = [&](int64_t r0, uint4 (&v)[4]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = tid + 256 * k;
+            const int64_t r = r0 + (c >> 4) < r_hi ? r0 + (c >> 4) : r_hi - 1;
+            v[k] = load16(store + r * kIdxDim + 8 * (c & 15));
+        }
+    };
+    auto lstore = [&](uint16_t* buf, const uint4 (&v)[4]) {
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+            const int c = tid + 256 * k;
+            *(uint4*)(buf + (c >> 4) * kStoreStrideU + 8 * (c & 15)) = v[k];
+        }
+    };
+    uint4 stage[4];
+    gload(r_lo, stage);
+    lstore(tiles[0], stage);
+    int cur = 0;
+    for (int64_t r0 = r_lo; r0 < r_hi; r0 += kStoreTile) {
+        const bool more = r0 + kStoreTile < r_hi;
+        if (more) gload(r0 + kStoreTile, stage);
         __syncthreads();
-        diff = red[0] | red[1] | red[2] | red[3];
-        prefix = k0;
-        pmask = 0xFFFFFFFFu;
-        if (diff != 0) {
-            const int hb = 31 - __builtin_clz(diff);
-            pmask = hb == 31 ? 0u : (0xFFFFFFFFu << (hb + 1));
-            prefix = k0 & pmask;
-            for (int hi = hb; hi >= 0;) {
-                const int lo = hi >= 7 ? hi - 7 : 0;
-                const int nbins = 1 << (hi - lo + 1);
-                const uint32_t dmask = (uint32_t)nbins - 1u;
-                for (int b = lane; b < 256; b += 64) hist[w][b] = 0u;
-                __syncthreads();
-                for (int i = tid; i < n; i += 256) {
-                    const uint32_t kk = keys[i];
-                    if ((kk & pmask) == prefix) atomicAdd(&hist[w][(kk >> lo) & dmask], 1u);
-                }
-                __syncthreads();
-                if (w == 0) {
-                    uint32_t h[4], tot = 0;
+        const uint16_t* buf = tiles[cur];
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        const int d = nbins - 1 - 4 * lane - j;
-                        h[j] = d >= 0 ? hist[0][d] + hist[1][d] + hist[2][d] + hist[3][d] : 0u;
-                        tot += h[j];
-                    }
-                    uint32_t incl = tot;
+        for (int sub = 0; sub < kStoreTile / 16; ++sub) {
+            const int64_t rb = r0 + 16 * sub;
+            if (rb >= r_hi) break;                  // workgroup-uniform
+            bf16x8 bf[4];
 #pragma unroll
-                    for (int o = 1; o < 64; o <<= 1) {
-                        const uint32_t up = __shfl_up(incl, o, 64);
-                        if (lane >= o) incl += up;
-                    }
-                    uint32_t above = incl - tot;
-                    int found = -1;
-                    uint32_t above_found = 0;
+            for (int kk = 0; kk < 4; ++kk)
+                bf[kk] = as_bf16x8(*(const uint4*)(buf + (16 * sub + m) * kStoreStrideU + 32 * kk + 8 * qq));
+            const int64_t r = rb + m;
 #pragma unroll
-                    for (int j = 0; j < 4; ++j) {
-                        if (found < 0 && h[j] > 0 && above + h[j] >= (uint32_t)krem) {
-                            found = nbins - 1 - 4 * lane - j;
-                            above_found = above;
-                        }
-                        above += h[j];
-                    }
-                    const uint64_t fm = __ballot(found >= 0);
-                    if (lane == (int)__builtin_ctzll(fm)) {
-                        s_digit = found;
-                        s_above = (int)above_found;
-                    }
-                }
-                __syncthreads();
-                prefix |= (uint32_t)s_digit << lo;
-                pmask |= dmask << lo;
-                krem -= s_above;
-                hi = lo - 1;
+            for (int j = 0; j < 4; ++j) {
+                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(af[j][kk], bf[kk], acc);
+                float s = wv[j].x * fmaxf(acc[0], 0.f);
+                s += wv[j].y * fmaxf(acc[1], 0.f);
+                s += wv[j].z * fmaxf(acc[2], 0.f);
+                s += wv[j].w * fmaxf(acc[3], 0.f);
+                if (r < nbq[j] && r < r_hi) keys[j][r] = score_key(s);
             }
         }
+        if (more) lstore(tiles[cur ^ 1], stage);
+        cur ^= 1;
     }
-    // ordered output: wavefront w owns entries [w*seg, (w+1)*seg)
+}
+
+// Top-k of one (query, group) from its score keys: the k largest, equal keys
+// to the lower block id, output in ascending block id, by four wavefronts.
+// The k-th largest key v and the number krem of entries equal to v that are
+// kept come from a radix select (8-bit digits from the highest bit in which
+// the keys differ, one histogram per wavefront per digit).  Short rows
+// (n <= kSelectStageKeys) are staged in LDS and selected there.  Long rows
+// first bound v from below with a sample (up to 2048 keys, groups of 16
+// consecutive keys spread over the row): the sample's j-th largest key tau,
+// j chosen so that about 3k keys are expected at or above it.  One
+// pass over the row then streams every key >= tau, with its block id, into
+// an LDS candidate list kept in block order; when a step would overflow it
+// (the sample misjudged a row whose high keys cluster), the list is cut to
+// its top k and the threshold raised, as in the fused kernel's streaming
+// top-k.  The list then holds every key >= v, so the select and the ordered
+// output run on it alone.  Only a row with fewer than k keys >= tau falls
+// back to selecting over the whole row in global memory.  Outputs are written in block order from four
+// contiguous segments whose offsets come from one exchange.
+constexpr int kSelectStageKeys = 4096;
+constexpr int kSelectSampleMax = 2048;     // sample keys (LDS words) for long rows
+
+__host__ __device__ constexpr int select_region(int k) { return ((k < 512 ? 512 : k) + 63) / 64 * 64; }
+// candidate list capacity: at least the 3k entries expected above the
+// sampled threshold plus a margin, and k plus one 4096-key step
+__host__ __device__ constexpr int select_capacity(int k) {
+    return 4 * select_region(k) > k + 4096 ? 4 * select_region(k) : k + 4096;
+}
+
+struct SelectShared {
+    uint32_t hist[4][256];
+    uint32_t red[4];
+    int cnt[2][4];
+    int digit, above, count;
+};
+
+// v (as prefix under pmask) and krem of the k-th largest of keys[0..n),
+// 1 <= k <= n.  Called by all 256 threads.
+__device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared& sh, uint32_t& prefix,
+                          uint32_t& pmask, int& krem) {
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    krem = k;
+    const uint32_t k0 = keys[0];
+    uint32_t diff = 0;
+    for (int i = tid; i < n; i += 256) diff |= keys[i] ^ k0;
+    diff = wave_or(diff);
+    if (lane == 0) sh.red[w] = diff;
+    __syncthreads();
+    diff = sh.red[0] | sh.red[1] | sh.red[2] | sh.red[3];
+    __syncthreads();
+    prefix = k0;
+    pmask = 0xFFFFFFFFu;
+    if (diff == 0) return;
+    const int hb = 31 - __builtin_clz(diff);
+    pmask = hb == 31 ? 0u : (0xFFFFFFFFu << (hb + 1));
+    prefix = k0 & pmask;
+    for (int hi = hb; hi >= 0;) {
+        const int lo = hi >= 7 ? hi - 7 : 0;
+        const int nbins = 1 << (hi - lo + 1);
+        const uint32_t dmask = (uint32_t)nbins - 1u;
+        for (int b = lane; b < 256; b += 64) sh.hist[w][b] = 0u;
+        __syncthreads();
+        int i = tid;
+        for (; i + 768 < n; i += 1024) {
+            const uint32_t k0 = keys[i], k1 = keys[i + 256], k2 = keys[i + 512], k3 = keys[i + 768];
+            if ((k0 & pmask) == prefix) atomicAdd(&sh.hist[w][(k0 >> lo) & dmask], 1u);
+            if ((k1 & pmask) == prefix) atomicAdd(&sh.hist[w][(k1 >> lo) & dmask], 1u);
+            if ((k2 & pmask) == prefix) atomicAdd(&sh.hist[w][(k2 >> lo) & dmask], 1u);
+            if ((k3 & pmask) == prefix) atomicAdd(&sh.hist[w][(k3 >> lo) & dmask], 1u);
+        }
+        for (; i < n; i += 256) {
+            const uint32_t kk = keys[i];
+            if ((kk & pmask) == prefix) atomicAdd(&sh.hist[w][(kk >> lo) & dmask], 1u);
+        }
+        __syncthreads();
+        if (w == 0) {
+            uint32_t h[4], tot = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const int d = nbins - 1 - 4 * lane - j;
+                h[j] = d >= 0 ? sh.hist[0][d] + sh.hist[1][d] + sh.hist[2][d] + sh.hist[3][d] : 0u;
+                tot += h[j];
+            }
+            uint32_t incl = tot;
+#pragma unroll
+            for (int o = 1; o < 64; o <<= 1) {
+                const uint32_t up = __shfl_up(incl, o, 64);
+                if (lane >= o) incl += up;
+            }
+            uint32_t above = incl - tot;
+            int found = -1;
+            uint32_t above_found = 0;
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                if (found < 0 && h[j] > 0 && above + h[j] >= (uint32_t)krem) {
+                    found = nbins - 1 - 4 * lane - j;
+                    above_found = above;
+                }
+                above += h[j];
+            }
+            const uint64_t fm = __ballot(found >= 0);
+            if (lane == (int)__builtin_ctzll(fm)) {
+                sh.digit = found;
+                sh.above = (int)above_found;
+            }
+        }
+        __syncthreads();
+        prefix |= (uint32_t)sh.digit << lo;
+        pmask |= dmask << lo;
+        krem -= sh.above;
+        hi = lo - 1;
+        __syncthreads();
+    }
+}
+
+// Keep rule over entries [0, n) of keys (block ids idx, or the entry index
+// when idx is null): key & pmask > prefix, or == prefix among the first krem
+// such; written in order to sel / ssc.
+__device__ void select_ordered_output(const uint32_t* keys, const int32_t* idx, int n, uint32_t prefix,
+                                      uint32_t pmask, int krem, int32_t* sel, float* ssc, SelectShared& sh) {
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const int seg = (n + 255) / 256 * 64;
     const int b0 = w * seg;
     const int b1 = b0 + seg < n ? b0 + seg : n;
@@ -507,15 +627,15 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
         n_eq += __popcll(__ballot(i < b1 && kk == prefix));
     }
     if (lane == 0) {
-        s_cnt[0][w] = n_gt;
-        s_cnt[1][w] = n_eq;
+        sh.cnt[0][w] = n_gt;
+        sh.cnt[1][w] = n_eq;
     }
     __syncthreads();
     // kept before this segment: every larger masked key, min(krem, equal ones)
     int out = 0, eq_seen = 0;
-    for (int j = 0; j < w; ++j) {
-        out += s_cnt[0][j];
-        eq_seen += s_cnt[1][j];
+    for (int jw = 0; jw < w; ++jw) {
+        out += sh.cnt[0][jw];
+        eq_seen += sh.cnt[1][jw];
     }
     out += eq_seen < krem ? eq_seen : krem;
     for (int base = b0; base < b1; base += 64) {
@@ -528,20 +648,189 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
         const uint64_t km = __ballot(keep);
         if (keep) {
             const int pos = out + (int)lanes_below(km);
-            sel[pos] = i;
+            sel[pos] = idx ? idx[i] : i;
             if (ssc) ssc[pos] = key_score(kk);
         }
         out += __popcll(km);
         eq_seen += __popcll(em);
     }
+}
+
+// LONG = false takes the rows of n <= kSelectStageKeys candidates, LONG =
+// true the others (two instantiations, so the short rows keep the smaller
+// register footprint)
+template <bool LONG>
+__global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexArgs a) {
+    extern __shared__ uint32_t lds_keys[];    // staged row, or candidate keys + block ids
+    __shared__ SelectShared sh;
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = blockIdx.x / kGroups;
+    const int g = blockIdx.x % kGroups;
+    if (qi >= sq.n_q) return;
+    const int64_t t = sq.pos0 + qi;
+    const int64_t row = sq.q_offset + qi;
+    const int64_t rg = row * kGroups + g;
+    const int n = (int)(t / a.block_size);
+    if ((n > kSelectStageKeys) != LONG) return;
+    const int K = a.topk;
+    const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
+    const uint32_t* gkeys = a.part_key + ((row - a.key_row0) * kGroups + g) * a.key_stride;
+    int32_t* sel = a.sel + rg * K;
+    float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
     const int total = n <= K ? n : K;
-    for (int j = total + tid; j < K; j += 256) {
-        sel[j] = -1;
-        if (ssc) ssc[j] = 0.0f;
+    for (int jj = total + tid; jj < K; jj += 256) {
+        sel[jj] = -1;
+        if (ssc) ssc[jj] = 0.0f;
     }
+
+    uint32_t prefix = 0, pmask = 0;   // pmask 0 keeps everything
+    int krem = K;
+    if (!LONG) {
+        for (int i = tid; i < n; i += 256) lds_keys[i] = gkeys[i];
+        __syncthreads();
+        if (n > K) radix_kth(lds_keys, n, K, sh, prefix, pmask, krem);
+        select_ordered_output(lds_keys, nullptr, n, prefix, pmask, krem, sel, ssc, sh);
+        return;
+    }
+    if (n <= K) {
+        select_ordered_output(gkeys, nullptr, n, prefix, pmask, krem, sel, ssc, sh);
+        return;
+    }
+
+    // ---- threshold tau: the j-th largest of a sample of S keys taken as
+    //      S/16 groups of 16 consecutive keys spread over the row ----
+    const int region = select_region(K);
+    const int smax = kSelectSampleMax < n / 4 ? kSelectSampleMax : n / 4;
+    const int S = smax / 16 * 16;
+    const int ngrp = S / 16;
+    for (int i = tid; i < S; i += 256) {
+        const int gi = i >> 4;
+        const int64_t start = (int64_t)gi * (n - 16) / (ngrp > 1 ? ngrp - 1 : 1);
+        lds_keys[i] = gkeys[start + (i & 15)];
+    }
+    __syncthreads();
+    const int64_t jt = ((int64_t)3 * K * S + n - 1) / n;
+    const int j = (int)(jt < 1 ? 1 : (jt > S ? S : jt));
+    uint32_t tau, tmask;
+    int trem;
+    radix_kth(lds_keys, S, j, sh, tau, tmask, trem);
+
+    // ---- candidates: the four wavefronts scan the row in 4096-key steps
+    //      (wavefront w takes quarter w of each, 16 loads in flight per
+    //      lane) and append the (key, block) pairs that pass the threshold
+    //      to one list in block order, counts exchanged once per step.  A
+    //      step that would overflow the list first compacts it to its top k
+    //      (block order kept) and raises the threshold to the k-th key: only
+    //      larger keys can still enter (an equal one would lose the tie).
+    //      The capacity leaves room for a whole step after a compaction. ----
+    const int cap = select_capacity(K);
+    uint32_t* ckeys = lds_keys;
+    int32_t* cidx = (int32_t*)(lds_keys + cap);
+    uint32_t thr = tau;
+    bool strict = false;          // accept key > thr (after a compaction) or key >= thr
+    int pool = 0, par = 0;
+    for (int base = 0; base < n; base += 4096) {
+        const int wb = base + 1024 * w;
+        uint32_t kv[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int i = wb + 64 * u + lane;
+            kv[u] = i < n ? gkeys[i] : 0u;
+        }
+        int pos[16];
+        int total = 0, off = 0;
+#pragma unroll 1
+        for (int attempt = 0; attempt < 2; ++attempt) {
+            int cw = 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int i = wb + 64 * u + lane;
+                const bool take = i < n && (strict ? kv[u] > thr : kv[u] >= thr);
+                const uint64_t m = __ballot(take);
+                pos[u] = take ? cw + (int)lanes_below(m) : -1;
+                cw += __popcll(m);
+            }
+            if (lane == 0) sh.cnt[par][w] = cw;
+            __syncthreads();
+            const int q0c = sh.cnt[par][0], q1c = sh.cnt[par][1], q2c = sh.cnt[par][2], q3c = sh.cnt[par][3];
+            par ^= 1;
+            total = q0c + q1c + q2c + q3c;
+            off = pool + (w > 0 ? q0c : 0) + (w > 1 ? q1c : 0) + (w > 2 ? q2c : 0);
+            if (pool + total <= cap) break;              // workgroup-uniform
+            // compact the list to its top k, in place and in order (one
+            // wavefront: every entry moves to an index <= its own)
+            uint32_t v, vm;
+            int vr;
+            radix_kth(ckeys, pool, K, sh, v, vm, vr);
+            if (w == 0) {
+                int out = 0, eq_seen = 0;
+                for (int i0 = 0; i0 < pool; i0 += 64) {
+                    const int i = i0 + lane;
+                    const uint32_t kk = i < pool ? ckeys[i] : 0u;
+                    const int32_t ii = i < pool ? cidx[i] : 0;
+                    const bool eq = i < pool && kk == v;
+                    const uint64_t em = __ballot(eq);
+                    const bool keep = i < pool && (kk > v || (eq && eq_seen + (int)lanes_below(em) < vr));
+                    const uint64_t km = __ballot(keep);
+                    wave_lds_sync();
+                    if (keep) {
+                        ckeys[out + (int)lanes_below(km)] = kk;
+                        cidx[out + (int)lanes_below(km)] = ii;
+                    }
+                    wave_lds_sync();
+                    out += __popcll(km);
+                    eq_seen += __popcll(em);
+                }
+            }
+            __syncthreads();
+            pool = K;
+            thr = v;
+            strict = true;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (pos[u] >= 0) {
+                ckeys[off + pos[u]] = kv[u];
+                cidx[off + pos[u]] = wb + 64 * u + lane;
+            }
+        }
+        pool += total;
+    }
+    __syncthreads();
+    const int c = pool;
+    if (c < K) {
+        // the sample's threshold was above the k-th key: select over the row
+        radix_kth(gkeys, n, K, sh, prefix, pmask, krem);
+        select_ordered_output(gkeys, nullptr, n, prefix, pmask, krem, sel, ssc, sh);
+        return;
+    }
+    radix_kth(ckeys, c, K, sh, prefix, pmask, krem);
+    select_ordered_output(ckeys, cidx, c, prefix, pmask, krem, sel, ssc, sh);
 }
 
 }  // namespace
+
+static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
+                                hipStream_t stream) {
+    const int64_t max_b = a.key_stride;
+    dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
+    // short rows: the staged row
+    const size_t lds_s = (size_t)(max_b < kSelectStageKeys ? max_b : kSelectStageKeys) * sizeof(uint32_t);
+    hipError_t e = hipFuncSetAttribute((const void*)index_select_kernel<false>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(index_select_kernel<false>, grid, dim3(256), lds_s, stream, seqs, a);
+    if ((e = hipGetLastError()) != hipSuccess || max_b <= kSelectStageKeys) return e;
+    // long rows: the sample, then the candidate keys and block ids
+    const int64_t cand = 2 * (int64_t)select_capacity(a.topk);
+    const int64_t samp = max_b / 4 < kSelectSampleMax ? max_b / 4 : kSelectSampleMax;
+    const size_t lds_l = (size_t)(cand > samp ? cand : samp) * sizeof(uint32_t);
+    e = hipFuncSetAttribute((const void*)index_select_kernel<true>,
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_l);
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(index_select_kernel<true>, grid, dim3(256), lds_l, stream, seqs, a);
+    return hipGetLastError();
+}
 
 size_t index_lds_bytes(int cap) { return (size_t)cap * 32u + 1024u; }
 
@@ -564,14 +853,18 @@ hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexA
     hipLaunchKernelGGL(index_score_kernel, grid, dim3(64), 0, stream, seqs, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    const int64_t max_b = a.key_stride;
-    const size_t lds = (size_t)(max_b < kSelectLdsKeys ? max_b : kSelectLdsKeys) * sizeof(uint32_t);
-    e = hipFuncSetAttribute((const void*)index_select_kernel,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    return launch_select(seqs, max_nq, a, stream);
+}
+
+hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
+                              hipStream_t stream) {
+    if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
+    const int64_t n_qt = (max_nq + kScoreTileQueries - 1) / kScoreTileQueries;
+    dim3 grid((unsigned)(n_qt * a.n_split), (unsigned)seqs.n);
+    hipLaunchKernelGGL(index_score_tile_kernel, grid, dim3(256), 0, stream, seqs, a);
+    hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    dim3 grid2((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
-    hipLaunchKernelGGL(index_select_kernel, grid2, dim3(256), lds, stream, seqs, a);
-    return hipGetLastError();
+    return launch_select(seqs, max_nq, a, stream);
 }
 
 }  // namespace sgqa

@@ -94,14 +94,23 @@ int check_seqs(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
 // ---------------------------------------------------------------------------
 // launch policy
 // ---------------------------------------------------------------------------
+enum class IndexMode { Fused, Split, Tiled };
+
 struct IndexPlan {
+    IndexMode mode = IndexMode::Fused;
     int n_split = 1;
     int split_blocks = 0;
     int cap = 0;
     int64_t key_stride = 0;
     int64_t rows = 0;           // packed query rows spanned (max q_offset + n_q)
+    int64_t chunk_rows = 0;     // tiled mode: query rows per key-workspace pass
     size_t ws = 0;
 };
+
+// key workspace of the tiled mode: query rows are processed in passes whose
+// keys (4 B per row, group and candidate) fit this budget
+constexpr size_t kTiledKeyBudget = (size_t)1 << 30;
+constexpr int kTiledSplitBlocks = 512;
 
 struct AttnPlan {
     int n_split = 1;
@@ -117,9 +126,15 @@ int64_t packed_rows(const sgqa_seq* s, int32_t n) {
     return r;
 }
 
-// Large query counts run the fused streaming kernel (one wavefront per
-// query); small ones (decode) spread each query's candidates over score
-// wavefronts and select from the score keys in the workspace.
+// Three ways to run the indexer and the selection:
+//  * Tiled (1024 queries or more): 16-query workgroups score candidate
+//    ranges against store tiles shared in LDS, keys go to the workspace in
+//    passes of at most kTiledKeyBudget bytes, one workgroup per (query,
+//    group) selects;
+//  * Split (fewer queries, long histories, keys within 1 GiB): each query's
+//    candidates are spread over score wavefronts, then the same selection;
+//  * Fused (the rest): one wavefront per query scores and keeps a streaming
+//    top-k in LDS; no workspace.
 IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     IndexPlan p;
     const int K = c->topk_blocks;
@@ -134,12 +149,29 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     p.n_split = 1;
     p.split_blocks = 0x7FFFFFF0;
     p.key_stride = 0;
-    const int64_t stride = (max_b + 15) / 16 * 16;
+    // key rows are 256 B x an odd number apart, so the rows that score and
+    // select workgroups touch at the same time spread over the memory
+    // channels instead of all starting at one power-of-two alignment
+    int64_t stride = std::max<int64_t>(64, (max_b + 63) / 64 * 64);
+    if ((stride / 64) % 2 == 0) stride += 64;
+    if (total_q >= 1024) {
+        const size_t row_bytes = (size_t)sgqa::kGroups * stride * 4;
+        int64_t chunk = (int64_t)(kTiledKeyBudget / row_bytes) / 16 * 16;
+        chunk = std::max<int64_t>(16, std::min<int64_t>(chunk, (p.rows + 15) / 16 * 16));
+        p.mode = IndexMode::Tiled;
+        p.chunk_rows = chunk;
+        p.key_stride = stride;
+        p.split_blocks = kTiledSplitBlocks;
+        p.n_split = (int)std::max<int64_t>(1, (max_b + kTiledSplitBlocks - 1) / kTiledSplitBlocks);
+        p.ws = align_up((size_t)chunk * row_bytes);
+        return p;
+    }
     const size_t key_bytes = (size_t)p.rows * sgqa::kGroups * stride * 4;
-    if (total_q == 0 || total_q >= 1024 || max_b <= K || key_bytes > ((size_t)1 << 30)) return p;
+    if (total_q == 0 || max_b <= K || key_bytes > ((size_t)1 << 30)) return p;
     int64_t split = std::min<int64_t>((4096 + total_q - 1) / total_q, std::max<int64_t>(1, max_b / 256));
     int64_t per = (max_b + split - 1) / split;
     per = (per + 15) / 16 * 16;
+    p.mode = IndexMode::Split;
     p.split_blocks = (int)per;
     p.n_split = (int)((max_b + per - 1) / per);
     p.key_stride = stride;
@@ -274,14 +306,47 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     rope_table(c, a.theta);
     a.part_key = nullptr;
     a.key_stride = p.key_stride;
+    a.key_row0 = 0;
     if (p.key_stride > 0) a.part_key = (uint32_t*)ws;
+    if (p.mode == IndexMode::Tiled) {
+        // passes over query rows [r0, r0 + chunk_rows): each sequence cut to
+        // the pass's rows, keys addressed relative to r0
+        for (int64_t r0 = 0; r0 < p.rows; r0 += p.chunk_rows) {
+            a.key_row0 = r0;
+            const int64_t r1 = r0 + p.chunk_rows;
+            for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
+                const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
+                sgqa::SeqTable tab;
+                tab.n = 0;
+                tab.pad_ = 0;
+                int64_t mx = 0;
+                for (int32_t i = first; i < first + cnt; ++i) {
+                    const sgqa_seq& q = s[i];
+                    const int64_t lo = std::max(q.q_offset, r0);
+                    const int64_t hi = std::min(q.q_offset + q.n_q, r1);
+                    if (lo >= hi) continue;
+                    sgqa::DevSeq& d = tab.s[tab.n++];
+                    d.q_offset = lo;
+                    d.n_q = hi - lo;
+                    d.pos0 = q.pos0 + (lo - q.q_offset);
+                    d.kv_offset = q.kv_offset;
+                    d.store_offset = q.store_offset;
+                    mx = std::max(mx, hi - lo);
+                }
+                if (tab.n == 0) continue;
+                hipError_t e = sgqa::launch_index_tiled(tab, mx, a, st);
+                if (e != hipSuccess) return hip_fail(e, "index_topk launch");
+            }
+        }
+        return SGQA_OK;
+    }
     for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
         const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
         sgqa::SeqTable tab;
         const int64_t mx = fill_table(tab, s, first, cnt, [](const sgqa_seq& q) { return q.n_q; });
         if (tab.n == 0) continue;
-        hipError_t e = p.key_stride > 0 ? sgqa::launch_index_split(tab, mx, a, st)
-                                        : sgqa::launch_index_topk(tab, mx, a, st);
+        hipError_t e = p.mode == IndexMode::Split ? sgqa::launch_index_split(tab, mx, a, st)
+                                                  : sgqa::launch_index_topk(tab, mx, a, st);
         if (e != hipSuccess) return hip_fail(e, "index_topk launch");
     }
     return SGQA_OK;

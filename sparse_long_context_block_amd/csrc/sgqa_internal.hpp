@@ -60,8 +60,9 @@ struct IndexArgs {
     int32_t* sel;
     float* sel_scores;          // may be null
     uint16_t* q_hat_out;        // may be null
-    uint32_t* part_key;         // split calls: score keys [rows, G, key_stride]
+    uint32_t* part_key;         // split calls: score keys [rows - key_row0, G, key_stride]
     int64_t key_stride;
+    int64_t key_row0;           // first query row held in part_key
     int32_t block_size;
     int32_t topk;               // K
     int32_t cap;                // per-row LDS buffer capacity C (fused kernel)
@@ -107,6 +108,12 @@ hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexAr
 // decode-sized calls: score wavefronts over candidate splits, then one
 // select workgroup per (query, group)
 hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
+                              hipStream_t stream);
+// prefill-sized calls: 16-query workgroups score candidate ranges of
+// a.split_blocks blocks against store tiles shared through LDS, then one
+// select workgroup per (query, group)
+constexpr int kScoreTileQueries = 16;
+hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
                               hipStream_t stream);
 hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                               hipStream_t stream);

@@ -96,6 +96,16 @@ def _decode(name, n_seqs=64, lo=131072, hi=262144, cap=262144, B=8, K=512, seed=
     return Workload(name, B, K, seqs, prebuilt=True, seed=seed)
 
 
+def _multi(name, parts, B, K) -> Workload:
+    """Sequences (n_q, pos0) packed back to back in rows, caches and store."""
+    seqs, row, kv, st = [], 0, 0, 0
+    for n, pos0 in parts:
+        T = pos0 + n
+        seqs.append(SeqLayout(row, n, pos0, kv, T, st, T // B))
+        row, kv, st = row + n, kv + T, st + T // B
+    return Workload(name, B, K, seqs, prebuilt=True)
+
+
 def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
     if name == "tiny_prefill_256":
         w = _prefill(name, 256, 8, 16)
@@ -109,6 +119,8 @@ def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
         w = _decode(name, seed=seed)
     elif name == "chunk_1m":
         w = _prefill(name, 8192, 8, 512, pos0=1_040_384)
+    elif name == "multi_b1_passes":              # ragged sequences, tiled index in passes (tests)
+        w = _multi(name, [(700, 180_000), (1500, 0), (333, 120_003)], B=1, K=64)
     elif name == "decode_small":                 # 8 sequences, split paths (tests)
         w = _decode(name, n_seqs=8, lo=8192, hi=40000, cap=40960, seed=seed)
     elif name.startswith("chunk_"):              # chunk_<pos0>_<n>[_b<B>_k<K>] (tests)

@@ -163,11 +163,19 @@ def test_workspace_size_invalid_args_is_zero(L):
     assert sg.workspace_size(sg.config(), [_good_seq()], 7) == 0
 
 
-def test_prefill_needs_no_workspace(L):
-    # large prefills run unsplit: no scratch memory
+def test_prefill_key_workspace(L):
+    # prefills of 1024+ queries keep 4-byte score keys per (row, group,
+    # candidate) in the workspace; compression and attention need none
     cfg = sg.config()
-    assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_FORWARD) == 0
+    # key rows: 1023 candidates padded to 1088 (64 x an odd count)
+    assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_INDEX_TOPK) == 8192 * 4 * 1088 * 4
+    assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_FORWARD) == 8192 * 4 * 1088 * 4
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_COMPRESS) == 0
+    assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_SPARSE_ATTN) == 0
+    # long prefills run in passes over query rows: the keys stay within 1 GiB
+    cfg1 = sg.config(block_size=1, topk_blocks=2048)
+    ws = sg.workspace_size(cfg1, [sg.seq(65536, block_size=1)], sg.OP_FORWARD)
+    assert (1 << 20) * 16 <= ws <= (1 << 30)
 
 
 def test_binding_rejects_wrong_tensors():

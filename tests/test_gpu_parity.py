@@ -57,6 +57,13 @@ def test_chunk_on_existing_cache_unaligned():
     _run_and_check("chunk_1003_997_b8_k64", n_rows=64)
 
 
+def test_tiled_index_passes_over_ragged_sequences():
+    # 2533 queries at B = 1 over histories up to 180K tokens: the tiled
+    # indexer runs in about seven key-workspace passes whose row boundaries
+    # cut through the sequences
+    _run_and_check("multi_b1_passes", n_rows=24, check_all_store=False)
+
+
 def test_decode_split_paths():
     st = _run_and_check("decode_small", n_rows=1, check_all_store=True)
     assert st["rows"] == 8
