@@ -12,17 +12,20 @@
 // Gather mapping (one workgroup of 4 wavefronts per (query, group, split)):
 // the query's token list (selected blocks in ascending order, then the
 // current block up to t) is cut into 16-token chunks; wavefront w takes
-// chunks w, w+4, ...  Per chunk it
+// chunks w, w+4, ..., with the rows of its next chunk in flight while the
+// current one is processed (two register sets alternate).  Per chunk it
 //   * loads the 16 K rows straight into the A operand of S^T = K Q^T
 //     (v_mfma_f32_16x16x32_bf16; the group's 16 heads are the N dimension,
 //     so every gathered K/V byte serves all 16 heads);
 //   * runs the online softmax on the result layout, where each lane holds 4
-//     tokens of one head: the exponentiated tile is directly the B operand
-//     (P^T) of O^T = V^T P^T (v_mfma_f32_16x16x16bf16_1k), no LDS round trip;
-//   * transposes the 16 V rows through a small per-wave LDS tile to form the
-//     A operand V^T.
+//     tokens of one head, with a lazily raised reference max: the
+//     exponentiated tile is directly the B operand (P^T) of O^T = V^T P^T
+//     (v_mfma_f32_16x16x16bf16_1k), no LDS round trip;
+//   * writes the 16 V rows to a per-wave LDS tile and reads the A operand
+//     V^T back with transposed reads.
 // The four wavefronts' (max, sum, O) are merged in LDS; a split call (decode:
-// few queries) writes partials that attn_merge_kernel combines.
+// few queries) writes partials that attn_merge_kernel combines.  Workgroups
+// run group-major.
 #include "sgqa_internal.hpp"
 
 namespace sgqa {
@@ -30,9 +33,42 @@ namespace {
 
 using namespace dev;
 
-constexpr int kVtStride = 20;                       // bf16 per V^T row: 16 tokens + pad
+constexpr int kGVStride = kHeadDim + 8;             // bf16 per row of a wave's V tile (100 dwords)
 constexpr int kWaveBufFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;
+static_assert(16 * kGVStride * 2 <= kWaveBufFloats * 4, "a wave's V tile fits its merge buffer");
 constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kLazyRescale = 8.0f;          // log2 units
+
+__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
+    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
+    bf16x2 v;
+    v[0] = (__bf16)a;
+    v[1] = (__bf16)b;
+    return __builtin_bit_cast(uint32_t, v);
+}
+
+// Reductions across lanes through v_permlane16_swap / v_permlane32_swap
+// (VALU ops: no LDS round trip as with ds_bpermute): xor16 combines lanes
+// l and l ^ 16, xor32 lanes l and l ^ 32.
+__device__ __forceinline__ float xor16_max(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xor16_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+__device__ __forceinline__ float xor32_max(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+
+__device__ __forceinline__ float xor32_sum(float x) {
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
+    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
 
 __device__ __forceinline__ int64_t token_at(int64_t i, int n_sel, int shift_b, int B,
                                             const int32_t* sel, int64_t cur_first) {
@@ -41,15 +77,114 @@ __device__ __forceinline__ int64_t token_at(int64_t i, int n_sel, int shift_b, i
     return cur_first + (i - ((int64_t)n_sel << shift_b));
 }
 
+// K/V rows of chunk c for this lane (token 16c + m; K dims 32kk + 8qq, V
+// dims 8(qq + 4j)); chunks past the token list read the current token, whose
+// values stay finite and are masked
+struct GatherRegs {
+    uint4 k[6], v[6];
+};
+
+__device__ __forceinline__ GatherRegs gather_chunk(int64_t c, int m, int qq, int64_t n_tok, int n_sel, int shift_b,
+                                                   int B, const int32_t* sel_lds, int64_t cur_first, int64_t t,
+                                                   const uint16_t* kbase, const uint16_t* vbase) {
+    constexpr int64_t kRowStride = (int64_t)kGroups * kHeadDim;
+    const int64_t ti = 16 * c + m;
+    int64_t tok = ti < n_tok ? token_at(ti, n_sel, shift_b, B, sel_lds, cur_first) : t;
+    tok = tok < 0 ? 0 : (tok > t ? t : tok);   // malformed ids never read past the cache
+    const uint16_t* krow = kbase + tok * kRowStride + 8 * qq;
+    const uint16_t* vrow = vbase + tok * kRowStride;
+    GatherRegs r;
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) r.k[kk] = *(const uint4*)(krow + 32 * kk);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) r.v[j] = *(const uint4*)(vrow + 8 * (qq + 4 * j));
+    return r;
+}
+
+struct GatherState {
+    f32x4 o[12];       // O^T: dims 16nt + 4qq + i of head m
+    float m_use;       // reference max of head m (raw score units), raised lazily
+    float lsum;        // this lane's tokens' sum relative to it
+};
+
+struct GatherLane {
+    uint16_t* vtile;   // this wavefront's V tile in LDS
+    int tr_off;        // this lane's transposed-read offset in it
+    int m, qq;
+    int64_t n_tok;
+    float sl2;
+};
+
+// One 16-token chunk.  The V rows go into the wavefront's tile (100-dword
+// rows: the b128 row writes are conflict-free); the O^T A operand comes out
+// of it with ds_read_b64_tr_b16: lane 16G + 4i + c supplies row 4G + i, dims
+// 4c..4c+3 of a 16-dim block, and lane 16G + j receives dim j of tokens
+// 4G..4G+3 -- row j, k = 4G + i of v_mfma_f32_16x16x16bf16_1k.  The softmax
+// runs on the S^T result layout (lane: tokens 16c + 4qq + i of head m) with
+// a lazily raised reference max; the exponentiated tile is the B operand.
+__device__ __forceinline__ void gather_step(GatherState& st, const GatherRegs& r, const bf16x8 (&qf)[6], int64_t c,
+                                            const GatherLane& gl) {
+    f32x4 s = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int kk = 0; kk < 6; ++kk) s = mfma_16x16x32(as_bf16x8(r.k[kk]), qf[kk], s);
+#pragma unroll
+    for (int j = 0; j < 6; ++j) *(uint4*)(gl.vtile + gl.m * kGVStride + 8 * (gl.qq + 4 * j)) = r.v[j];
+    float xv[4];
+    float tmax = -INFINITY;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const bool valid = 16 * c + 4 * gl.qq + i < gl.n_tok;
+        xv[i] = valid ? s[i] : -INFINITY;
+        tmax = fmaxf(tmax, xv[i]);
+    }
+    tmax = xor32_max(xor16_max(tmax));
+    const float sl2 = gl.sl2;
+    const float ts = tmax * sl2;
+    float ms = st.m_use * sl2;
+    const bool need = ts > ms + kLazyRescale;
+    if (__ballot(need)) {
+        const float alpha = need ? __builtin_amdgcn_exp2f(ms - ts) : 1.0f;
+#pragma unroll
+        for (int nt = 0; nt < 12; ++nt) st.o[nt] *= alpha;
+        st.lsum *= alpha;
+        if (need) st.m_use = tmax;
+        ms = st.m_use * sl2;
+    }
+    float p[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        p[i] = __builtin_amdgcn_exp2f(xv[i] * sl2 - ms);   // ms finite: token 16c is valid
+        st.lsum += p[i];
+    }
+    uint2 pb;
+    pb.x = pack_bf16(p[0], p[1]);
+    pb.y = pack_bf16(p[2], p[3]);
+    const i16x4 pbv = as_i16x4(pb);
+    wave_lds_sync();
+#pragma unroll
+    for (int nt = 0; nt < 12; ++nt) {
+        const i16x4 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(gl.vtile + gl.tr_off + 16 * nt));
+        st.o[nt] = mfma_16x16x16(av, pbv, st.o[nt]);
+    }
+    wave_lds_sync();
+}
+
 __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArgs a) {
     extern __shared__ int32_t sel_lds[];                        // [K]
     __shared__ float wave_buf[4][kWaveBufFloats];
     __shared__ int s_nsel;
 
+    // group-major order: the workgroups in flight read one group's K/V
+    // (disjoint cache lines per group), a quarter of the cache's footprint,
+    // which keeps the re-read rows of neighbouring queries in the last-level
+    // cache
     const DevSeq sq = seqs.s[blockIdx.y];
-    const int split = blockIdx.x % a.n_split;
-    const int g = (blockIdx.x / a.n_split) % kGroups;
-    const int64_t qi = blockIdx.x / (a.n_split * kGroups);
+    const int64_t per_group = (int64_t)(gridDim.x / kGroups);
+    const int g = (int)(blockIdx.x / per_group);
+    const int64_t rem = blockIdx.x - g * per_group;
+    const int split = (int)(rem % a.n_split);
+    const int64_t qi = rem / a.n_split;
     if (qi >= sq.n_q) return;
     const int64_t t = sq.pos0 + qi;
     const int64_t row = sq.q_offset + qi;
@@ -84,85 +219,42 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
 #pragma unroll
     for (int kk = 0; kk < 6; ++kk) qf[kk] = as_bf16x8(*(const uint4*)(qrow + 32 * kk));
 
-    float mrow = -INFINITY;   // running max of head m, log2 domain
-    float lsum = 0.f;
-    f32x4 o[12];
+    GatherState st;
 #pragma unroll
-    for (int nt = 0; nt < 12; ++nt) o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
-
-    uint16_t* vt = (uint16_t*)wave_buf[w];
+    for (int nt = 0; nt < 12; ++nt) st.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
+    st.m_use = -INFINITY;
+    st.lsum = 0.f;
+    GatherLane gl;
+    gl.vtile = (uint16_t*)wave_buf[w];
+    gl.tr_off = (4 * qq + ((lane >> 2) & 3)) * kGVStride + 4 * (lane & 3);
+    gl.m = m;
+    gl.qq = qq;
+    gl.n_tok = n_tok;
+    gl.sl2 = a.scale_log2;
     const uint16_t* kbase = a.k + (sq.kv_offset * kGroups + g) * kHeadDim;
     const uint16_t* vbase = a.v + (sq.kv_offset * kGroups + g) * kHeadDim;
-    constexpr int64_t kRowStride = (int64_t)kGroups * kHeadDim;
 
-    for (int64_t c = c_lo + w; c < c_hi; c += 4) {
-        // this lane's token for the K/V loads
-        const int64_t ti = 16 * c + m;
-        int64_t tok = ti < n_tok ? token_at(ti, n_sel, shift_b, B, sel_lds, cur_first) : t;
-        tok = tok < 0 ? 0 : (tok > t ? t : tok);   // malformed ids never read past the cache
-        const uint16_t* krow = kbase + tok * kRowStride + 8 * qq;
-        const uint16_t* vrow = vbase + tok * kRowStride;
-        uint4 kr[6], vr[6];
-#pragma unroll
-        for (int kk = 0; kk < 6; ++kk) kr[kk] = *(const uint4*)(krow + 32 * kk);
-#pragma unroll
-        for (int j = 0; j < 6; ++j) vr[j] = *(const uint4*)(vrow + 8 * (qq + 4 * j));
-
-        // S^T[token][head] = K Q^T
-        f32x4 s = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 6; ++kk) s = mfma_16x16x32(as_bf16x8(kr[kk]), qf[kk], s);
-
-        // online softmax; lane holds tokens 16c + 4qq + i of head m
-        float xv[4];
-        float tmax = -INFINITY;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const bool valid = 16 * c + 4 * qq + i < n_tok;
-            xv[i] = valid ? s[i] * a.scale_log2 : -INFINITY;
-            tmax = fmaxf(tmax, xv[i]);
+    // two register sets alternate: one chunk's rows are in flight while the
+    // other chunk is processed
+    if (c_lo + w < c_hi) {
+        GatherRegs ra = gather_chunk(c_lo + w, m, qq, n_tok, n_sel, shift_b, B, sel_lds, cur_first, t, kbase, vbase);
+        for (int64_t c = c_lo + w; c < c_hi; c += 8) {
+            const GatherRegs rb =
+                gather_chunk(c + 4, m, qq, n_tok, n_sel, shift_b, B, sel_lds, cur_first, t, kbase, vbase);
+            gather_step(st, ra, qf, c, gl);
+            if (c + 4 >= c_hi) break;
+            ra = gather_chunk(c + 8, m, qq, n_tok, n_sel, shift_b, B, sel_lds, cur_first, t, kbase, vbase);
+            gather_step(st, rb, qf, c + 4, gl);
         }
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 16, 64));
-        tmax = fmaxf(tmax, __shfl_xor(tmax, 32, 64));
-        const float mnew = fmaxf(mrow, tmax);           // finite: token 16c is valid
-        const float alpha = exp2f(mrow - mnew);
-        float p[4], psum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            p[i] = exp2f(xv[i] - mnew);
-            psum += p[i];
-        }
-        psum += __shfl_xor(psum, 16, 64);
-        psum += __shfl_xor(psum, 32, 64);
-        lsum = lsum * alpha + psum;
-        mrow = mnew;
-#pragma unroll
-        for (int nt = 0; nt < 12; ++nt) o[nt] *= alpha;
-
-        // V^T tile: lane wrote token m, dims 8(qq+4j) .. +7
-#pragma unroll
-        for (int j = 0; j < 6; ++j) {
-            const uint32_t w4[4] = {vr[j].x, vr[j].y, vr[j].z, vr[j].w};
-            const int d0 = 8 * (qq + 4 * j);
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                vt[(d0 + 2 * e) * kVtStride + m] = (uint16_t)(w4[e] & 0xFFFFu);
-                vt[(d0 + 2 * e + 1) * kVtStride + m] = (uint16_t)(w4[e] >> 16);
-            }
-        }
-        wave_lds_sync();
-
-        uint2 pb;
-        pb.x = f32_to_bf16(p[0]) | (f32_to_bf16(p[1]) << 16);
-        pb.y = f32_to_bf16(p[2]) | (f32_to_bf16(p[3]) << 16);
-        const i16x4 pbv = as_i16x4(pb);
-#pragma unroll
-        for (int nt = 0; nt < 12; ++nt) {
-            const uint2 av = *(const uint2*)(vt + (16 * nt + m) * kVtStride + 4 * qq);
-            o[nt] = mfma_16x16x16(as_i16x4(av), pbv, o[nt]);
-        }
-        wave_lds_sync();
     }
+    float lsum = st.lsum;
+    f32x4 (&o)[12] = st.o;
+    const float m_use = st.m_use;
+    const float sl2 = a.scale_log2;
+    // the head's sum over its four token lanes; the merge takes the max in
+    // log2 units
+    lsum = xor32_sum(xor16_sum(lsum));
+    const float mrow = m_use * sl2;
 
     // ---- merge the four wavefronts ----
     __syncthreads();
@@ -224,19 +316,10 @@ constexpr int kVTileElems = kHeadDim * kVtStrideU;
 constexpr int kBufElems = kKTileElems + kVTileElems;
 constexpr int kVSlots = (kHeadDim / 2) * (kTileTok / 8);   // (dim pair, token octet) slots of one V tile
 constexpr int kOutStride = kHeadDim + 8;      // bf16 per staged output row (400 B)
-constexpr float kLazyRescale = 8.0f;          // log2 units
-
 __device__ __forceinline__ f32x16 mfma_32x32x16(bf16x8 a, bf16x8 b, f32x16 c) {
     return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
-__device__ __forceinline__ uint32_t pack_bf16(float a, float b) {
-    typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2;
-    bf16x2 v;
-    v[0] = (__bf16)a;
-    v[1] = (__bf16)b;
-    return __builtin_bit_cast(uint32_t, v);
-}
 
 // Staging of one 32-token tile (12 dwords per thread).  Threads below
 // kVSlots each carry one V slot -- one dim pair of eight tokens, loaded as
@@ -353,18 +436,6 @@ __device__ __forceinline__ f32x16 tile_scores(const uint16_t* buf, const bf16x8 
 #pragma unroll
     for (int kk = 0; kk < 12; ++kk) s = mfma_32x32x16(as_bf16x8(*(const uint4*)(kl + 16 * kk)), qf[kk], s);
     return s;
-}
-
-// Reductions across the two 32-lane halves of a wavefront through
-// v_permlane32_swap (a VALU op: no LDS round trip as with ds_bpermute).
-__device__ __forceinline__ float xor32_max(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
-}
-
-__device__ __forceinline__ float xor32_sum(float x) {
-    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(x), false, false);
-    return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
 struct UnionState {
