@@ -814,13 +814,23 @@ static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const Inde
                                 hipStream_t stream) {
     const int64_t max_b = a.key_stride;
     dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
-    // short rows: the staged row
-    const size_t lds_s = (size_t)(max_b < kSelectStageKeys ? max_b : kSelectStageKeys) * sizeof(uint32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)index_select_kernel<false>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(index_select_kernel<false>, grid, dim3(256), lds_s, stream, seqs, a);
-    if ((e = hipGetLastError()) != hipSuccess || max_b <= kSelectStageKeys) return e;
+    // short rows (skipped when every sequence's first query already has a
+    // long row): the staged row
+    int64_t min_b = INT64_MAX;
+    for (int i = 0; i < seqs.n; ++i) {
+        const int64_t b = seqs.s[i].pos0 / a.block_size;
+        min_b = b < min_b ? b : min_b;
+    }
+    hipError_t e = hipSuccess;
+    if (min_b <= kSelectStageKeys) {
+        const size_t lds_s = (size_t)(max_b < kSelectStageKeys ? max_b : kSelectStageKeys) * sizeof(uint32_t);
+        e = hipFuncSetAttribute((const void*)index_select_kernel<false>,
+                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
+        if (e != hipSuccess) return e;
+        hipLaunchKernelGGL(index_select_kernel<false>, grid, dim3(256), lds_s, stream, seqs, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (max_b <= kSelectStageKeys) return e;
     // long rows: the sample, then the candidate keys and block ids
     const int64_t cand = 2 * (int64_t)select_capacity(a.topk);
     const int64_t samp = max_b / 4 < kSelectSampleMax ? max_b / 4 : kSelectSampleMax;
