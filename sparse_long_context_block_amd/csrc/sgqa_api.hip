@@ -168,7 +168,9 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     }
     const size_t key_bytes = (size_t)p.rows * sgqa::kGroups * stride * 4;
     if (total_q == 0 || max_b <= K || key_bytes > ((size_t)1 << 30)) return p;
-    int64_t split = std::min<int64_t>((4096 + total_q - 1) / total_q, std::max<int64_t>(1, max_b / 256));
+    // about 8192 score wavefronts, at least 256 candidate blocks each (measured
+    // on the 64-sequence decode against 2048..16384)
+    int64_t split = std::min<int64_t>((8192 + total_q - 1) / total_q, std::max<int64_t>(1, max_b / 256));
     int64_t per = (max_b + split - 1) / split;
     per = (per + 15) / 16 * 16;
     p.mode = IndexMode::Split;
@@ -202,7 +204,10 @@ AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     const int64_t max_chunks =
         ((int64_t)c->topk_blocks * c->block_size + c->block_size + 15) / 16;
     const int64_t units = total_q * sgqa::kGroups;
-    int64_t want = units > 0 ? (1024 + units - 1) / units : 1;
+    // split only calls too small to give each CU a workgroup (measured on the
+    // 64-sequence decode: 256 unsplit workgroups beat 1024 split ones and the
+    // merge they need)
+    int64_t want = units > 0 ? (256 + units - 1) / units : 1;
     int64_t split = std::min<int64_t>({want, std::max<int64_t>(1, max_chunks / 8),
                                        (int64_t)sgqa::kMaxAttnSplits});
     if (split <= 1) {
