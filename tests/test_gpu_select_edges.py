@@ -1,0 +1,96 @@
+"""Selection edge cases whose exact answer follows from the selection rule
+alone (page "Step-5-Preview: Sparse Reads Are Not a Compressed KV Cache",
+section "Selection is a weighted ReLU score, not attention softmax": the k
+highest scores among blocks r < floor(t/B), equal scores to the lower block
+id), so no oracle run is needed:
+
+* every score equal (indexer weights zero): every row keeps blocks
+  0..min(n, k)-1.  Long rows (more than 4096 candidates) then start from a
+  threshold every key passes, so the candidate list overflows and is cut to
+  its top k, repeatedly -- the compaction path, with all keys tied;
+* a row whose only positive scores sit exactly at the positions the
+  long-row select samples (2048 blocks in groups of 16, k = 3072): the
+  sampled threshold admits fewer than k keys, so the select must fall back
+  to a radix over the whole row; the answer is those 2048 blocks plus the
+  1024 lowest-numbered others (score 0, ties to the lower id).
+
+Inputs are seeded random tensors (or constructed exactly), written straight
+into the indexer's inputs; only the index step runs.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_long_context_block_amd as sg
+
+from .gpu_checks import log
+
+pytestmark = pytest.mark.gpu
+
+
+def _run_index(cfg, seqs, n_rows, q_idx, w, store):
+    K = cfg.topk_blocks
+    sel = torch.full((n_rows, 4, K), -7, dtype=torch.int32, device="cuda")
+    ssc = torch.full((n_rows, 4, K), 7.0, dtype=torch.float32, device="cuda")
+    sg.index_topk(cfg, seqs, q_idx, w, store, sel, sel_scores=ssc)
+    torch.cuda.synchronize()
+    return sel.cpu().numpy(), ssc.cpu().numpy()
+
+
+@pytest.mark.parametrize("n_q,pos0,B,K", [
+    (1, 20000, 1, 3072),          # decode-sized call: split scoring, long row
+    (1100, 16000, 1, 512),        # tiled call, long rows
+    (1100, 160000, 8, 512),       # tiled call at B = 8, 20000+ candidates per row
+    (3, 300000, 8, 2048),         # decode-sized, several queries, k = 2048
+])
+def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
+    log("case equal scores", n_q, pos0, B, K)
+    gen = torch.Generator(device="cuda").manual_seed(5)
+    cache = pos0 + n_q
+    q_idx = torch.randn(n_q, 4, 4, 128, generator=gen, device="cuda").to(torch.bfloat16)
+    w = torch.zeros(n_q, 4, 4, dtype=torch.float32, device="cuda")
+    store = torch.randn(cache // B, 128, generator=gen, device="cuda").to(torch.bfloat16)
+    cfg = sg.config(block_size=B, topk_blocks=K)
+    sel, ssc = _run_index(cfg, [sg.seq(n_q, pos0=pos0, block_size=B)], n_q, q_idx, w, store)
+    n = (pos0 + np.arange(n_q)) // B                       # candidates per row
+    m = np.minimum(n, K)
+    j = np.arange(K)[None, :]
+    exp = np.where(j < m[:, None], j, -1).astype(np.int32)  # [n_q, K]
+    assert (sel == exp[:, None, :]).all()
+    assert (ssc == 0.0).all()
+
+
+def test_sample_overestimate_falls_back_exactly():
+    B, K = 1, 3072
+    t = 16383                        # one query; n = 16383 candidate blocks
+    n = t // B
+    # the long-row select's sample: S keys in S/16 groups of 16 consecutive
+    # keys, group g starting at g * (n - 16) // (S/16 - 1)
+    S = min(2048, n // 4) // 16 * 16
+    ngrp = S // 16
+    hot = sorted({(g * (n - 16)) // (ngrp - 1) + i for g in range(ngrp) for i in range(16)})
+    assert len(hot) == S and hot[-1] < n
+    log("case sampled-threshold fallback", n, K, len(hot))
+    # u: zero on the rotary span (dims 0..31), one elsewhere, so q_hat . u
+    # does not depend on positions; hot store rows are u, all others zero
+    u = torch.zeros(128, dtype=torch.float32)
+    u[32:] = 1.0
+    store = torch.zeros(t + 1, 128, dtype=torch.float32)
+    store[hot] = u
+    q_idx = torch.zeros(1, 4, 4, 128, dtype=torch.float32)
+    q_idx[0, :, 0] = u               # head 0 of every group
+    w = torch.zeros(1, 4, 4, dtype=torch.float32)
+    w[0, :, 0] = 1.0
+    cfg = sg.config(block_size=B, topk_blocks=K)
+    sel, ssc = _run_index(cfg, [sg.seq(1, pos0=t, block_size=B)], 1,
+                          q_idx.to(torch.bfloat16).cuda(), w.cuda(),
+                          store.to(torch.bfloat16).cuda())
+    hot_set = set(hot)
+    cold = [r for r in range(n) if r not in hot_set][:K - len(hot)]
+    exp = np.array(sorted(hot + cold), dtype=np.int32)
+    is_hot = np.isin(exp, hot)
+    for g in range(4):
+        assert (sel[0, g] == exp).all()
+        assert (ssc[0, g][~is_hot] == 0.0).all()
+        hs = ssc[0, g][is_hot]
+        assert (hs > 100.0).all() and (hs == hs[0]).all()
