@@ -677,23 +677,22 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
     const uint32_t* gkeys = a.part_key + ((row - a.key_row0) * kGroups + g) * a.key_stride;
     int32_t* sel = a.sel + rg * K;
     float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
-    const int total = n <= K ? n : K;
-    for (int jj = total + tid; jj < K; jj += 256) {
-        sel[jj] = -1;
-        if (ssc) ssc[jj] = 0.0f;
+    if (n <= K) {
+        // every candidate is selected, in block order, then -1 padding
+        for (int jj = tid; jj < K; jj += 256) {
+            sel[jj] = jj < n ? jj : -1;
+            if (ssc) ssc[jj] = jj < n ? key_score(gkeys[jj]) : 0.0f;
+        }
+        return;
     }
 
-    uint32_t prefix = 0, pmask = 0;   // pmask 0 keeps everything
+    uint32_t prefix = 0, pmask = 0;
     int krem = K;
     if (!LONG) {
         for (int i = tid; i < n; i += 256) lds_keys[i] = gkeys[i];
         __syncthreads();
-        if (n > K) radix_kth(lds_keys, n, K, sh, prefix, pmask, krem);
+        radix_kth(lds_keys, n, K, sh, prefix, pmask, krem);
         select_ordered_output(lds_keys, nullptr, n, prefix, pmask, krem, sel, ssc, sh);
-        return;
-    }
-    if (n <= K) {
-        select_ordered_output(gkeys, nullptr, n, prefix, pmask, krem, sel, ssc, sh);
         return;
     }
 
