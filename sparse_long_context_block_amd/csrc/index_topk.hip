@@ -1,4 +1,4 @@
-// Steps 2 and 3: indexer scores and the causal top-k block selection, fused.
+// Steps 2 and 3: indexer scores and the causal top-k block selection.
 //
 // Page "Step-5-Preview: Sparse Reads Are Not a Compressed KV Cache",
 // section "Selection is a weighted ReLU score, not attention softmax": for
@@ -8,25 +8,30 @@
 // softmax; only r < floor(t/8) compete for the K slots, equal scores go to
 // the lower block id.  Section "A configured million-token window is not a
 // validated million-token launch" shows why the [G*N, R] FP32 score matrix
-// must not be materialised (512 GiB per rank at 1M tokens): here no score
-// leaves the wavefront that computed it unless it may still be selected.
+// must not be materialised (512 GiB per rank at 1M tokens): the fused kernel
+// keeps scores in the wavefront that computed them, the other paths write
+// 4-byte keys for a bounded number of query rows at a time.
 //
-// Mapping (one wavefront per query and candidate split):
+// Common MFMA mapping (every score kernel):
 //   * the query's 4 groups x 4 heads of q_hat are exactly the 16 rows of a
 //     v_mfma_f32_16x16x32_bf16 A operand, so the four groups share every
-//     store row the wavefront reads;
-//   * a 16-block tile of the store is the B operand, read straight from HBM /
-//     L2 into registers (16 B per lane per 32-wide k step), two tiles ahead;
+//     store row read;
+//   * a 16-block tile of the store is the B operand (16 B per lane per
+//     32-wide k step);
 //   * the result layout puts all 4 heads of (group, block) in one lane, so
-//     the weighted ReLU sum is in-lane;
-//   * each group's selection is a streaming top-k: an LDS buffer of `cap`
-//     (key, block) entries in ascending block order, an acceptance threshold
-//     (the current k-th key) and a radix-select compaction back to k entries
-//     when the buffer is nearly full.  Keys are order-preserving uint32 images
-//     of the fp32 scores (-0 folded into +0); ties keep the earlier entry,
-//     which is the lower block id because blocks arrive in ascending order.
-// A decode-sized call (few queries) splits each query's candidates over
-// several wavefronts; index_merge_kernel then selects from their lists.
+//     the weighted ReLU sum is in-lane.
+// Keys are order-preserving uint32 images of the fp32 scores (-0 folded into
+// +0).  Three paths (the host picks one per call):
+//   * index_topk_kernel -- one wavefront per query, store tiles straight from
+//     memory two tiles ahead, and per group a streaming top-k: an LDS buffer
+//     of `cap` (key, block) entries in ascending block order, an acceptance
+//     threshold (the current k-th key) and a radix-select compaction back to
+//     k entries when the buffer is nearly full; ties keep the earlier entry,
+//     which is the lower block id because blocks arrive in ascending order;
+//   * index_score_kernel + index_select_kernel -- decode-sized calls spread
+//     each query's candidates over many score wavefronts that write keys;
+//   * index_score_tile_kernel + index_select_kernel -- calls of 1024+
+//     queries score 16 queries per workgroup against store tiles in LDS.
 #include "sgqa_internal.hpp"
 
 namespace sgqa {
