@@ -503,7 +503,8 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
 }
 
 // Top-k of one (query, group) from its score keys: the k largest, equal keys
-// to the lower block id, output in ascending block id, by four wavefronts.
+// to the lower block id, output in ascending block id, by NW wavefronts (4;
+// 16 for the long rows of calls with few rows).
 // The k-th largest key v and the number krem of entries equal to v that are
 // kept come from a radix select (8-bit digits from the highest bit in which
 // the keys differ, one histogram per wavefront per digit).  Short rows
@@ -524,31 +525,38 @@ constexpr int kSelectSampleMax = 2048;     // sample keys (LDS words) for long r
 
 __host__ __device__ constexpr int select_region(int k) { return ((k < 512 ? 512 : k) + 63) / 64 * 64; }
 // candidate list capacity: at least the 3k entries expected above the
-// sampled threshold plus a margin, and k plus one 4096-key step
-__host__ __device__ constexpr int select_capacity(int k) {
-    return 4 * select_region(k) > k + 4096 ? 4 * select_region(k) : k + 4096;
+// sampled threshold plus a margin, and k plus one step of 1024 keys per
+// wavefront
+__host__ __device__ constexpr int select_capacity(int k, int nw) {
+    return 4 * select_region(k) > k + 1024 * nw ? 4 * select_region(k) : k + 1024 * nw;
 }
 
+// shared state of a select workgroup of NW wavefronts
+template <int NW>
 struct SelectShared {
-    uint32_t hist[4][256];
-    uint32_t red[4];
-    int cnt[2][4];
+    uint32_t hist[NW][256];
+    uint32_t red[NW];
+    int cnt[2][NW];
     int digit, above, count;
 };
 
 // v (as prefix under pmask) and krem of the k-th largest of keys[0..n),
-// 1 <= k <= n.  Called by all 256 threads.
-__device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared& sh, uint32_t& prefix,
+// 1 <= k <= n.  Called by all 64*NW threads.
+template <int NW>
+__device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared<NW>& sh, uint32_t& prefix,
                           uint32_t& pmask, int& krem) {
+    constexpr int NT = 64 * NW;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     krem = k;
     const uint32_t k0 = keys[0];
     uint32_t diff = 0;
-    for (int i = tid; i < n; i += 256) diff |= keys[i] ^ k0;
+    for (int i = tid; i < n; i += NT) diff |= keys[i] ^ k0;
     diff = wave_or(diff);
     if (lane == 0) sh.red[w] = diff;
     __syncthreads();
-    diff = sh.red[0] | sh.red[1] | sh.red[2] | sh.red[3];
+    diff = 0;
+#pragma unroll
+    for (int j = 0; j < NW; ++j) diff |= sh.red[j];
     __syncthreads();
     prefix = k0;
     pmask = 0xFFFFFFFFu;
@@ -563,14 +571,14 @@ __device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared& sh, 
         for (int b = lane; b < 256; b += 64) sh.hist[w][b] = 0u;
         __syncthreads();
         int i = tid;
-        for (; i + 768 < n; i += 1024) {
-            const uint32_t k0 = keys[i], k1 = keys[i + 256], k2 = keys[i + 512], k3 = keys[i + 768];
+        for (; i + 3 * NT < n; i += 4 * NT) {
+            const uint32_t k0 = keys[i], k1 = keys[i + NT], k2 = keys[i + 2 * NT], k3 = keys[i + 3 * NT];
             if ((k0 & pmask) == prefix) atomicAdd(&sh.hist[w][(k0 >> lo) & dmask], 1u);
             if ((k1 & pmask) == prefix) atomicAdd(&sh.hist[w][(k1 >> lo) & dmask], 1u);
             if ((k2 & pmask) == prefix) atomicAdd(&sh.hist[w][(k2 >> lo) & dmask], 1u);
             if ((k3 & pmask) == prefix) atomicAdd(&sh.hist[w][(k3 >> lo) & dmask], 1u);
         }
-        for (; i < n; i += 256) {
+        for (; i < n; i += NT) {
             const uint32_t kk = keys[i];
             if ((kk & pmask) == prefix) atomicAdd(&sh.hist[w][(kk >> lo) & dmask], 1u);
         }
@@ -580,7 +588,11 @@ __device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared& sh, 
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d = nbins - 1 - 4 * lane - j;
-                h[j] = d >= 0 ? sh.hist[0][d] + sh.hist[1][d] + sh.hist[2][d] + sh.hist[3][d] : 0u;
+                uint32_t hs = 0;
+                if (d >= 0)
+#pragma unroll
+                    for (int ww = 0; ww < NW; ++ww) hs += sh.hist[ww][d];
+                h[j] = hs;
                 tot += h[j];
             }
             uint32_t incl = tot;
@@ -618,10 +630,11 @@ __device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared& sh, 
 // Keep rule over entries [0, n) of keys (block ids idx, or the entry index
 // when idx is null): key & pmask > prefix, or == prefix among the first krem
 // such; written in order to sel / ssc.
+template <int NW>
 __device__ void select_ordered_output(const uint32_t* keys, const int32_t* idx, int n, uint32_t prefix,
-                                      uint32_t pmask, int krem, int32_t* sel, float* ssc, SelectShared& sh) {
+                                      uint32_t pmask, int krem, int32_t* sel, float* ssc, SelectShared<NW>& sh) {
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const int seg = (n + 255) / 256 * 64;
+    const int seg = (n + 64 * NW - 1) / (64 * NW) * 64;
     const int b0 = w * seg;
     const int b1 = b0 + seg < n ? b0 + seg : n;
     int n_gt = 0, n_eq = 0;
@@ -664,10 +677,11 @@ __device__ void select_ordered_output(const uint32_t* keys, const int32_t* idx, 
 // LONG = false takes the rows of n <= kSelectStageKeys candidates, LONG =
 // true the others (two instantiations, so the short rows keep the smaller
 // register footprint)
-template <bool LONG>
-__global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexArgs a) {
+template <bool LONG, int NW>
+__global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, IndexArgs a) {
+    constexpr int NT = 64 * NW;
     extern __shared__ uint32_t lds_keys[];    // staged row, or candidate keys + block ids
-    __shared__ SelectShared sh;
+    __shared__ SelectShared<NW> sh;
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = blockIdx.x / kGroups;
     const int g = blockIdx.x % kGroups;
@@ -684,7 +698,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
     float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
     if (n <= K) {
         // every candidate is selected, in block order, then -1 padding
-        for (int jj = tid; jj < K; jj += 256) {
+        for (int jj = tid; jj < K; jj += NT) {
             sel[jj] = jj < n ? jj : -1;
             if (ssc) ssc[jj] = jj < n ? key_score(gkeys[jj]) : 0.0f;
         }
@@ -694,7 +708,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
     uint32_t prefix = 0, pmask = 0;
     int krem = K;
     if (!LONG) {
-        for (int i = tid; i < n; i += 256) lds_keys[i] = gkeys[i];
+        for (int i = tid; i < n; i += NT) lds_keys[i] = gkeys[i];
         __syncthreads();
         radix_kth(lds_keys, n, K, sh, prefix, pmask, krem);
         select_ordered_output(lds_keys, nullptr, n, prefix, pmask, krem, sel, ssc, sh);
@@ -707,7 +721,7 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
     const int smax = kSelectSampleMax < n / 4 ? kSelectSampleMax : n / 4;
     const int S = smax / 16 * 16;
     const int ngrp = S / 16;
-    for (int i = tid; i < S; i += 256) {
+    for (int i = tid; i < S; i += NT) {
         const int gi = i >> 4;
         const int64_t start = (int64_t)gi * (n - 16) / (ngrp > 1 ? ngrp - 1 : 1);
         lds_keys[i] = gkeys[start + (i & 15)];
@@ -719,21 +733,21 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
     int trem;
     radix_kth(lds_keys, S, j, sh, tau, tmask, trem);
 
-    // ---- candidates: the four wavefronts scan the row in 4096-key steps
-    //      (wavefront w takes quarter w of each, 16 loads in flight per
+    // ---- candidates: the wavefronts scan the row in steps of 1024 keys
+    //      per wavefront (wavefront w takes the w-th 1024, 16 loads in flight per
     //      lane) and append the (key, block) pairs that pass the threshold
     //      to one list in block order, counts exchanged once per step.  A
     //      step that would overflow the list first compacts it to its top k
     //      (block order kept) and raises the threshold to the k-th key: only
     //      larger keys can still enter (an equal one would lose the tie).
     //      The capacity leaves room for a whole step after a compaction. ----
-    const int cap = select_capacity(K);
+    const int cap = select_capacity(K, NW);
     uint32_t* ckeys = lds_keys;
     int32_t* cidx = (int32_t*)(lds_keys + cap);
     uint32_t thr = tau;
     bool strict = false;          // accept key > thr (after a compaction) or key >= thr
     int pool = 0, par = 0;
-    for (int base = 0; base < n; base += 4096) {
+    for (int base = 0; base < n; base += 1024 * NW) {
         const int wb = base + 1024 * w;
         uint32_t kv[16];
 #pragma unroll
@@ -756,10 +770,15 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
             }
             if (lane == 0) sh.cnt[par][w] = cw;
             __syncthreads();
-            const int q0c = sh.cnt[par][0], q1c = sh.cnt[par][1], q2c = sh.cnt[par][2], q3c = sh.cnt[par][3];
+            total = 0;
+            off = pool;
+#pragma unroll
+            for (int j = 0; j < NW; ++j) {
+                const int cj = sh.cnt[par][j];
+                total += cj;
+                off += j < w ? cj : 0;
+            }
             par ^= 1;
-            total = q0c + q1c + q2c + q3c;
-            off = pool + (w > 0 ? q0c : 0) + (w > 1 ? q1c : 0) + (w > 2 ? q2c : 0);
             if (pool + total <= cap) break;              // workgroup-uniform
             // compact the list to its top k, in place and in order (one
             // wavefront: every entry moves to an index <= its own)
@@ -814,36 +833,48 @@ __global__ __launch_bounds__(256) void index_select_kernel(SeqTable seqs, IndexA
 
 }  // namespace
 
+template <int NW>
+static hipError_t launch_select_long(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a, hipStream_t stream) {
+    const int64_t max_b = a.key_stride;
+    const int64_t cand = 2 * (int64_t)select_capacity(a.topk, NW);
+    const int64_t samp = max_b / 4 < kSelectSampleMax ? max_b / 4 : kSelectSampleMax;
+    const size_t lds = (size_t)(cand > samp ? cand : samp) * sizeof(uint32_t);
+    hipError_t e = hipFuncSetAttribute((const void*)index_select_kernel<true, NW>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+    dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
+    hipLaunchKernelGGL((index_select_kernel<true, NW>), grid, dim3(64 * NW), lds, stream, seqs, a);
+    return hipGetLastError();
+}
+
 static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
                                 hipStream_t stream) {
     const int64_t max_b = a.key_stride;
     dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
     // short rows (skipped when every sequence's first query already has a
     // long row): the staged row
-    int64_t min_b = INT64_MAX;
+    int64_t min_b = INT64_MAX, rows = 0;
     for (int i = 0; i < seqs.n; ++i) {
         const int64_t b = seqs.s[i].pos0 / a.block_size;
         min_b = b < min_b ? b : min_b;
+        rows += seqs.s[i].n_q * kGroups;
     }
     hipError_t e = hipSuccess;
     if (min_b <= kSelectStageKeys) {
         const size_t lds_s = (size_t)(max_b < kSelectStageKeys ? max_b : kSelectStageKeys) * sizeof(uint32_t);
-        e = hipFuncSetAttribute((const void*)index_select_kernel<false>,
+        e = hipFuncSetAttribute((const void*)index_select_kernel<false, 4>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
         if (e != hipSuccess) return e;
-        hipLaunchKernelGGL(index_select_kernel<false>, grid, dim3(256), lds_s, stream, seqs, a);
+        hipLaunchKernelGGL((index_select_kernel<false, 4>), grid, dim3(256), lds_s, stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (max_b <= kSelectStageKeys) return e;
-    // long rows: the sample, then the candidate keys and block ids
-    const int64_t cand = 2 * (int64_t)select_capacity(a.topk);
-    const int64_t samp = max_b / 4 < kSelectSampleMax ? max_b / 4 : kSelectSampleMax;
-    const size_t lds_l = (size_t)(cand > samp ? cand : samp) * sizeof(uint32_t);
-    e = hipFuncSetAttribute((const void*)index_select_kernel<true>,
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_l);
-    if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(index_select_kernel<true>, grid, dim3(256), lds_l, stream, seqs, a);
-    return hipGetLastError();
+    // long rows: a few rows (decode) get sixteen wavefronts each, so each
+    // row's scan has four times the loads in flight
+    // (the candidate list then takes k plus one 16384-key step: k <= 1024
+    // keeps it within LDS)
+    return rows <= 1024 && a.topk <= 1024 ? launch_select_long<16>(seqs, max_nq, a, stream)
+                                          : launch_select_long<4>(seqs, max_nq, a, stream);
 }
 
 size_t index_lds_bytes(int cap) { return (size_t)cap * 32u + 1024u; }

@@ -8,11 +8,11 @@ id), so no oracle run is needed:
   0..min(n, k)-1.  Long rows (more than 4096 candidates) then start from a
   threshold every key passes, so the candidate list overflows and is cut to
   its top k, repeatedly -- the compaction path, with all keys tied;
-* a row whose only positive scores sit exactly at the positions the
-  long-row select samples (2048 blocks in groups of 16, k = 3072): the
-  sampled threshold admits fewer than k keys, so the select must fall back
-  to a radix over the whole row; the answer is those 2048 blocks plus the
-  1024 lowest-numbered others (score 0, ties to the lower id).
+* a row whose only positive scores sit at positions the long-row select
+  samples (2048 blocks at k = 3072, 512 at k = 1024): the sampled threshold
+  admits fewer than k keys, so the select must fall back to a radix over
+  the whole row; the answer is those blocks plus the lowest-numbered others
+  (score 0, ties to the lower id).
 
 Inputs are seeded random tensors (or constructed exactly), written straight
 into the indexer's inputs; only the index step runs.
@@ -42,6 +42,7 @@ def _run_index(cfg, seqs, n_rows, q_idx, w, store):
     (1100, 16000, 1, 512),        # tiled call, long rows
     (1100, 160000, 8, 512),       # tiled call at B = 8, 20000+ candidates per row
     (3, 300000, 8, 2048),         # decode-sized, several queries, k = 2048
+    (2, 40000, 1, 512),           # decode-sized, k <= 1024: 16-wavefront select
 ])
 def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
     log("case equal scores", n_q, pos0, B, K)
@@ -60,16 +61,20 @@ def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
     assert (ssc == 0.0).all()
 
 
-def test_sample_overestimate_falls_back_exactly():
-    B, K = 1, 3072
+@pytest.mark.parametrize("K,hot_groups", [(3072, 128), (1024, 32)])
+def test_sample_overestimate_falls_back_exactly(K, hot_groups):
+    B = 1
     t = 16383                        # one query; n = 16383 candidate blocks
     n = t // B
     # the long-row select's sample: S keys in S/16 groups of 16 consecutive
-    # keys, group g starting at g * (n - 16) // (S/16 - 1)
+    # keys, group g starting at g * (n - 16) // (S/16 - 1); the first
+    # hot_groups groups hold the only positive scores, fewer than k of them
+    # but more than the sample rank the threshold is taken at
     S = min(2048, n // 4) // 16 * 16
     ngrp = S // 16
-    hot = sorted({(g * (n - 16)) // (ngrp - 1) + i for g in range(ngrp) for i in range(16)})
-    assert len(hot) == S and hot[-1] < n
+    hot = sorted({(g * (n - 16)) // (ngrp - 1) + i for g in range(hot_groups) for i in range(16)})
+    assert len(hot) == 16 * hot_groups < K and hot[-1] < n
+    assert len(hot) >= -(-3 * K * S // n)
     log("case sampled-threshold fallback", n, K, len(hot))
     # u: zero on the rotary span (dims 0..31), one elsewhere, so q_hat . u
     # does not depend on positions; hot store rows are u, all others zero
