@@ -17,6 +17,8 @@ prefill_64k            prefill N=65,536                            8       512
 prefill_64k_b1         prefill N=65,536 (ablation)                 1       2,048
 decode_64x256k         64 sequences x 1 new token, lengths U[131072,262144],
                        262,144-token allocation each               8       512
+decode_loop_64x256k    the same 64 sequences decoded for 80 consecutive
+                       tokens (lengths U[131072,262064])           8       512
 chunk_1m               8,192 queries at 1,040,384..1,048,575 over a
                        1,048,576-token cache                       8       512
 =====================  ==========================================  ======  =====
@@ -66,6 +68,13 @@ class Workload:
     store_q8: bool = True
     seed: int = 0
     notes: str = ""
+    # decode loops: seqs holds loop_steps x loop_seqs entries, step-major;
+    # entry (s, i) is sequence i's one query at its s-th step
+    loop_steps: int = 0
+    loop_seqs: int = 0
+
+    def step_seqs(self, s: int) -> List[SeqLayout]:
+        return self.seqs[s * self.loop_seqs:(s + 1) * self.loop_seqs]
 
     @property
     def n_q_total(self) -> int:
@@ -96,6 +105,19 @@ def _decode(name, n_seqs=64, lo=131072, hi=262144, cap=262144, B=8, K=512, seed=
     return Workload(name, B, K, seqs, prebuilt=True, seed=seed)
 
 
+def _decode_loop(name, n_seqs, lo, hi, cap, steps, B=8, K=512, seed=0) -> Workload:
+    """n_seqs sequences decoded for `steps` consecutive tokens: sequence i
+    starts with a cache of L_i - 1 tokens (L_i uniform in [lo, hi]) and its
+    step s appends position L_i - 1 + s; query rows i * steps + s."""
+    assert hi + steps <= cap
+    L = seq_lengths(seed, n_seqs, lo, hi)
+    seqs = [SeqLayout(i * steps + st, 1, int(L[i]) - 1 + st, i * cap, cap, i * (cap // B), cap // B)
+            for st in range(steps) for i in range(n_seqs)]
+    w = Workload(name, B, K, seqs, prebuilt=True, seed=seed)
+    w.loop_steps, w.loop_seqs = steps, n_seqs
+    return w
+
+
 def _multi(name, parts, B, K) -> Workload:
     """Sequences (n_q, pos0) packed back to back in rows, caches and store."""
     seqs, row, kv, st = [], 0, 0, 0
@@ -121,6 +143,10 @@ def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
         w = _prefill(name, 8192, 8, 512, pos0=1_040_384)
     elif name == "multi_b1_passes":              # ragged sequences, tiled index in passes (tests)
         w = _multi(name, [(700, 180_000), (1500, 0), (333, 120_003)], B=1, K=64)
+    elif name == "decode_loop_small":            # 8 sequences x 12 decode steps (tests)
+        w = _decode_loop(name, 8, 8192, 40960 - 16, 40960, 12, seed=seed)
+    elif name == "decode_loop_64x256k":          # 64 sequences x 80 decode steps
+        w = _decode_loop(name, 64, 131072, 262144 - 80, 262144, 80, seed=seed)
     elif name == "decode_small":                 # 8 sequences, split paths (tests)
         w = _decode(name, n_seqs=8, lo=8192, hi=40000, cap=40960, seed=seed)
     elif name.startswith("chunk_"):              # chunk_<pos0>_<n>[_b<B>_k<K>] (tests)
