@@ -36,13 +36,15 @@ H, G, D, HI, DI = 64, 4, 192, 4, 128
 # algorithmic work of one step (what the method must compute / move)
 # ---------------------------------------------------------------------------
 
-def work_model(wl) -> dict:
+def work_model(wl, seqs=None) -> dict:
+    """Work of one step over `seqs` (default: the workload's sequences)."""
     B, K = wl.block_size, wl.topk
     attn_pairs = 0          # sum over (t, g) of |U_t,g|
     idx_pairs = 0           # sum over t of b(t) (per group)
     comp_blocks = 0
     store_bytes = 0
-    for s in wl.seqs:
+    seqs = wl.seqs if seqs is None else seqs
+    for s in seqs:
         t = np.arange(s.pos0, s.pos0 + s.n_q, dtype=np.int64)
         b = t // B
         u = np.minimum(b, K) * B + (t - b * B) + 1
@@ -56,7 +58,7 @@ def work_model(wl) -> dict:
         "index_flops": idx_pairs * G * HI * 2 * DI,
         "index_store_bytes": store_bytes,                     # store read once per query
         "compress_bytes": comp_blocks * (B * (DI * 2 + DI * 4) + DI * 2),
-        "queries": sum(s.n_q for s in wl.seqs),
+        "queries": sum(s.n_q for s in seqs),
     }
 
 
@@ -211,19 +213,28 @@ def main() -> int:
 
     import sparse_long_context_block_amd as sg
     from synth import workloads as W
-    from tests.gpu_checks import lib_seqs, prepare
+    from tests.gpu_checks import lib_seq, lib_seqs, prepare
 
     wl = W.make(args.workload)
     print(f"[bench] workload {wl.name}: preparing inputs", file=sys.stderr, flush=True)
     di, cfg = prepare(wl)
-    seqs = lib_seqs(wl)
+    # a decode loop advances one token per step (step k decodes loop step k,
+    # wrapping around; repeating a step recomputes the same outputs)
+    if wl.loop_steps:
+        loop = [[lib_seq(s) for s in wl.step_seqs(k)] for k in range(wl.loop_steps)]
+        ws_n = max(sg.workspace_size(cfg, sq, sg.OP_FORWARD) for sq in loop)
+    else:
+        loop = [lib_seqs(wl)]
+        ws_n = sg.workspace_size(cfg, loop[0], sg.OP_FORWARD)
     stream = torch.cuda.current_stream()
-    ws_n = sg.workspace_size(cfg, seqs, sg.OP_FORWARD)
     ws = torch.empty(max(ws_n, 1) + 256, dtype=torch.uint8, device="cuda")
     ws_view = ws[(-ws.data_ptr()) % 256:][:max(ws_n, 1)]
+    step_no = [0]
 
     def step():
-        sg.forward(cfg, seqs, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
+        sq = loop[step_no[0] % len(loop)]
+        step_no[0] += 1
+        sg.forward(cfg, sq, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
                    di["sel"], di["q"], di["k"], di["v"], di["out"], lse=di["lse"],
                    ws=ws_view, stream=stream)
 
@@ -243,12 +254,15 @@ def main() -> int:
     torch.cuda.synchronize()
     print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
           flush=True)
+    first_timed = step_no[0]
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
+    timed = [loop[k % len(loop)] for k in range(first_timed, step_no[0])]
+    seqs = timed[-1]                     # per-op timings and the roofline use the last step
 
     reps = args.kernel_reps
     k_ms = {
@@ -265,7 +279,14 @@ def main() -> int:
         torch.cuda.synchronize()
         del src, dst
 
-    wm = work_model(wl)
+    if wl.loop_steps:
+        last = (step_no[0] - 1) % len(loop)
+        wm = work_model(wl, wl.step_seqs(last))
+        # throughput over the timed loop steps (each step one query per sequence)
+        wm_loop_queries = sum(sum(s.n_q for s in sq) for sq in timed)
+    else:
+        wm = work_model(wl)
+        wm_loop_queries = None
     decode = wl.name.startswith("decode")
     dense = sum(min(s.n_q, max(0, 4 * wl.topk * wl.block_size - s.pos0)) if s.n_q >= 64 else 0
                 for s in wl.seqs)
@@ -278,7 +299,8 @@ def main() -> int:
                 "kernel": "sparse_attn_kernel + attn_merge_kernel (one sgqa_sparse_attn call)",
                 "algorithmic_bytes_per_launch": wm["attn_gather_bytes"],
                 "launch_ms": k_ms["sparse_attn"]}
-        value, unit = wm["queries"] / (ms_step * 1e-3), "queries/s"
+        queries = wm_loop_queries / args.steps if wm_loop_queries else wm["queries"]
+        value, unit = queries / (ms_step * 1e-3), "queries/s"
     else:
         achieved = wm["attn_flops"] / (k_ms["sparse_attn"] * 1e-3) / 1e12
         kern = (f"attn_union_kernel<{wl.block_size.bit_length() - 1}>" if dense == wm["queries"]
@@ -304,7 +326,13 @@ def main() -> int:
     }
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        res["cpu_baseline"] = cpu_baseline(wl)
+        if wl.loop_steps:
+            import dataclasses
+            one = dataclasses.replace(wl, seqs=wl.step_seqs((step_no[0] - 1) % len(loop)),
+                                      loop_steps=0, loop_seqs=0)
+            res["cpu_baseline"] = cpu_baseline(one)
+        else:
+            res["cpu_baseline"] = cpu_baseline(wl)
     print(json.dumps(res), flush=True)
     return 0
 

@@ -124,12 +124,14 @@ enum {
  * Bytes of workspace the operation needs for these arguments (0 when none),
  * or 0 with sgqa_last_error() set when the arguments are invalid.  What it
  * holds: for SGQA_OP_INDEX_TOPK, the 4-byte score keys of every candidate of
- * the query rows processed at once -- calls of 1024+ queries work in passes
- * over query rows sized to at most 1 GiB, smaller calls with long histories
- * keep all rows (at most 1 GiB, else they need none); for
- * SGQA_OP_SPARSE_ATTN, the per-split partial outputs of calls whose queries
- * are spread over several workgroups (decode-sized calls); SGQA_OP_FORWARD
- * needs the larger of the two (the steps run one after the other).
+ * the queries processed at once -- calls of 1024+ queries work in passes of
+ * at most 1 GiB of keys, smaller calls with long histories keep the queries
+ * of 64 consecutive seqs[] entries at a time (at most 1 GiB, else they need
+ * none); for SGQA_OP_SPARSE_ATTN, the per-split partial outputs of calls
+ * whose queries are spread over several workgroups (decode-sized calls), for
+ * 64 consecutive seqs[] entries at a time.  The size depends on the entries'
+ * n_q, pos0 and order, not on their q_offset.  SGQA_OP_FORWARD needs the
+ * larger of the two (the steps run one after the other).
  */
 size_t sgqa_workspace_size(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                            int32_t op);

@@ -369,7 +369,7 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
     if (r_lo >= r_hi) return;
     const float4 wv = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
     const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
-    uint32_t* keys = a.part_key + ((row - a.key_row0) * kGroups + qq) * a.key_stride;
+    uint32_t* keys = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
     uint4 b0[4], b1[4];
     auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * kIdxDim; };
     {
@@ -444,7 +444,7 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
         index_query_fragments(a, row, t, qq, m, ok && split == 0, af[j]);
         wv[j] = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
         nbq[j] = ok ? t / a.block_size : 0;
-        keys[j] = a.part_key + ((row - a.key_row0) * kGroups + qq) * a.key_stride;
+        keys[j] = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
     }
     if (r_lo >= r_hi) return;                       // workgroup-uniform
 
@@ -693,7 +693,7 @@ __global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, In
     if ((n > kSelectStageKeys) != LONG) return;
     const int K = a.topk;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
-    const uint32_t* gkeys = a.part_key + ((row - a.key_row0) * kGroups + g) * a.key_stride;
+    const uint32_t* gkeys = a.part_key + ((sq.ws_row + qi) * kGroups + g) * a.key_stride;
     int32_t* sel = a.sel + rg * K;
     float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
     if (n <= K) {

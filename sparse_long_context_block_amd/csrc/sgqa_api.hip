@@ -102,8 +102,8 @@ struct IndexPlan {
     int split_blocks = 0;
     int cap = 0;
     int64_t key_stride = 0;
-    int64_t rows = 0;           // packed query rows spanned (max q_offset + n_q)
-    int64_t chunk_rows = 0;     // tiled mode: query rows per key-workspace pass
+    int64_t rows = 0;           // key-workspace rows: queries of the largest launch
+    int64_t chunk_rows = 0;     // tiled mode: queries per launch (one key pass)
     size_t ws = 0;
 };
 
@@ -119,11 +119,20 @@ struct AttnPlan {
     size_t ws = 0;
 };
 
-int64_t packed_rows(const sgqa_seq* s, int32_t n) {
-    int64_t r = 0;
-    for (int32_t i = 0; i < n; ++i)
-        if (s[i].n_q > 0) r = std::max(r, s[i].q_offset + s[i].n_q);
-    return r;
+// Workspace rows are numbered per launch table (DevSeq::ws_row), so a
+// workspace holds the queries of the largest table, whatever the queries'
+// row offsets.  With tables of kMaxSeqsPerLaunch sequences in call order,
+// that is the largest sum of nq(seq) over such a group.
+template <typename Rows>
+int64_t max_launch_rows(const sgqa_seq* s, int32_t n, Rows nq) {
+    int64_t best = 0;
+    for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
+        const int32_t end = std::min<int32_t>(n, first + sgqa::kMaxSeqsPerLaunch);
+        int64_t sum = 0;
+        for (int32_t i = first; i < end; ++i) sum += std::max<int64_t>(0, nq(s[i]));
+        best = std::max(best, sum);
+    }
+    return best;
 }
 
 // Three ways to run the indexer and the selection:
@@ -140,7 +149,6 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     const int K = c->topk_blocks;
     p.cap = (K + 256 + 63) / 64 * 64;
     while (p.cap > K + 64 && sgqa::index_lds_bytes(p.cap) > sgqa::kMaxLds) p.cap -= 64;
-    p.rows = packed_rows(s, n);
     int64_t total_q = 0, max_b = 0;
     for (int32_t i = 0; i < n; ++i) {
         total_q += s[i].n_q;
@@ -157,15 +165,17 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     if (total_q >= 1024) {
         const size_t row_bytes = (size_t)sgqa::kGroups * stride * 4;
         int64_t chunk = (int64_t)(kTiledKeyBudget / row_bytes) / 16 * 16;
-        chunk = std::max<int64_t>(16, std::min<int64_t>(chunk, (p.rows + 15) / 16 * 16));
+        chunk = std::max<int64_t>(16, std::min<int64_t>(chunk, (total_q + 15) / 16 * 16));
         p.mode = IndexMode::Tiled;
         p.chunk_rows = chunk;
+        p.rows = chunk;
         p.key_stride = stride;
         p.split_blocks = kTiledSplitBlocks;
         p.n_split = (int)std::max<int64_t>(1, (max_b + kTiledSplitBlocks - 1) / kTiledSplitBlocks);
         p.ws = align_up((size_t)chunk * row_bytes);
         return p;
     }
+    p.rows = max_launch_rows(s, n, [](const sgqa_seq& q) { return q.n_q; });
     const size_t key_bytes = (size_t)p.rows * sgqa::kGroups * stride * 4;
     if (total_q == 0 || max_b <= K || key_bytes > ((size_t)1 << 30)) return p;
     // about 8192 score wavefronts, at least 256 candidate blocks each (measured
@@ -198,7 +208,7 @@ int64_t dense_queries(const sgqa_config* c, const sgqa_seq& q) {
 
 AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     AttnPlan p;
-    p.rows = packed_rows(s, n);
+    p.rows = max_launch_rows(s, n, [c](const sgqa_seq& q) { return q.n_q - dense_queries(c, q); });
     int64_t total_q = 0;
     for (int32_t i = 0; i < n; ++i) total_q += s[i].n_q - dense_queries(c, s[i]);
     const int64_t max_chunks =
@@ -246,7 +256,7 @@ int64_t fill_table(sgqa::SeqTable& tab, const sgqa_seq* s, int32_t first, int32_
                    Extent ext) {
     tab.n = 0;
     tab.pad_ = 0;
-    int64_t mx = 0;
+    int64_t mx = 0, rows = 0;
     for (int32_t i = first; i < first + count; ++i) {
         const int64_t e = ext(s[i]);
         if (e <= 0) continue;
@@ -256,6 +266,8 @@ int64_t fill_table(sgqa::SeqTable& tab, const sgqa_seq* s, int32_t first, int32_
         d.pos0 = s[i].pos0;
         d.kv_offset = s[i].kv_offset;
         d.store_offset = s[i].store_offset;
+        d.ws_row = rows;
+        rows += s[i].n_q;
         mx = std::max(mx, e);
     }
     return mx;
@@ -311,37 +323,41 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     rope_table(c, a.theta);
     a.part_key = nullptr;
     a.key_stride = p.key_stride;
-    a.key_row0 = 0;
     if (p.key_stride > 0) a.part_key = (uint32_t*)ws;
     if (p.mode == IndexMode::Tiled) {
-        // passes over query rows [r0, r0 + chunk_rows): each sequence cut to
-        // the pass's rows, keys addressed relative to r0
-        for (int64_t r0 = 0; r0 < p.rows; r0 += p.chunk_rows) {
-            a.key_row0 = r0;
-            const int64_t r1 = r0 + p.chunk_rows;
-            for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
-                const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
-                sgqa::SeqTable tab;
-                tab.n = 0;
-                tab.pad_ = 0;
-                int64_t mx = 0;
-                for (int32_t i = first; i < first + cnt; ++i) {
-                    const sgqa_seq& q = s[i];
-                    const int64_t lo = std::max(q.q_offset, r0);
-                    const int64_t hi = std::min(q.q_offset + q.n_q, r1);
-                    if (lo >= hi) continue;
-                    sgqa::DevSeq& d = tab.s[tab.n++];
-                    d.q_offset = lo;
-                    d.n_q = hi - lo;
-                    d.pos0 = q.pos0 + (lo - q.q_offset);
-                    d.kv_offset = q.kv_offset;
-                    d.store_offset = q.store_offset;
-                    mx = std::max(mx, hi - lo);
+        // launches of at most chunk_rows queries (one pass over the key
+        // workspace each) and kMaxSeqsPerLaunch entries, filled in call
+        // order; a sequence that does not fit the room left is cut
+        sgqa::SeqTable tab;
+        tab.n = 0;
+        tab.pad_ = 0;
+        int64_t used = 0, mx = 0;
+        for (int32_t i = 0; i < n; ++i) {
+            const sgqa_seq& q = s[i];
+            for (int64_t done = 0; done < q.n_q;) {
+                const int64_t take = std::min(q.n_q - done, p.chunk_rows - used);
+                sgqa::DevSeq& d = tab.s[tab.n++];
+                d.q_offset = q.q_offset + done;
+                d.n_q = take;
+                d.pos0 = q.pos0 + done;
+                d.kv_offset = q.kv_offset;
+                d.store_offset = q.store_offset;
+                d.ws_row = used;
+                used += take;
+                done += take;
+                mx = std::max(mx, take);
+                if (used == p.chunk_rows || tab.n == sgqa::kMaxSeqsPerLaunch) {
+                    hipError_t e = sgqa::launch_index_tiled(tab, mx, a, st);
+                    if (e != hipSuccess) return hip_fail(e, "index_topk launch");
+                    tab.n = 0;
+                    used = 0;
+                    mx = 0;
                 }
-                if (tab.n == 0) continue;
-                hipError_t e = sgqa::launch_index_tiled(tab, mx, a, st);
-                if (e != hipSuccess) return hip_fail(e, "index_topk launch");
             }
+        }
+        if (tab.n > 0) {
+            hipError_t e = sgqa::launch_index_tiled(tab, mx, a, st);
+            if (e != hipSuccess) return hip_fail(e, "index_topk launch");
         }
         return SGQA_OK;
     }
@@ -389,7 +405,7 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
         sgqa::SeqTable gt;
         gt.n = 0;
         gt.pad_ = 0;
-        int64_t gmax = 0;
+        int64_t gmax = 0, grows = 0;
         for (int32_t i = first; i < first + cnt; ++i) {
             const sgqa_seq& q = s[i];
             const int64_t nd = dense_queries(c, q);
@@ -400,6 +416,7 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
                 d.pos0 = q.pos0;
                 d.kv_offset = q.kv_offset;
                 d.store_offset = q.store_offset;
+                d.ws_row = 0;   // the tiled kernel uses no workspace
                 umax = std::max(umax, nd);
                 ublk = std::max(ublk, (q.pos0 + nd - 1) / c->block_size);
             }
@@ -410,6 +427,8 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
                 d.pos0 = q.pos0 + nd;
                 d.kv_offset = q.kv_offset;
                 d.store_offset = q.store_offset;
+                d.ws_row = grows;
+                grows += q.n_q - nd;
                 gmax = std::max(gmax, q.n_q - nd);
             }
         }

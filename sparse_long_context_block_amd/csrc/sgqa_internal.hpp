@@ -29,6 +29,10 @@ struct DevSeq {
     int64_t pos0;
     int64_t kv_offset;
     int64_t store_offset;
+    int64_t ws_row;      // first workspace row of this entry's queries: the
+                         // host numbers the queries of one launch table
+                         // 0, 1, ... in table order (split index keys and
+                         // split attention partials are addressed by it)
 };
 
 struct SeqTable {
@@ -60,9 +64,9 @@ struct IndexArgs {
     int32_t* sel;
     float* sel_scores;          // may be null
     uint16_t* q_hat_out;        // may be null
-    uint32_t* part_key;         // split calls: score keys [rows - key_row0, G, key_stride]
+    uint32_t* part_key;         // split calls: score keys [launch rows, G, key_stride],
+                                // row = DevSeq::ws_row + query index
     int64_t key_stride;
-    int64_t key_row0;           // first query row held in part_key
     int32_t block_size;
     int32_t topk;               // K
     int32_t cap;                // per-row LDS buffer capacity C (fused kernel)
@@ -79,8 +83,8 @@ struct AttnArgs {
     const int32_t* sel;
     uint16_t* out;
     float* lse;            // may be null
-    float* part_o;         // split mode: [rows, G, n_split, 16, 192]
-    float* part_ml;        // split mode: [rows, G, n_split, 16, 2]
+    float* part_o;         // split mode: [launch rows, G, n_split, 16, 192]
+    float* part_ml;        // split mode: [launch rows, G, n_split, 16, 2]
     int32_t block_size;
     int32_t topk;
     int32_t n_split;
@@ -95,6 +99,11 @@ struct AttnMergeArgs {
     float* lse;
     int32_t n_split;
 };
+
+// a launch table travels in the kernel arguments, which hold at most 4 KiB
+static_assert(sizeof(SeqTable) + sizeof(IndexArgs) <= 4096, "index kernel arguments fit");
+static_assert(sizeof(SeqTable) + sizeof(AttnArgs) + 8 <= 4096, "attention kernel arguments fit");
+static_assert(sizeof(SeqTable) + sizeof(CompressArgs) <= 4096, "compress kernel arguments fit");
 
 // ---------------------------------------------------------------------------
 // launchers (defined next to their kernels); return hipError_t of the launch

@@ -269,7 +269,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
     }
     __syncthreads();
 
-    const int64_t rg = row * kGroups + g;
+    const int64_t rg = (sq.ws_row + qi) * kGroups + g;     // partials row
     for (int e = threadIdx.x; e < kHeadsPerGroup * kHeadDim; e += 256) {
         const int head = e / kHeadDim;
         float mw[4], M = -INFINITY;
@@ -711,7 +711,7 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(SeqTable seqs, AttnMerg
     const int64_t qi = blockIdx.x / kGroups;
     if (qi >= sq.n_q) return;
     const int64_t row = sq.q_offset + qi;
-    const int64_t rg = row * kGroups + g;
+    const int64_t rg = (sq.ws_row + qi) * kGroups + g;     // partials row
     const int tid = threadIdx.x;
     if (tid < kHeadsPerGroup) {
         const int head = tid;

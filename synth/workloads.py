@@ -118,13 +118,17 @@ def _decode_loop(name, n_seqs, lo, hi, cap, steps, B=8, K=512, seed=0) -> Worklo
     return w
 
 
-def _multi(name, parts, B, K) -> Workload:
-    """Sequences (n_q, pos0) packed back to back in rows, caches and store."""
+def _multi(name, parts, B, K, row_gap=0, order=None) -> Workload:
+    """Sequences (n_q, pos0) back to back in caches and store; their query
+    rows `row_gap` rows apart; listed in the call in `order` (default: as
+    given)."""
     seqs, row, kv, st = [], 0, 0, 0
     for n, pos0 in parts:
         T = pos0 + n
         seqs.append(SeqLayout(row, n, pos0, kv, T, st, T // B))
-        row, kv, st = row + n, kv + T, st + T // B
+        row, kv, st = row + n + row_gap, kv + T, st + T // B
+    if order is not None:
+        seqs = [seqs[j] for j in order]
     return Workload(name, B, K, seqs, prebuilt=True)
 
 
@@ -143,6 +147,9 @@ def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
         w = _prefill(name, 8192, 8, 512, pos0=1_040_384)
     elif name == "multi_b1_passes":              # ragged sequences, tiled index in passes (tests)
         w = _multi(name, [(700, 180_000), (1500, 0), (333, 120_003)], B=1, K=64)
+    elif name == "multi_b1_shuffled":            # the same, rows apart and out of call order (tests)
+        w = _multi(name, [(700, 180_000), (1500, 0), (333, 120_003)], B=1, K=64,
+                   row_gap=1000, order=[2, 0, 1])
     elif name == "decode_loop_small":            # 8 sequences x 12 decode steps (tests)
         w = _decode_loop(name, 8, 8192, 40960 - 16, 40960, 12, seed=seed)
     elif name == "decode_loop_64x256k":          # 64 sequences x 80 decode steps

@@ -43,11 +43,18 @@ def lib_seqs(wl: W.Workload):
 
 def setup_seqs(wl: W.Workload):
     """Descriptors that write the store blocks of the cached history (before
-    the measured step's new tokens)."""
+    the measured step's new tokens; for a decode loop, before its first step)."""
+    seqs = wl.step_seqs(0) if wl.loop_steps else wl.seqs
     return [sg.Seq(q_offset=0, n_q=s.pos0, pos0=0, cache_len=s.pos0, kv_offset=s.kv_offset,
                    kv_capacity=s.kv_capacity, store_offset=s.store_offset,
                    store_capacity=s.store_capacity)
-            for s in wl.seqs if s.pos0 > 0]
+            for s in seqs if s.pos0 > 0]
+
+
+def lib_seq(s: W.SeqLayout) -> sg.Seq:
+    return sg.Seq(q_offset=s.q_offset, n_q=s.n_q, pos0=s.pos0, cache_len=s.cache_len,
+                  kv_offset=s.kv_offset, kv_capacity=s.kv_capacity,
+                  store_offset=s.store_offset, store_capacity=s.store_capacity)
 
 
 def prepare(wl: W.Workload):

@@ -178,6 +178,22 @@ def test_prefill_key_workspace(L):
     assert (1 << 20) * 16 <= ws <= (1 << 30)
 
 
+def test_workspace_ignores_query_row_offsets(L):
+    # workspace rows are numbered per launch, so the size follows the queries
+    # a launch holds, not where their rows sit in the caller's tensors (a
+    # decode loop keeps every step's rows in one output buffer)
+    cfg = sg.config()
+    for op in (sg.OP_INDEX_TOPK, sg.OP_SPARSE_ATTN, sg.OP_FORWARD):
+        for n_seq, n_q, pos0 in [(64, 1, 200_000), (2, 1, 200_000), (3, 600, 20_000)]:
+            packed = [sg.seq(n_q, pos0=pos0, q_offset=n_q * i) for i in range(n_seq)]
+            spread = [sg.seq(n_q, pos0=pos0, q_offset=5000 * n_q + 80 * n_q * i) for i in range(n_seq)]
+            assert sg.workspace_size(cfg, packed, op) == sg.workspace_size(cfg, spread, op)
+    # 64 decode queries: keys of 64 rows x 4 groups x 25024 candidates (25000
+    # blocks padded to 64 x an odd count)
+    spread = [sg.seq(1, pos0=200_000, q_offset=4000 + 80 * i) for i in range(64)]
+    assert sg.workspace_size(cfg, spread, sg.OP_INDEX_TOPK) == 64 * 4 * 25024 * 4
+
+
 def test_binding_rejects_wrong_tensors():
     import torch
     cfg = sg.config()

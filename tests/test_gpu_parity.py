@@ -59,9 +59,16 @@ def test_chunk_on_existing_cache_unaligned():
 
 def test_tiled_index_passes_over_ragged_sequences():
     # 2533 queries at B = 1 over histories up to 180K tokens: the tiled
-    # indexer runs in about seven key-workspace passes whose row boundaries
-    # cut through the sequences
+    # indexer runs in seven launches of at most 368 queries (one pass over
+    # its 1 GiB key workspace each) that cut through the sequences
     _run_and_check("multi_b1_passes", n_rows=24, check_all_store=False)
+
+
+def test_tiled_index_rows_out_of_call_order():
+    # the same sequences with 1000 unused rows between them, listed in the
+    # call in another order than their rows: key-workspace rows follow the
+    # call order, output rows follow q_offset
+    _run_and_check("multi_b1_shuffled", n_rows=24, check_all_store=False)
 
 
 def test_decode_split_paths():
