@@ -218,8 +218,9 @@ def main() -> int:
     wl = W.make(args.workload)
     print(f"[bench] workload {wl.name}: preparing inputs", file=sys.stderr, flush=True)
     di, cfg = prepare(wl)
-    # a decode loop advances one token per step (step k decodes loop step k,
-    # wrapping around; repeating a step recomputes the same outputs)
+    # a loop of calls (a decode loop: one token per sequence per call; a
+    # chained prefill: one chunk per call) runs call k at step k, wrapping
+    # around; repeating a call recomputes the same outputs
     if wl.loop_steps:
         loop = [[lib_seq(s) for s in wl.step_seqs(k)] for k in range(wl.loop_steps)]
         ws_n = max(sg.workspace_size(cfg, sq, sg.OP_FORWARD) for sq in loop)
@@ -262,7 +263,9 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     timed = [loop[k % len(loop)] for k in range(first_timed, step_no[0])]
-    seqs = timed[-1]                     # per-op timings and the roofline use the last step
+    # per-op timings and the roofline use the loop's last call (its longest
+    # context), or the step itself
+    seqs = loop[-1]
 
     reps = args.kernel_reps
     k_ms = {
@@ -280,16 +283,17 @@ def main() -> int:
         del src, dst
 
     if wl.loop_steps:
-        last = (step_no[0] - 1) % len(loop)
-        wm = work_model(wl, wl.step_seqs(last))
-        # throughput over the timed loop steps (each step one query per sequence)
+        op_seqs = wl.step_seqs(wl.loop_steps - 1)
+        wm = work_model(wl, op_seqs)
+        # throughput over the timed calls
         wm_loop_queries = sum(sum(s.n_q for s in sq) for sq in timed)
     else:
+        op_seqs = wl.seqs
         wm = work_model(wl)
         wm_loop_queries = None
     decode = wl.name.startswith("decode")
     dense = sum(min(s.n_q, max(0, 4 * wl.topk * wl.block_size - s.pos0)) if s.n_q >= 64 else 0
-                for s in wl.seqs)
+                for s in op_seqs)
     if decode:
         # dominant op: the attention call (split gather + merge), HBM-bound:
         # every gathered K/V row is read once per query and group
@@ -312,7 +316,12 @@ def main() -> int:
                 "kernel": kern,
                 "algorithmic_flops_per_launch": wm["attn_flops"],
                 "launch_ms": k_ms["sparse_attn"]}
-        value, unit = wm["queries"] / (ms_step * 1e-3), "tokens/s"
+        if dense < wm["queries"]:
+            # gathered K/V rows (768 B per query, group and attended token):
+            # the rate the gather kernel moves them at, against HBM peak
+            roof["gathered_GBps"] = wm["attn_gather_bytes"] / (k_ms["sparse_attn"] * 1e-3) / 1e9
+        queries = wm_loop_queries / args.steps if wm_loop_queries else wm["queries"]
+        value, unit = queries / (ms_step * 1e-3), "tokens/s"
 
     res = {
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
@@ -324,11 +333,18 @@ def main() -> int:
         "per_op_ms": k_ms,
         "roofline": roof,
     }
+    if wl.loop_steps:
+        res["config"]["loop_calls"] = wl.loop_steps
+        res["config"]["per_op_call"] = wl.loop_steps - 1
+        if args.steps % wl.loop_steps == 0:
+            # wall time of one pass over every call of the loop (a chained
+            # prefill: the whole prefill of one layer)
+            res["loop_pass_s"] = wall / (args.steps // wl.loop_steps)
     if not args.no_cpu_baseline:
         print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
         if wl.loop_steps:
             import dataclasses
-            one = dataclasses.replace(wl, seqs=wl.step_seqs((step_no[0] - 1) % len(loop)),
+            one = dataclasses.replace(wl, seqs=wl.step_seqs(wl.loop_steps - 1),
                                       loop_steps=0, loop_seqs=0)
             res["cpu_baseline"] = cpu_baseline(one)
         else:

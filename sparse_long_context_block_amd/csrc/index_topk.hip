@@ -402,6 +402,26 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
 }
 
 // ---------------------------------------------------------------------------
+// Prefill-sized calls, first step: every query's indexer rows (RMSNorm,
+// rotary span, bf16) once, written to the workspace in the score kernel's
+// A-operand order: per query 4 k-chunks x 64 lanes x 16 B, so a score
+// workgroup loads its fragments with one coalesced 16-byte read per lane and
+// k-chunk instead of recomputing them for every candidate range.  One
+// wavefront per query; q_hat is written here when asked.
+// ---------------------------------------------------------------------------
+__global__ __launch_bounds__(256) void index_qfrag_kernel(SeqTable seqs, IndexArgs a) {
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (qi >= sq.n_q) return;
+    const int lane = lane_id();
+    bf16x8 af[4];
+    index_query_fragments(a, sq.q_offset + qi, sq.pos0 + qi, lane >> 4, lane & 15, true, af);
+    uint4* dst = a.q_frag + (sq.ws_row + qi) * 256;
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) dst[kk * 64 + lane] = __builtin_bit_cast(uint4, af[kk]);
+}
+
+// ---------------------------------------------------------------------------
 // Prefill-sized calls: a workgroup of four wavefronts scores 16 consecutive
 // queries (four per wavefront) against one range of candidate blocks.  The
 // range streams through LDS in tiles of 64 store rows (double-buffered, rows
@@ -432,8 +452,8 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
     // ---- the wavefront's four queries: A fragments, weights, candidates ----
     bf16x8 af[4][4];
     float4 wv[4];
-    int64_t nbq[4];
-    uint32_t* keys[4];
+    int lim[4];                   // keys kept for block ids r_lo + [0, lim)
+    uint32_t kofs[4];             // byte offset of the key row of (query, group qq)
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int qo = 4 * wave + j;
@@ -441,23 +461,37 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
         const int64_t qi = q0 + (ok ? qo : 0);
         const int64_t row = sq.q_offset + qi;
         const int64_t t = sq.pos0 + qi;
-        index_query_fragments(a, row, t, qq, m, ok && split == 0, af[j]);
+        const uint4* qf = a.q_frag + (sq.ws_row + qi) * 256;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) af[j][kk] = as_bf16x8(qf[kk * 64 + lane]);
         wv[j] = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
-        nbq[j] = ok ? t / a.block_size : 0;
-        keys[j] = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
+        const int64_t nb = ok ? t / a.block_size : 0;
+        const int64_t hi = nb < r_hi ? nb : r_hi;
+        lim[j] = hi > r_lo ? (int)(hi - r_lo) : 0;
+        kofs[j] = (uint32_t)((qo * kGroups + qq) * a.key_stride * 4);
     }
     if (r_lo >= r_hi) return;                       // workgroup-uniform
 
-    // ---- store tiles: 64 rows x 16 chunks of 16 B, four chunks per thread
-    //      (rows past the range repeat its last row; their scores are not
-    //      written) ----
-    const uint16_t* store = a.store + sq.store_offset * kIdxDim;
-    auto gload = [&](int64_t r0, uint4 (&v)[4]) {
+    // keys of the workgroup's 16 queries from block r_lo on, through a buffer
+    // resource: 32-bit offsets (the host keeps 64 key rows below 4 GiB), and
+    // a store at an offset past the resource's end is dropped, which is how
+    // candidates outside a query's range are skipped without a branch
+    const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.part_key + (sq.ws_row + q0) * kGroups * a.key_stride + r_lo), (short)0,
+        (int)(uint32_t)(kScoreTileQueries * kGroups * a.key_stride * 4), 0x00020000);
+    constexpr uint32_t kDropped = 0xFFFFFFF0u;
+
+    // ---- store tiles: 64 rows x 16 chunks of 16 B, four chunks per thread;
+    //      rows past the range read as zero (their scores are dropped) ----
+    const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
+        (void*)(a.store + (sq.store_offset + r_lo) * kIdxDim), (short)0,
+        (int)((r_hi - r_lo) * kIdxDim * 2), 0x00020000);
+    auto gload = [&](int rt, uint4 (&v)[4]) {
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
             const int c = tid + 256 * k;
-            const int64_t r = r0 + (c >> 4) < r_hi ? r0 + (c >> 4) : r_hi - 1;
-            v[k] = load16(store + r * kIdxDim + 8 * (c & 15));
+            v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
+                                                 srs, (rt + (c >> 4)) * (kIdxDim * 2) + 16 * (c & 15), 0, 0));
         }
     };
     auto lstore = [&](uint16_t* buf, const uint4 (&v)[4]) {
@@ -468,33 +502,39 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
         }
     };
     uint4 stage[4];
-    gload(r_lo, stage);
+    gload(0, stage);
     lstore(tiles[0], stage);
     int cur = 0;
     for (int64_t r0 = r_lo; r0 < r_hi; r0 += kStoreTile) {
+        const int rt = (int)(r0 - r_lo);
         const bool more = r0 + kStoreTile < r_hi;
-        if (more) gload(r0 + kStoreTile, stage);
+        if (more) gload(rt + kStoreTile, stage);
         __syncthreads();
         const uint16_t* buf = tiles[cur];
 #pragma unroll
         for (int sub = 0; sub < kStoreTile / 16; ++sub) {
-            const int64_t rb = r0 + 16 * sub;
-            if (rb >= r_hi) break;                  // workgroup-uniform
+            if (r0 + 16 * sub >= r_hi) break;       // workgroup-uniform
             bf16x8 bf[4];
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 bf[kk] = as_bf16x8(*(const uint4*)(buf + (16 * sub + m) * kStoreStrideU + 32 * kk + 8 * qq));
-            const int64_t r = rb + m;
+            // the four queries' chains interleaved, one accumulator each
+            f32x4 acc[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+                for (int j = 0; j < 4; ++j) acc[j] = mfma_16x16x32(af[j][kk], bf[kk], acc[j]);
+            const int rr = rt + 16 * sub + m;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(af[j][kk], bf[kk], acc);
-                float s = wv[j].x * fmaxf(acc[0], 0.f);
-                s += wv[j].y * fmaxf(acc[1], 0.f);
-                s += wv[j].z * fmaxf(acc[2], 0.f);
-                s += wv[j].w * fmaxf(acc[3], 0.f);
-                if (r < nbq[j] && r < r_hi) keys[j][r] = score_key(s);
+                float s = wv[j].x * fmaxf(acc[j][0], 0.f);
+                s += wv[j].y * fmaxf(acc[j][1], 0.f);
+                s += wv[j].z * fmaxf(acc[j][2], 0.f);
+                s += wv[j].w * fmaxf(acc[j][3], 0.f);
+                const uint32_t off = rr < lim[j] ? kofs[j] + 4u * (uint32_t)rr : kDropped;
+                __builtin_amdgcn_raw_buffer_store_b32(score_key(s), krs, (int)off, 0, 0);
             }
         }
         if (more) lstore(tiles[cur ^ 1], stage);
@@ -905,9 +945,13 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
                               hipStream_t stream) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
     const int64_t n_qt = (max_nq + kScoreTileQueries - 1) / kScoreTileQueries;
+    hipLaunchKernelGGL(index_qfrag_kernel, dim3((unsigned)((max_nq + 3) / 4), (unsigned)seqs.n),
+                       dim3(256), 0, stream, seqs, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
     dim3 grid((unsigned)(n_qt * a.n_split), (unsigned)seqs.n);
     hipLaunchKernelGGL(index_score_tile_kernel, grid, dim3(256), 0, stream, seqs, a);
-    hipError_t e = hipGetLastError();
+    e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_select(seqs, max_nq, a, stream);
 }

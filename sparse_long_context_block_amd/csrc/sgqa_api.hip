@@ -104,8 +104,15 @@ struct IndexPlan {
     int64_t key_stride = 0;
     int64_t rows = 0;           // key-workspace rows: queries of the largest launch
     int64_t chunk_rows = 0;     // tiled mode: queries per launch (one key pass)
+    size_t frag_off = 0;        // tiled mode: byte offset of the query fragments
     size_t ws = 0;
 };
+
+// tiled mode: bytes of one query's indexer A fragments (16 rows x 128 bf16)
+constexpr size_t kQueryFragBytes = (size_t)sgqa::kGroups * sgqa::kIdxHeads * sgqa::kIdxDim * 2;
+// tiled mode: the score kernel addresses the keys of 16 queries with 32-bit
+// byte offsets
+constexpr int64_t kTiledMaxStride = ((int64_t)1 << 32) / (16 * sgqa::kGroups * 4) - 64;
 
 // key workspace of the tiled mode: query rows are processed in passes whose
 // keys (4 B per row, group and candidate) fit this budget
@@ -136,7 +143,8 @@ int64_t max_launch_rows(const sgqa_seq* s, int32_t n, Rows nq) {
 }
 
 // Three ways to run the indexer and the selection:
-//  * Tiled (1024 queries or more): 16-query workgroups score candidate
+//  * Tiled (1024 queries or more, fewer than 16.7M candidates): each query's
+//    indexer rows are prepared once, 16-query workgroups score candidate
 //    ranges against store tiles shared in LDS, keys go to the workspace in
 //    passes of at most kTiledKeyBudget bytes, one workgroup per (query,
 //    group) selects;
@@ -162,7 +170,7 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     // channels instead of all starting at one power-of-two alignment
     int64_t stride = std::max<int64_t>(64, (max_b + 63) / 64 * 64);
     if ((stride / 64) % 2 == 0) stride += 64;
-    if (total_q >= 1024) {
+    if (total_q >= 1024 && stride <= kTiledMaxStride) {
         const size_t row_bytes = (size_t)sgqa::kGroups * stride * 4;
         int64_t chunk = (int64_t)(kTiledKeyBudget / row_bytes) / 16 * 16;
         chunk = std::max<int64_t>(16, std::min<int64_t>(chunk, (total_q + 15) / 16 * 16));
@@ -172,7 +180,8 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
         p.key_stride = stride;
         p.split_blocks = kTiledSplitBlocks;
         p.n_split = (int)std::max<int64_t>(1, (max_b + kTiledSplitBlocks - 1) / kTiledSplitBlocks);
-        p.ws = align_up((size_t)chunk * row_bytes);
+        p.frag_off = align_up((size_t)chunk * row_bytes);
+        p.ws = p.frag_off + align_up((size_t)chunk * kQueryFragBytes);
         return p;
     }
     p.rows = max_launch_rows(s, n, [](const sgqa_seq& q) { return q.n_q; });
@@ -322,8 +331,10 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     a.eps = c->eps_rms;
     rope_table(c, a.theta);
     a.part_key = nullptr;
+    a.q_frag = nullptr;
     a.key_stride = p.key_stride;
     if (p.key_stride > 0) a.part_key = (uint32_t*)ws;
+    if (p.frag_off > 0) a.q_frag = (uint4*)((char*)ws + p.frag_off);
     if (p.mode == IndexMode::Tiled) {
         // launches of at most chunk_rows queries (one pass over the key
         // workspace each) and kMaxSeqsPerLaunch entries, filled in call

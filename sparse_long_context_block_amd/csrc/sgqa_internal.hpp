@@ -66,6 +66,7 @@ struct IndexArgs {
     uint16_t* q_hat_out;        // may be null
     uint32_t* part_key;         // split calls: score keys [launch rows, G, key_stride],
                                 // row = DevSeq::ws_row + query index
+    uint4* q_frag;              // tiled calls: indexer A fragments [launch rows, 4, 64]
     int64_t key_stride;
     int32_t block_size;
     int32_t topk;               // K

@@ -21,6 +21,10 @@ decode_loop_64x256k    the same 64 sequences decoded for 80 consecutive
                        tokens (lengths U[131072,262064])           8       512
 chunk_1m               8,192 queries at 1,040,384..1,048,575 over a
                        1,048,576-token cache                       8       512
+prefill_1m_chained     a 1,048,576-token prefill as 128 calls of
+                       8,192 queries, each on the cache and store
+                       the calls before it built                   8       512
+prefill_1m_chained_b1  the same                                    1       2,048
 =====================  ==========================================  ======  =====
 
 Distributions: main Q and K bf16 unit normal then RMS-normalised per
@@ -68,8 +72,9 @@ class Workload:
     store_q8: bool = True
     seed: int = 0
     notes: str = ""
-    # decode loops: seqs holds loop_steps x loop_seqs entries, step-major;
-    # entry (s, i) is sequence i's one query at its s-th step
+    # loops of calls (decode loops, chained prefills): seqs holds
+    # loop_steps x loop_seqs entries, step-major; entry (s, i) is sequence
+    # i's part of call s
     loop_steps: int = 0
     loop_seqs: int = 0
 
@@ -118,6 +123,18 @@ def _decode_loop(name, n_seqs, lo, hi, cap, steps, B=8, K=512, seed=0) -> Worklo
     return w
 
 
+def _chained(name, n_chunks, chunk, B, K) -> Workload:
+    """One sequence prefilled in n_chunks consecutive calls of `chunk`
+    queries: call c covers positions c*chunk .. (c+1)*chunk - 1 and finds
+    the store blocks of everything before it written by the earlier calls'
+    compression step; query rows = positions."""
+    T = n_chunks * chunk
+    seqs = [SeqLayout(c * chunk, chunk, c * chunk, 0, T, 0, T // B) for c in range(n_chunks)]
+    w = Workload(name, B, K, seqs)
+    w.loop_steps, w.loop_seqs = n_chunks, 1
+    return w
+
+
 def _multi(name, parts, B, K, row_gap=0, order=None) -> Workload:
     """Sequences (n_q, pos0) back to back in caches and store; their query
     rows `row_gap` rows apart; listed in the call in `order` (default: as
@@ -154,6 +171,14 @@ def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
         w = _decode_loop(name, 8, 8192, 40960 - 16, 40960, 12, seed=seed)
     elif name == "decode_loop_64x256k":          # 64 sequences x 80 decode steps
         w = _decode_loop(name, 64, 131072, 262144 - 80, 262144, 80, seed=seed)
+    elif name == "prefill_1m_chained":           # 1M-token prefill, 128 calls of 8192
+        w = _chained(name, 128, 8192, 8, 512)
+    elif name == "prefill_1m_chained_b1":        # the same at B = 1, k = 2048 blocks
+        w = _chained(name, 128, 8192, 1, 2048)
+    elif name == "chained_small":                # 6 calls of 1024 (tests)
+        w = _chained(name, 6, 1024, 8, 32)
+    elif name == "chained_small_b1":             # 4 calls of 1024 at B = 1 (tests)
+        w = _chained(name, 4, 1024, 1, 256)
     elif name == "decode_small":                 # 8 sequences, split paths (tests)
         w = _decode(name, n_seqs=8, lo=8192, hi=40000, cap=40960, seed=seed)
     elif name.startswith("chunk_"):              # chunk_<pos0>_<n>[_b<B>_k<K>] (tests)
