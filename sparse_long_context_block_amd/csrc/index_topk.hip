@@ -428,11 +428,17 @@ __global__ __launch_bounds__(256) void index_qfrag_kernel(SeqTable seqs, IndexAr
 // padded to 68 dwords so the 16 rows a B-operand read touches hit distinct
 // banks); every B fragment a wavefront reads serves the MFMAs of its four
 // queries, so the store is read once per 16 queries instead of once per
-// query.  Keys go to the workspace exactly as in the decode-sized path.
+// query.  LISTED = false writes every key to the workspace, as the
+// decode-sized path does; LISTED = true (tiles with long rows) keeps only the
+// keys >= the row's sampled threshold, with their block ids, in per-segment
+// lists (in block order: lanes append in block order, segments lie inside
+// one workgroup's range) plus one count per segment.
 // ---------------------------------------------------------------------------
 constexpr int kStoreTile = 64;
 constexpr int kStoreStrideU = kIdxDim + 8;    // bf16 per LDS store row (68 dwords = 4 x 17)
+static_assert(kSegBlocks % kStoreTile == 0, "a store tile lies inside one segment");
 
+template <bool LISTED>
 __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, IndexArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tiles[2][kStoreTile * kStoreStrideU];
     const DevSeq sq = seqs.s[blockIdx.y];
@@ -441,6 +447,7 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
     const int split = blockIdx.x % a.n_split;
     if (qt >= n_qt) return;
     const int64_t q0 = qt * kScoreTileQueries;
+    if ((a.listed && list_tile((sq.pos0 + q0) / a.block_size, a.topk)) != LISTED) return;
     const int n_valid = (int)(sq.n_q - q0 < kScoreTileQueries ? sq.n_q - q0 : kScoreTileQueries);
     const int64_t nb_max = (sq.pos0 + q0 + n_valid - 1) / a.block_size;
     const int64_t r_lo = (int64_t)split * a.split_blocks;
@@ -452,8 +459,10 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
     // ---- the wavefront's four queries: A fragments, weights, candidates ----
     bf16x8 af[4][4];
     float4 wv[4];
-    int lim[4];                   // keys kept for block ids r_lo + [0, lim)
-    uint32_t kofs[4];             // byte offset of the key row of (query, group qq)
+    int lim[4];                   // candidates r_lo + [0, lim) of (query, group qq)
+    uint32_t kofs[4];             // byte offset of its key row (keys: from block r_lo)
+    uint32_t tauv[4];             // listed: its threshold
+    int cnt[4];                   // listed: entries of the current segment
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int qo = 4 * wave + j;
@@ -468,16 +477,21 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
         const int64_t nb = ok ? t / a.block_size : 0;
         const int64_t hi = nb < r_hi ? nb : r_hi;
         lim[j] = hi > r_lo ? (int)(hi - r_lo) : 0;
-        kofs[j] = (uint32_t)((qo * kGroups + qq) * a.key_stride * 4);
+        kofs[j] = (uint32_t)((qo * kGroups + qq) * a.key_stride * 4) + (LISTED ? 0u : 4u * (uint32_t)r_lo);
+        if (LISTED) {
+            tauv[j] = a.part_key[((sq.ws_row + qi) * kGroups + qq) * a.key_stride + a.tau_off];
+            cnt[j] = 0;
+        }
     }
     if (r_lo >= r_hi) return;                       // workgroup-uniform
 
-    // keys of the workgroup's 16 queries from block r_lo on, through a buffer
-    // resource: 32-bit offsets (the host keeps 64 key rows below 4 GiB), and
-    // a store at an offset past the resource's end is dropped, which is how
-    // candidates outside a query's range are skipped without a branch
+    // key rows of the workgroup's 16 queries through a buffer resource: 32-bit
+    // offsets (the host keeps 64 key rows below 4 GiB), and a store at an
+    // offset past the resource's end is dropped, which is how candidates
+    // outside a query's range (or below its threshold) are skipped without a
+    // branch
     const __amdgpu_buffer_rsrc_t krs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.part_key + (sq.ws_row + q0) * kGroups * a.key_stride + r_lo), (short)0,
+        (void*)(a.part_key + (sq.ws_row + q0) * kGroups * a.key_stride), (short)0,
         (int)(uint32_t)(kScoreTileQueries * kGroups * a.key_stride * 4), 0x00020000);
     constexpr uint32_t kDropped = 0xFFFFFFF0u;
 
@@ -511,6 +525,7 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
         if (more) gload(rt + kStoreTile, stage);
         __syncthreads();
         const uint16_t* buf = tiles[cur];
+        const uint32_t seg = (uint32_t)(r0 / kSegBlocks);
 #pragma unroll
         for (int sub = 0; sub < kStoreTile / 16; ++sub) {
             if (r0 + 16 * sub >= r_hi) break;       // workgroup-uniform
@@ -533,8 +548,35 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
                 s += wv[j].y * fmaxf(acc[j][1], 0.f);
                 s += wv[j].z * fmaxf(acc[j][2], 0.f);
                 s += wv[j].w * fmaxf(acc[j][3], 0.f);
-                const uint32_t off = rr < lim[j] ? kofs[j] + 4u * (uint32_t)rr : kDropped;
-                __builtin_amdgcn_raw_buffer_store_b32(score_key(s), krs, (int)off, 0, 0);
+                const uint32_t key = score_key(s);
+                if (!LISTED) {
+                    const uint32_t off = rr < lim[j] ? kofs[j] + 4u * (uint32_t)rr : kDropped;
+                    __builtin_amdgcn_raw_buffer_store_b32(key, krs, (int)off, 0, 0);
+                } else {
+                    // append (key, block id) to the segment's list: the 16
+                    // lanes of group qq count the passing lanes below them
+                    const bool pass = rr < lim[j] && key >= tauv[j];
+                    const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * qq)) & 0xFFFFu;
+                    const int pos = cnt[j] + __builtin_popcount(gm & ((1u << m) - 1u));
+                    const uint32_t off = pass && pos < kSegCap
+                        ? kofs[j] + 4u * ((uint32_t)a.list_off + seg * (2 * kSegCap) + 2u * (uint32_t)pos)
+                        : kDropped;
+                    const uint32_t blk = (uint32_t)(r_lo + rr);
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{key, blk}, krs, (int)off, 0, 0);
+                    cnt[j] += __builtin_popcount(gm);
+                }
+            }
+        }
+        if (LISTED && (((r0 + kStoreTile) % kSegBlocks) == 0 || r0 + kStoreTile >= r_hi)) {
+            // the segment ends: its count (above kSegCap when entries were
+            // dropped), for every query whose range reaches into it
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+                const bool wr = m == 0 && (int64_t)seg * kSegBlocks - r_lo < lim[j];
+                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)cnt[j], krs,
+                                                      (int)(wr ? kofs[j] + 4u * seg : kDropped), 0, 0);
+                cnt[j] = 0;
             }
         }
         if (more) lstore(tiles[cur ^ 1], stage);
@@ -667,6 +709,40 @@ __device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared<NW>& 
     }
 }
 
+// Cut an LDS candidate list (keys, block ids, in block order) to its top k in
+// place, order kept, and return the k-th key v: kept are the keys > v and the
+// first entries equal to v.  Called by every thread of the workgroup; one
+// wavefront moves the entries (each to an index <= its own).
+template <int NW>
+__device__ uint32_t compact_to_topk(uint32_t* ckeys, int32_t* cidx, int pool, int K, SelectShared<NW>& sh) {
+    const int w = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    uint32_t v, vm;
+    int vr;
+    radix_kth(ckeys, pool, K, sh, v, vm, vr);
+    if (w == 0) {
+        int out = 0, eq_seen = 0;
+        for (int i0 = 0; i0 < pool; i0 += 64) {
+            const int i = i0 + lane;
+            const uint32_t kk = i < pool ? ckeys[i] : 0u;
+            const int32_t ii = i < pool ? cidx[i] : 0;
+            const bool eq = i < pool && kk == v;
+            const uint64_t em = __ballot(eq);
+            const bool keep = i < pool && (kk > v || (eq && eq_seen + (int)lanes_below(em) < vr));
+            const uint64_t km = __ballot(keep);
+            wave_lds_sync();
+            if (keep) {
+                ckeys[out + (int)lanes_below(km)] = kk;
+                cidx[out + (int)lanes_below(km)] = ii;
+            }
+            wave_lds_sync();
+            out += __popcll(km);
+            eq_seen += __popcll(em);
+        }
+    }
+    __syncthreads();
+    return v;
+}
+
 // Keep rule over entries [0, n) of keys (block ids idx, or the entry index
 // when idx is null): key & pmask > prefix, or == prefix among the first krem
 // such; written in order to sel / ssc.
@@ -718,19 +794,13 @@ __device__ void select_ordered_output(const uint32_t* keys, const int32_t* idx, 
 // true the others (two instantiations, so the short rows keep the smaller
 // register footprint)
 template <bool LONG, int NW>
-__global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, IndexArgs a) {
+__device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs& a, uint32_t* lds_keys,
+                           SelectShared<NW>& sh) {
     constexpr int NT = 64 * NW;
-    extern __shared__ uint32_t lds_keys[];    // staged row, or candidate keys + block ids
-    __shared__ SelectShared<NW> sh;
-    const DevSeq sq = seqs.s[blockIdx.y];
-    const int64_t qi = blockIdx.x / kGroups;
-    const int g = blockIdx.x % kGroups;
-    if (qi >= sq.n_q) return;
     const int64_t t = sq.pos0 + qi;
     const int64_t row = sq.q_offset + qi;
     const int64_t rg = row * kGroups + g;
     const int n = (int)(t / a.block_size);
-    if ((n > kSelectStageKeys) != LONG) return;
     const int K = a.topk;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     const uint32_t* gkeys = a.part_key + ((sq.ws_row + qi) * kGroups + g) * a.key_stride;
@@ -820,34 +890,8 @@ __global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, In
             }
             par ^= 1;
             if (pool + total <= cap) break;              // workgroup-uniform
-            // compact the list to its top k, in place and in order (one
-            // wavefront: every entry moves to an index <= its own)
-            uint32_t v, vm;
-            int vr;
-            radix_kth(ckeys, pool, K, sh, v, vm, vr);
-            if (w == 0) {
-                int out = 0, eq_seen = 0;
-                for (int i0 = 0; i0 < pool; i0 += 64) {
-                    const int i = i0 + lane;
-                    const uint32_t kk = i < pool ? ckeys[i] : 0u;
-                    const int32_t ii = i < pool ? cidx[i] : 0;
-                    const bool eq = i < pool && kk == v;
-                    const uint64_t em = __ballot(eq);
-                    const bool keep = i < pool && (kk > v || (eq && eq_seen + (int)lanes_below(em) < vr));
-                    const uint64_t km = __ballot(keep);
-                    wave_lds_sync();
-                    if (keep) {
-                        ckeys[out + (int)lanes_below(km)] = kk;
-                        cidx[out + (int)lanes_below(km)] = ii;
-                    }
-                    wave_lds_sync();
-                    out += __popcll(km);
-                    eq_seen += __popcll(em);
-                }
-            }
-            __syncthreads();
+            thr = compact_to_topk(ckeys, cidx, pool, K, sh);
             pool = K;
-            thr = v;
             strict = true;
         }
 #pragma unroll
@@ -871,14 +915,292 @@ __global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, In
     select_ordered_output(ckeys, cidx, c, prefix, pmask, krem, sel, ssc, sh);
 }
 
+// a listed row of a tiled call (its key row holds candidate lists)
+__device__ __forceinline__ bool listed_row(const DevSeq& sq, int64_t qi, const IndexArgs& a) {
+    return a.listed && list_tile((sq.pos0 + (qi & ~(int64_t)(kScoreTileQueries - 1))) / a.block_size, a.topk);
+}
+
+template <bool LONG, int NW>
+__global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, IndexArgs a) {
+    extern __shared__ uint32_t lds_keys[];    // staged row, or candidate keys + block ids
+    __shared__ SelectShared<NW> sh;
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = blockIdx.x / kGroups;
+    const int g = blockIdx.x % kGroups;
+    if (qi >= sq.n_q) return;
+    const int64_t n = (sq.pos0 + qi) / a.block_size;
+    if ((n > kSelectStageKeys) != LONG) return;
+    if (LONG && listed_row(sq, qi, a)) return;    // selected from its lists
+    select_row<LONG, NW>(sq, qi, g, a, lds_keys, sh);
+}
+
+// ---------------------------------------------------------------------------
+// Listed rows (tiled calls, long histories), before the score step: the
+// scores of each tile's sample, S blocks in S/16 groups of 16 consecutive
+// blocks spread over [0, n0) (n0 = the tile's first query's candidates, so
+// every sample block is a candidate of all 16 queries), written to the key
+// rows' sample area.  Workgroups of four wavefronts, four queries each, an
+// eighth of the groups per workgroup; B fragments straight from memory.
+// ---------------------------------------------------------------------------
+constexpr int kSampleParts = 8;
+
+__global__ __launch_bounds__(256) void index_sample_kernel(SeqTable seqs, IndexArgs a) {
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t n_qt = (sq.n_q + kScoreTileQueries - 1) / kScoreTileQueries;
+    const int64_t qt = blockIdx.x / kSampleParts;
+    const int part = blockIdx.x % kSampleParts;
+    if (qt >= n_qt) return;
+    const int64_t q0 = qt * kScoreTileQueries;
+    const int64_t n0 = (sq.pos0 + q0) / a.block_size;
+    if (!(a.listed && list_tile(n0, a.topk))) return;
+    const int ngrp = list_sample(n0) / 16;
+    const int g_lo = part * ngrp / kSampleParts, g_hi = (part + 1) * ngrp / kSampleParts;
+    const int n_valid = (int)(sq.n_q - q0 < kScoreTileQueries ? sq.n_q - q0 : kScoreTileQueries);
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int qq = lane >> 4, m = lane & 15;
+    bf16x8 af[4][4];
+    float4 wv[4];
+    uint32_t* sk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        const int qo = 4 * wave + j;
+        const int64_t qi = q0 + (qo < n_valid ? qo : 0);
+        const uint4* qf = a.q_frag + (sq.ws_row + qi) * 256;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) af[j][kk] = as_bf16x8(qf[kk * 64 + lane]);
+        wv[j] = *(const float4*)(a.w + ((sq.q_offset + qi) * kGroups + qq) * kIdxHeads);
+        sk[j] = qo < n_valid ? a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride + a.samp_off
+                             : nullptr;
+    }
+    const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
+    auto start = [&](int gi) { return (int64_t)gi * (n0 - 16) / (ngrp > 1 ? ngrp - 1 : 1); };
+    uint4 b[4];
+    if (g_lo < g_hi) {
+        const uint16_t* src = store + (start(g_lo) + m) * kIdxDim;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) b[kk] = load16(src + 32 * kk);
+    }
+    for (int gi = g_lo; gi < g_hi; ++gi) {
+        bf16x8 bf[4];
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) bf[kk] = as_bf16x8(b[kk]);
+        if (gi + 1 < g_hi) {
+            const uint16_t* src = store + (start(gi + 1) + m) * kIdxDim;
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) b[kk] = load16(src + 32 * kk);
+        }
+        f32x4 acc[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) acc[j] = mfma_16x16x32(af[j][kk], bf[kk], acc[j]);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            float s = wv[j].x * fmaxf(acc[j][0], 0.f);
+            s += wv[j].y * fmaxf(acc[j][1], 0.f);
+            s += wv[j].z * fmaxf(acc[j][2], 0.f);
+            s += wv[j].w * fmaxf(acc[j][3], 0.f);
+            if (sk[j]) sk[j][16 * gi + m] = score_key(s);
+        }
+    }
+}
+
+// Listed rows: the threshold tau of each (query, group), the j-th largest of
+// its S sample keys (list_rank), into the key row's tau slot.  The first
+// workgroup also clears the failed-row count of the launch.
+__global__ __launch_bounds__(256) void index_tau_kernel(SeqTable seqs, IndexArgs a) {
+    __shared__ uint32_t skeys[kListSampleMax];
+    __shared__ SelectShared<4> sh;
+    if (blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x == 0) a.ctl[0] = 0u;
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = blockIdx.x / kGroups;
+    const int g = blockIdx.x % kGroups;
+    if (qi >= sq.n_q || !listed_row(sq, qi, a)) return;
+    const int64_t n0 = (sq.pos0 + (qi & ~(int64_t)(kScoreTileQueries - 1))) / a.block_size;
+    const int S = list_sample(n0);
+    uint32_t* krow = a.part_key + ((sq.ws_row + qi) * kGroups + g) * a.key_stride;
+    for (int i = threadIdx.x; i < S; i += 256) skeys[i] = krow[a.samp_off + i];
+    __syncthreads();
+    uint32_t tau, tmask;
+    int trem;
+    radix_kth(skeys, S, list_rank(n0, a.topk), sh, tau, tmask, trem);
+    if (threadIdx.x == 0) krow[a.tau_off] = tau;
+}
+
+// exclusive prefix sum over the 256 threads of a workgroup (4 wavefronts)
+__device__ __forceinline__ int block_scan256(int v, int* part, int& total) {
+    const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+    int incl = v;
+#pragma unroll
+    for (int o = 1; o < 64; o <<= 1) {
+        const int up = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += up;
+    }
+    if (lane == 63) part[w] = incl;
+    __syncthreads();
+    int before = 0;
+    total = 0;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+        before += j < w ? part[j] : 0;
+        total += part[j];
+    }
+    __syncthreads();
+    return before + incl - v;
+}
+
+// Listed rows: the top k from the candidate lists.  The segments' lists are
+// streamed into an LDS pool in block order, 64 segments per step (four
+// threads per segment, counts and offsets from one workgroup scan); a step
+// that would overflow the pool first cuts it to its top k and raises the
+// threshold to the k-th key, as the long-row select does (rows whose scores
+// tie at the threshold can list many more than k entries).  The pool is then
+// selected exactly.  A row whose lists cannot give the exact answer -- a
+// segment that dropped entries, or fewer than k entries (the threshold was
+// above the k-th score) -- is appended to the launch's failed rows instead,
+// to be scored again in full.
+__global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, IndexArgs a) {
+    extern __shared__ uint32_t lds[];            // keys [cap], block ids [cap]
+    __shared__ SelectShared<4> sh;
+    __shared__ int part[4];
+    __shared__ int s_bad;
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = blockIdx.x / kGroups;
+    const int g = blockIdx.x % kGroups;
+    if (qi >= sq.n_q || !listed_row(sq, qi, a)) return;
+    const int K = a.topk;
+    const int cap = list_capacity(K);
+    static_assert(64 * kSegCap <= 16384 - 3072 && 64 * kSegCap <= 8192 - 1024,
+                  "a step of 64 full segments fits the pool after a cut to k");
+    const int n = (int)((sq.pos0 + qi) / a.block_size);
+    const int nseg = (n + kSegBlocks - 1) / kSegBlocks;
+    const uint32_t* krow = a.part_key + ((sq.ws_row + qi) * kGroups + g) * a.key_stride;
+    uint32_t* ckeys = lds;
+    int32_t* cidx = (int32_t*)(lds + cap);
+    const int tid = threadIdx.x;
+    const int sl = tid >> 2, quarter = tid & 3;  // segment of the step, a quarter of its slots
+    if (tid == 0) s_bad = 0;
+    __syncthreads();
+    uint32_t thr = krow[a.tau_off];
+    bool strict = false;        // accept key > thr (after a cut) or key >= thr
+    int pool = 0;
+    for (int base = 0; base < nseg; base += 64) {
+        const int sgi = base + sl;
+        const int c = sgi < nseg ? (int)krow[sgi] : 0;
+        if (c > kSegCap) s_bad = 1;
+        const int cc = c < kSegCap ? c : kSegCap;
+        const uint2* lst = (const uint2*)(krow + a.list_off + (int64_t)(sgi < nseg ? sgi : 0) * (2 * kSegCap));
+        uint2 ev[16];
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            const int e = 16 * quarter + u;
+            ev[u] = e < cc ? lst[e] : make_uint2(0u, 0u);
+        }
+        int off = 0, tot = 0;
+#pragma unroll 1
+        for (int attempt = 0; attempt < 2; ++attempt) {
+            int mine = 0;
+#pragma unroll
+            for (int u = 0; u < 16; ++u)
+                mine += 16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr);
+            off = pool + block_scan256(mine, part, tot);
+            if (pool + tot <= cap) break;            // workgroup-uniform
+            thr = compact_to_topk(ckeys, cidx, pool, K, sh);
+            pool = K;
+            strict = true;
+        }
+#pragma unroll
+        for (int u = 0; u < 16; ++u) {
+            if (16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr)) {
+                ckeys[off] = ev[u].x;
+                cidx[off] = (int32_t)ev[u].y;
+                ++off;
+            }
+        }
+        pool += tot;
+        __syncthreads();
+    }
+    if (s_bad || pool < K) {
+        if (tid == 0) {
+            const uint32_t slot = atomicAdd(&a.ctl[0], 1u);
+            a.ctl[1 + slot] = ((uint32_t)qi << 8) | ((uint32_t)blockIdx.y << 2) | (uint32_t)g;
+        }
+        return;
+    }
+    uint32_t prefix, pmask;
+    int krem;
+    radix_kth(ckeys, pool, K, sh, prefix, pmask, krem);
+    const int64_t rg = (sq.q_offset + qi) * kGroups + g;
+    select_ordered_output(ckeys, cidx, pool, prefix, pmask, krem, a.sel + rg * K,
+                          a.sel_scores ? a.sel_scores + rg * K : nullptr, sh);
+}
+
+// Failed listed rows, again in full: every key of the row's query (all four
+// groups, one wavefront per range of split_blocks candidates) into its key
+// rows, over the launch's failed-row list (a grid-stride loop: the count is
+// known only on the device).
+__global__ __launch_bounds__(256) void index_rescore_kernel(SeqTable seqs, IndexArgs a) {
+    const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    const int qq = lane >> 4, m = lane & 15;
+    const int64_t units = (int64_t)a.ctl[0] * a.n_split;
+    for (int64_t u = (int64_t)blockIdx.x * 4 + wave; u < units; u += (int64_t)gridDim.x * 4) {
+        const uint32_t item = a.ctl[1 + u / a.n_split];
+        const int split = (int)(u % a.n_split);
+        const DevSeq sq = seqs.s[(item >> 2) & 63];
+        const int64_t qi = item >> 8;
+        const int64_t nb = (sq.pos0 + qi) / a.block_size;
+        const int64_t r_lo = (int64_t)split * a.split_blocks;
+        const int64_t r_hi = nb < r_lo + a.split_blocks ? nb : r_lo + a.split_blocks;
+        if (r_lo >= r_hi) continue;
+        bf16x8 af[4];
+        const uint4* qf = a.q_frag + (sq.ws_row + qi) * 256;
+#pragma unroll
+        for (int kk = 0; kk < 4; ++kk) af[kk] = as_bf16x8(qf[kk * 64 + lane]);
+        const float4 wv = *(const float4*)(a.w + ((sq.q_offset + qi) * kGroups + qq) * kIdxHeads);
+        const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
+        uint32_t* keys = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
+        for (int64_t r0 = r_lo; r0 < r_hi; r0 += 16) {
+            const int64_t r = r0 + m < r_hi ? r0 + m : r_lo;
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                acc = mfma_16x16x32(af[kk], as_bf16x8(load16(store + r * kIdxDim + 32 * kk)), acc);
+            float s = wv.x * fmaxf(acc[0], 0.f);
+            s += wv.y * fmaxf(acc[1], 0.f);
+            s += wv.z * fmaxf(acc[2], 0.f);
+            s += wv.w * fmaxf(acc[3], 0.f);
+            if (r0 + m < r_hi) keys[r0 + m] = score_key(s);
+        }
+    }
+}
+
+// Failed listed rows: the long-row select over the keys just written.
+__global__ __launch_bounds__(256) void index_select_rescue_kernel(SeqTable seqs, IndexArgs a) {
+    extern __shared__ uint32_t lds_keys[];
+    __shared__ SelectShared<4> sh;
+    const uint32_t count = a.ctl[0];
+    for (uint32_t it = blockIdx.x; it < count; it += gridDim.x) {
+        const uint32_t item = a.ctl[1 + it];
+        select_row<true, 4>(seqs.s[(item >> 2) & 63], item >> 8, (int)(item & 3), a, lds_keys, sh);
+        __syncthreads();
+    }
+}
+
 }  // namespace
 
 template <int NW>
-static hipError_t launch_select_long(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a, hipStream_t stream) {
+static size_t select_long_lds(const IndexArgs& a) {
     const int64_t max_b = a.key_stride;
     const int64_t cand = 2 * (int64_t)select_capacity(a.topk, NW);
     const int64_t samp = max_b / 4 < kSelectSampleMax ? max_b / 4 : kSelectSampleMax;
-    const size_t lds = (size_t)(cand > samp ? cand : samp) * sizeof(uint32_t);
+    return (size_t)(cand > samp ? cand : samp) * sizeof(uint32_t);
+}
+
+template <int NW>
+static hipError_t launch_select_long(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a, hipStream_t stream) {
+    const size_t lds = select_long_lds<NW>(a);
     hipError_t e = hipFuncSetAttribute((const void*)index_select_kernel<true, NW>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
@@ -887,8 +1209,10 @@ static hipError_t launch_select_long(const SeqTable& seqs, int64_t max_nq, const
     return hipGetLastError();
 }
 
+// keyed_long = false: no long row of the launch selects from its keys (every
+// one is listed), so the long-row select is not launched
 static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
-                                hipStream_t stream) {
+                                hipStream_t stream, bool keyed_long = true) {
     const int64_t max_b = a.key_stride;
     dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
     // short rows (skipped when every sequence's first query already has a
@@ -908,7 +1232,7 @@ static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const Inde
         hipLaunchKernelGGL((index_select_kernel<false, 4>), grid, dim3(256), lds_s, stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (max_b <= kSelectStageKeys) return e;
+    if (max_b <= kSelectStageKeys || !keyed_long) return e;
     // long rows: a few rows (decode) get sixteen wavefronts each, so each
     // row's scan has four times the loads in flight
     // (the candidate list then takes k plus one 16384-key step: k <= 1024
@@ -945,15 +1269,59 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
                               hipStream_t stream) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
     const int64_t n_qt = (max_nq + kScoreTileQueries - 1) / kScoreTileQueries;
+    // which kinds of tiles the launch holds (listed: long rows, candidate
+    // lists; keyed: every key written)
+    bool any_listed = false, any_keyed = false, keyed_long = false;
+    for (int i = 0; i < seqs.n; ++i) {
+        const DevSeq& d = seqs.s[i];
+        for (int64_t q0 = 0; q0 < d.n_q; q0 += kScoreTileQueries) {
+            const int64_t n0 = (d.pos0 + q0) / a.block_size;
+            const bool l = a.listed && list_tile(n0, a.topk);
+            any_listed |= l;
+            any_keyed |= !l;
+            const int64_t q1 = q0 + kScoreTileQueries < d.n_q ? q0 + kScoreTileQueries : d.n_q;
+            keyed_long |= !l && (d.pos0 + q1 - 1) / a.block_size > kSelectStageKeys;
+        }
+    }
+    hipError_t e;
     hipLaunchKernelGGL(index_qfrag_kernel, dim3((unsigned)((max_nq + 3) / 4), (unsigned)seqs.n),
                        dim3(256), 0, stream, seqs, a);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    dim3 grid((unsigned)(n_qt * a.n_split), (unsigned)seqs.n);
-    hipLaunchKernelGGL(index_score_tile_kernel, grid, dim3(256), 0, stream, seqs, a);
-    e = hipGetLastError();
-    if (e != hipSuccess) return e;
-    return launch_select(seqs, max_nq, a, stream);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const dim3 rows_grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
+    if (any_listed) {
+        hipLaunchKernelGGL(index_sample_kernel, dim3((unsigned)(n_qt * kSampleParts), (unsigned)seqs.n), dim3(256), 0,
+                           stream, seqs, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+        hipLaunchKernelGGL(index_tau_kernel, rows_grid, dim3(256), 0, stream, seqs, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    const dim3 grid((unsigned)(n_qt * a.n_split), (unsigned)seqs.n);
+    if (any_keyed) {
+        hipLaunchKernelGGL(index_score_tile_kernel<false>, grid, dim3(256), 0, stream, seqs, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (any_listed) {
+        hipLaunchKernelGGL(index_score_tile_kernel<true>, grid, dim3(256), 0, stream, seqs, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (any_keyed && (e = launch_select(seqs, max_nq, a, stream, keyed_long)) != hipSuccess) return e;
+    if (!any_listed) return hipSuccess;
+    const size_t lds_l = (size_t)list_capacity(a.topk) * 8;
+    if ((e = hipFuncSetAttribute((const void*)index_list_select_kernel,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_l)) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(index_list_select_kernel, rows_grid, dim3(256), lds_l, stream, seqs, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    // rows whose lists failed (usually none): scored again, then selected
+    // from their keys; grid-stride loops over the count the device holds
+    hipLaunchKernelGGL(index_rescore_kernel, dim3(1024), dim3(256), 0, stream, seqs, a);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    const size_t lds_r = select_long_lds<4>(a);
+    if ((e = hipFuncSetAttribute((const void*)index_select_rescue_kernel,
+                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r)) != hipSuccess)
+        return e;
+    hipLaunchKernelGGL(index_select_rescue_kernel, dim3(512), dim3(256), lds_r, stream, seqs, a);
+    return hipGetLastError();
 }
 
 }  // namespace sgqa

@@ -105,6 +105,9 @@ struct IndexPlan {
     int64_t rows = 0;           // key-workspace rows: queries of the largest launch
     int64_t chunk_rows = 0;     // tiled mode: queries per launch (one key pass)
     size_t frag_off = 0;        // tiled mode: byte offset of the query fragments
+    size_t ctl_off = 0;         // tiled mode: byte offset of the failed-row list
+    bool listed = false;        // tiled mode: long rows may use candidate lists
+    int32_t list_off = 0, samp_off = 0, tau_off = 0;
     size_t ws = 0;
 };
 
@@ -181,7 +184,19 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
         p.split_blocks = kTiledSplitBlocks;
         p.n_split = (int)std::max<int64_t>(1, (max_b + kTiledSplitBlocks - 1) / kTiledSplitBlocks);
         p.frag_off = align_up((size_t)chunk * row_bytes);
-        p.ws = p.frag_off + align_up((size_t)chunk * kQueryFragBytes);
+        p.ctl_off = p.frag_off + align_up((size_t)chunk * kQueryFragBytes);
+        p.ws = p.ctl_off + align_up((size_t)(1 + chunk * sgqa::kGroups) * 4);
+        // candidate lists share a key row with one count per segment, the
+        // sample and the threshold; rows short enough to hold them all are
+        // long enough to be listed
+        const int64_t nseg = (stride + sgqa::kSegBlocks - 1) / sgqa::kSegBlocks;
+        const int64_t list_off = (nseg + 63) / 64 * 64;
+        const int64_t samp_off = list_off + 2 * sgqa::kSegCap * nseg;
+        const int64_t tau_off = samp_off + sgqa::kListSampleMax;
+        p.listed = max_b >= sgqa::kListMinBlocks && tau_off < stride;
+        p.list_off = (int32_t)list_off;
+        p.samp_off = (int32_t)samp_off;
+        p.tau_off = (int32_t)tau_off;
         return p;
     }
     p.rows = max_launch_rows(s, n, [](const sgqa_seq& q) { return q.n_q; });
@@ -332,9 +347,15 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     rope_table(c, a.theta);
     a.part_key = nullptr;
     a.q_frag = nullptr;
+    a.ctl = nullptr;
     a.key_stride = p.key_stride;
+    a.listed = p.listed ? 1 : 0;
+    a.list_off = p.list_off;
+    a.samp_off = p.samp_off;
+    a.tau_off = p.tau_off;
     if (p.key_stride > 0) a.part_key = (uint32_t*)ws;
     if (p.frag_off > 0) a.q_frag = (uint4*)((char*)ws + p.frag_off);
+    if (p.ctl_off > 0) a.ctl = (uint32_t*)((char*)ws + p.ctl_off);
     if (p.mode == IndexMode::Tiled) {
         // launches of at most chunk_rows queries (one pass over the key
         // workspace each) and kMaxSeqsPerLaunch entries, filled in call

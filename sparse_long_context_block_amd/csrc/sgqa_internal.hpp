@@ -3,6 +3,7 @@
 #pragma once
 
 #include <hip/hip_runtime.h>
+#include <math.h>
 #include <stdint.h>
 
 namespace sgqa {
@@ -67,7 +68,12 @@ struct IndexArgs {
     uint32_t* part_key;         // split calls: score keys [launch rows, G, key_stride],
                                 // row = DevSeq::ws_row + query index
     uint4* q_frag;              // tiled calls: indexer A fragments [launch rows, 4, 64]
+    uint32_t* ctl;              // tiled calls: [0] rows whose list failed, [1..] those rows
     int64_t key_stride;
+    int32_t listed;             // tiled calls: long rows may select from candidate lists
+    int32_t list_off;           // listed rows: u32 offsets inside a key row of the
+    int32_t samp_off;           //   candidate lists, the sample keys and the threshold
+    int32_t tau_off;            //   (segment counts at offset 0)
     int32_t block_size;
     int32_t topk;               // K
     int32_t cap;                // per-row LDS buffer capacity C (fused kernel)
@@ -100,6 +106,47 @@ struct AttnMergeArgs {
     float* lse;
     int32_t n_split;
 };
+
+// ---------------------------------------------------------------------------
+// candidate lists of long rows (tiled calls)
+//
+// A 16-query tile whose first query has n0 candidate blocks is "listed" when
+// n0 is large: its queries' selections then come from candidate lists
+// instead of every score key.  A sample of S scores per (query, group) gives
+// a threshold tau, the j-th largest sample score, j = ceil(m k S / n0) with
+// m = 1 + 5 / sqrt(k S / n0), so that about m k scores are expected at or
+// above tau and fewer than k only five standard deviations out.  The score
+// step keeps the scores >= tau, with their block ids, in lists of at most
+// kSegCap entries per segment of kSegBlocks blocks (m k kSegBlocks / n0 <= 21
+// expected per segment).  A row whose lists overflow, or hold fewer than k
+// entries, or more than the select can stage, is scored again in full and
+// selected from its keys, so the result is always the exact top k.
+// ---------------------------------------------------------------------------
+constexpr int kSegBlocks = 256;
+constexpr int kSegCap = 64;
+constexpr int64_t kListMinBlocks = 32768;
+constexpr int64_t kListMaxBlocks = (int64_t)1 << 21;
+constexpr int kListSampleMax = 2048;
+
+__host__ __device__ inline int list_sample(int64_t n0) {
+    const int64_t s = n0 / 4 < kListSampleMax ? n0 / 4 : kListSampleMax;
+    return (int)(s / 16 * 16);
+}
+__host__ __device__ inline double list_margin(int64_t n0, int k) {
+    return 1.0 + 5.0 / sqrt((double)k * list_sample(n0) / (double)n0);
+}
+__host__ __device__ inline bool list_tile(int64_t n0, int k) {
+    return n0 >= kListMinBlocks && n0 <= kListMaxBlocks &&
+           list_margin(n0, k) * k * kSegBlocks <= 21.0 * (double)n0;
+}
+__host__ __device__ inline int list_rank(int64_t n0, int k) {
+    const int S = list_sample(n0);
+    const double j = ceil(list_margin(n0, k) * k * S / (double)n0);
+    return j < 1.0 ? 1 : (j > S ? S : (int)j);
+}
+// entries of a listed row's LDS pool (8 B each): k plus a step of 64 full
+// segments, with room to spare
+__host__ __device__ constexpr int list_capacity(int k) { return k < 1024 ? 8192 : 16384; }
 
 // a launch table travels in the kernel arguments, which hold at most 4 KiB
 static_assert(sizeof(SeqTable) + sizeof(IndexArgs) <= 4096, "index kernel arguments fit");

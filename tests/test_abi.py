@@ -165,11 +165,12 @@ def test_workspace_size_invalid_args_is_zero(L):
 
 def test_prefill_key_workspace(L):
     # prefills of 1024+ queries keep 4-byte score keys per (row, group,
-    # candidate) and each query's 16 x 128 bf16 indexer rows in the
-    # workspace; compression and attention need none
+    # candidate), each query's 16 x 128 bf16 indexer rows and a list of rows
+    # to score again (a count and one word per row and group, rounded up to
+    # 256 B) in the workspace; compression and attention need none
     cfg = sg.config()
     # key rows: 1023 candidates padded to 1088 (64 x an odd count)
-    need = 8192 * 4 * 1088 * 4 + 8192 * 16 * 128 * 2
+    need = 8192 * 4 * 1088 * 4 + 8192 * 16 * 128 * 2 + (1 + 8192 * 4) * 4 // 256 * 256 + 256
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_INDEX_TOPK) == need
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_FORWARD) == need
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_COMPRESS) == 0

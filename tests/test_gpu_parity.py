@@ -71,6 +71,15 @@ def test_tiled_index_rows_out_of_call_order():
     _run_and_check("multi_b1_shuffled", n_rows=24, check_all_store=False)
 
 
+@pytest.mark.parametrize("name", ["chunk_40000_1024_b1_k64", "chunk_65536_1024_b1_k2048",
+                                  "chunk_300000_1040_b8_k512"])
+def test_listed_long_rows(name):
+    # tiled calls whose tiles start at 32768+ candidate blocks: their rows
+    # select from the candidates at or above a sampled threshold (the last
+    # case with a ragged 16-query tile)
+    _run_and_check(name, n_rows=24, check_all_store=False)
+
+
 def test_decode_split_paths():
     st = _run_and_check("decode_small", n_rows=1, check_all_store=True)
     assert st["rows"] == 8

@@ -12,7 +12,12 @@ id), so no oracle run is needed:
   samples (2048 blocks at k = 3072, 512 at k = 1024): the sampled threshold
   admits fewer than k keys, so the select must fall back to a radix over
   the whole row; the answer is those blocks plus the lowest-numbered others
-  (score 0, ties to the lower id).
+  (score 0, ties to the lower id);
+* the same two situations for the candidate lists of prefill calls whose
+  rows have 32768+ candidates: all scores equal overflow every segment's
+  list, and hot blocks placed on the positions the list threshold is
+  sampled from leave fewer than k candidates; both rows are scored again in
+  full and selected from their keys.
 
 Inputs are seeded random tensors (or constructed exactly), written straight
 into the indexer's inputs; only the index step runs.
@@ -43,6 +48,7 @@ def _run_index(cfg, seqs, n_rows, q_idx, w, store):
     (1100, 160000, 8, 512),       # tiled call at B = 8, 20000+ candidates per row
     (3, 300000, 8, 2048),         # decode-sized, several queries, k = 2048
     (2, 40000, 1, 512),           # decode-sized, k <= 1024: 16-wavefront select
+    (1100, 300000, 8, 512),       # tiled call, listed rows: every segment's list overflows
 ])
 def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
     log("case equal scores", n_q, pos0, B, K)
@@ -99,3 +105,44 @@ def test_sample_overestimate_falls_back_exactly(K, hot_groups):
         assert (ssc[0, g][~is_hot] == 0.0).all()
         hs = ssc[0, g][is_hot]
         assert (hs > 100.0).all() and (hs == hs[0]).all()
+
+
+def test_listed_threshold_above_kth_falls_back_exactly():
+    # 1024 queries at B = 1 from t = 40960: tiles start at 40960+ candidates,
+    # so their rows are listed.  The list threshold is the j-th largest of a
+    # sample of 2048 scores taken as 128 groups of 16 consecutive blocks, group
+    # g starting at g * (n0 - 16) // 127 (n0 = the tile's first position);
+    # j = ceil(m k S / n0) = 51 here.  The blocks of the first four groups of
+    # the first tile are the only positive scores: 64 >= j of them, fewer
+    # than k, so the threshold admits fewer than k candidates and the row
+    # must be scored again (later tiles sample other blocks: their lists
+    # overflow instead); every row's answer is still the hot blocks plus the
+    # lowest-numbered others.
+    B, K, n_q, pos0 = 1, 512, 1024, 40960
+    S, ngrp = 2048, 128
+    n0 = pos0 // B
+    hot = sorted({(g * (n0 - 16)) // (ngrp - 1) + i for g in range(4) for i in range(16)})
+    m = 1.0 + 5.0 / np.sqrt(K * S / n0)
+    j = int(np.ceil(m * K * S / n0))
+    assert j <= len(hot) < K
+    log("case listed-threshold fallback", n_q, pos0, K, len(hot), "j", j)
+    u = torch.zeros(128, dtype=torch.float32)
+    u[32:] = 1.0
+    cache = pos0 + n_q
+    store = torch.zeros(cache // B, 128, dtype=torch.float32)
+    store[hot] = u
+    q_idx = torch.zeros(n_q, 4, 4, 128, dtype=torch.float32)
+    q_idx[:, :, 0] = u
+    w = torch.zeros(n_q, 4, 4, dtype=torch.float32)
+    w[:, :, 0] = 1.0
+    cfg = sg.config(block_size=B, topk_blocks=K)
+    sel, ssc = _run_index(cfg, [sg.seq(n_q, pos0=pos0, block_size=B)], n_q,
+                          q_idx.to(torch.bfloat16).cuda(), w.cuda(), store.to(torch.bfloat16).cuda())
+    hot_set = set(hot)
+    cold = [r for r in range(K) if r not in hot_set][:K - len(hot)]
+    exp = np.array(sorted(hot + cold), dtype=np.int32)
+    is_hot = np.isin(exp, hot)
+    assert (sel == exp[None, None, :]).all()
+    assert (ssc[:, :, ~is_hot] == 0.0).all()
+    hs = ssc[:, :, is_hot]
+    assert (hs > 100.0).all() and (hs == hs[0, 0, 0]).all()
