@@ -439,8 +439,13 @@ constexpr int kStoreStrideU = kIdxDim + 8;    // bf16 per LDS store row (68 dwor
 static_assert(kSegBlocks % kStoreTile == 0, "a store tile lies inside one segment");
 
 template <bool LISTED>
-__global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, IndexArgs a) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void index_score_tile_kernel(
+    SeqTable seqs, IndexArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tiles[2][kStoreTile * kStoreStrideU];
+    // indexer weights of the 16 queries (query, group): read by the score
+    // epilogues from LDS (the 16 lanes of a group read one address) rather
+    // than held in registers
+    __shared__ float4 wlds[kScoreTileQueries][kGroups];
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t n_qt = (sq.n_q + kScoreTileQueries - 1) / kScoreTileQueries;
     const int64_t qt = blockIdx.x / a.n_split;
@@ -458,11 +463,16 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
 
     // ---- the wavefront's four queries: A fragments, weights, candidates ----
     bf16x8 af[4][4];
-    float4 wv[4];
     int lim[4];                   // candidates r_lo + [0, lim) of (query, group qq)
-    uint32_t kofs[4];             // byte offset of its key row (keys: from block r_lo)
     uint32_t tauv[4];             // listed: its threshold
-    int cnt[4];                   // listed: entries of the current segment
+    // byte offset of the key row of (query 4 * wave + j, group qq): kofs0 +
+    // j * krow_bytes (keys: from block r_lo)
+    const uint32_t krow_bytes = (uint32_t)(kGroups * a.key_stride * 4);
+    const uint32_t kofs0 = (uint32_t)((4 * wave * kGroups + qq) * a.key_stride * 4) +
+                           (LISTED ? 0u : 4u * (uint32_t)r_lo);
+    // listed: entries of the current segment per query, 8 bits each
+    // (saturating at 255: anything above kSegCap marks an overflow)
+    uint32_t cnts = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int qo = 4 * wave + j;
@@ -473,15 +483,11 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
         const uint4* qf = a.q_frag + (sq.ws_row + qi) * 256;
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) af[j][kk] = as_bf16x8(qf[kk * 64 + lane]);
-        wv[j] = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
+        if (m == 0) wlds[qo][qq] = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
         const int64_t nb = ok ? t / a.block_size : 0;
         const int64_t hi = nb < r_hi ? nb : r_hi;
         lim[j] = hi > r_lo ? (int)(hi - r_lo) : 0;
-        kofs[j] = (uint32_t)((qo * kGroups + qq) * a.key_stride * 4) + (LISTED ? 0u : 4u * (uint32_t)r_lo);
-        if (LISTED) {
-            tauv[j] = a.part_key[((sq.ws_row + qi) * kGroups + qq) * a.key_stride + a.tau_off];
-            cnt[j] = 0;
-        }
+        if (LISTED) tauv[j] = a.part_key[((sq.ws_row + qi) * kGroups + qq) * a.key_stride + a.tau_off];
     }
     if (r_lo >= r_hi) return;                       // workgroup-uniform
 
@@ -544,27 +550,31 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
             const int rr = rt + 16 * sub + m;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                float s = wv[j].x * fmaxf(acc[j][0], 0.f);
-                s += wv[j].y * fmaxf(acc[j][1], 0.f);
-                s += wv[j].z * fmaxf(acc[j][2], 0.f);
-                s += wv[j].w * fmaxf(acc[j][3], 0.f);
+                const float4 wv = wlds[4 * wave + j][qq];
+                float s = wv.x * fmaxf(acc[j][0], 0.f);
+                s += wv.y * fmaxf(acc[j][1], 0.f);
+                s += wv.z * fmaxf(acc[j][2], 0.f);
+                s += wv.w * fmaxf(acc[j][3], 0.f);
                 const uint32_t key = score_key(s);
+                const uint32_t kofs = kofs0 + (uint32_t)j * krow_bytes;
                 if (!LISTED) {
-                    const uint32_t off = rr < lim[j] ? kofs[j] + 4u * (uint32_t)rr : kDropped;
+                    const uint32_t off = rr < lim[j] ? kofs + 4u * (uint32_t)rr : kDropped;
                     __builtin_amdgcn_raw_buffer_store_b32(key, krs, (int)off, 0, 0);
                 } else {
                     // append (key, block id) to the segment's list: the 16
                     // lanes of group qq count the passing lanes below them
                     const bool pass = rr < lim[j] && key >= tauv[j];
                     const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * qq)) & 0xFFFFu;
-                    const int pos = cnt[j] + __builtin_popcount(gm & ((1u << m) - 1u));
-                    const uint32_t off = pass && pos < kSegCap
-                        ? kofs[j] + 4u * ((uint32_t)a.list_off + seg * (2 * kSegCap) + 2u * (uint32_t)pos)
+                    const uint32_t cj = (cnts >> (8 * j)) & 0xFFu;
+                    const uint32_t pos = cj + (uint32_t)__builtin_popcount(gm & ((1u << m) - 1u));
+                    const uint32_t off = pass && pos < (uint32_t)kSegCap
+                        ? kofs + 4u * ((uint32_t)a.list_off + seg * (2 * kSegCap) + 2u * pos)
                         : kDropped;
                     const uint32_t blk = (uint32_t)(r_lo + rr);
                     typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
                     __builtin_amdgcn_raw_buffer_store_b64(u32x2{key, blk}, krs, (int)off, 0, 0);
-                    cnt[j] += __builtin_popcount(gm);
+                    const uint32_t cn = cj + (uint32_t)__builtin_popcount(gm);
+                    cnts = (cnts & ~(0xFFu << (8 * j))) | ((cn < 255u ? cn : 255u) << (8 * j));
                 }
             }
         }
@@ -574,10 +584,11 @@ __global__ __launch_bounds__(256) void index_score_tile_kernel(SeqTable seqs, In
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool wr = m == 0 && (int64_t)seg * kSegBlocks - r_lo < lim[j];
-                __builtin_amdgcn_raw_buffer_store_b32((uint32_t)cnt[j], krs,
-                                                      (int)(wr ? kofs[j] + 4u * seg : kDropped), 0, 0);
-                cnt[j] = 0;
+                __builtin_amdgcn_raw_buffer_store_b32((cnts >> (8 * j)) & 0xFFu, krs,
+                                                      (int)(wr ? kofs0 + (uint32_t)j * krow_bytes + 4u * seg
+                                                               : kDropped), 0, 0);
             }
+            cnts = 0u;
         }
         if (more) lstore(tiles[cur ^ 1], stage);
         cur ^= 1;
