@@ -550,12 +550,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
             const int rr = rt + 16 * sub + m;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const float4 wv = wlds[4 * wave + j][qq];
-                float s = wv.x * fmaxf(acc[j][0], 0.f);
-                s += wv.y * fmaxf(acc[j][1], 0.f);
-                s += wv.z * fmaxf(acc[j][2], 0.f);
-                s += wv.w * fmaxf(acc[j][3], 0.f);
-                const uint32_t key = score_key(s);
+                const uint32_t key = score_key_nz(head_score(acc[j], wlds[4 * wave + j][qq]));
                 const uint32_t kofs = kofs0 + (uint32_t)j * krow_bytes;
                 if (!LISTED) {
                     const uint32_t off = rr < lim[j] ? kofs + 4u * (uint32_t)rr : kDropped;
@@ -1008,13 +1003,8 @@ __global__ __launch_bounds__(256) void index_sample_kernel(SeqTable seqs, IndexA
 #pragma unroll
             for (int j = 0; j < 4; ++j) acc[j] = mfma_16x16x32(af[j][kk], bf[kk], acc[j]);
 #pragma unroll
-        for (int j = 0; j < 4; ++j) {
-            float s = wv[j].x * fmaxf(acc[j][0], 0.f);
-            s += wv[j].y * fmaxf(acc[j][1], 0.f);
-            s += wv[j].z * fmaxf(acc[j][2], 0.f);
-            s += wv[j].w * fmaxf(acc[j][3], 0.f);
-            if (sk[j]) sk[j][16 * gi + m] = score_key(s);
-        }
+        for (int j = 0; j < 4; ++j)
+            if (sk[j]) sk[j][16 * gi + m] = score_key_nz(head_score(acc[j], wv[j]));
     }
 }
 
@@ -1063,12 +1053,15 @@ __device__ __forceinline__ int block_scan256(int v, int* part, int& total) {
 }
 
 // Listed rows: the top k from the candidate lists.  The segments' lists are
-// streamed into an LDS pool in block order, 64 segments per step (four
-// threads per segment, counts and offsets from one workgroup scan); a step
-// that would overflow the pool first cuts it to its top k and raises the
-// threshold to the k-th key, as the long-row select does (rows whose scores
-// tie at the threshold can list many more than k entries).  The pool is then
-// selected exactly.  A row whose lists cannot give the exact answer -- a
+// streamed into an LDS pool in block order.  While the threshold is still
+// tau every listed entry passes, so 256 segments at a time go in whole (one
+// thread per segment, offsets from one workgroup scan of the counts).
+// Otherwise -- or when those 256 would overflow the pool -- they go 64 at a
+// time with every entry tested (four threads per segment); a step that would
+// overflow the pool first cuts it to its top k and raises the threshold to
+// the k-th key, as the long-row select does (rows whose scores tie at the
+// threshold can list many more than k entries).  The pool is then selected
+// exactly.  A row whose lists cannot give the exact answer -- a
 // segment that dropped entries, or fewer than k entries (the threshold was
 // above the k-th score) -- is appended to the launch's failed rows instead,
 // to be scored again in full.
@@ -1097,41 +1090,63 @@ __global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, I
     uint32_t thr = krow[a.tau_off];
     bool strict = false;        // accept key > thr (after a cut) or key >= thr
     int pool = 0;
-    for (int base = 0; base < nseg; base += 64) {
-        const int sgi = base + sl;
-        const int c = sgi < nseg ? (int)krow[sgi] : 0;
-        if (c > kSegCap) s_bad = 1;
-        const int cc = c < kSegCap ? c : kSegCap;
-        const uint2* lst = (const uint2*)(krow + a.list_off + (int64_t)(sgi < nseg ? sgi : 0) * (2 * kSegCap));
-        uint2 ev[16];
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            const int e = 16 * quarter + u;
-            ev[u] = e < cc ? lst[e] : make_uint2(0u, 0u);
-        }
-        int off = 0, tot = 0;
-#pragma unroll 1
-        for (int attempt = 0; attempt < 2; ++attempt) {
-            int mine = 0;
-#pragma unroll
-            for (int u = 0; u < 16; ++u)
-                mine += 16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr);
-            off = pool + block_scan256(mine, part, tot);
-            if (pool + tot <= cap) break;            // workgroup-uniform
-            thr = compact_to_topk(ckeys, cidx, pool, K, sh);
-            pool = K;
-            strict = true;
-        }
-#pragma unroll
-        for (int u = 0; u < 16; ++u) {
-            if (16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr)) {
-                ckeys[off] = ev[u].x;
-                cidx[off] = (int32_t)ev[u].y;
-                ++off;
+    for (int chunk = 0; chunk < nseg; chunk += 256) {
+        if (!strict) {
+            const int sg = chunk + tid;
+            const int c = sg < nseg ? (int)krow[sg] : 0;
+            if (c > kSegCap) s_bad = 1;
+            const int cc = c < kSegCap ? c : kSegCap;
+            int tot;
+            const int off = pool + block_scan256(cc, part, tot);
+            if (pool + tot <= cap) {                 // workgroup-uniform
+                const uint2* lst = (const uint2*)(krow + a.list_off + (int64_t)(sg < nseg ? sg : 0) * (2 * kSegCap));
+                for (int e = 0; e < cc; ++e) {
+                    const uint2 kv = lst[e];
+                    ckeys[off + e] = kv.x;
+                    cidx[off + e] = (int32_t)kv.y;
+                }
+                pool += tot;
+                __syncthreads();
+                continue;
             }
         }
-        pool += tot;
-        __syncthreads();
+        // 64 segments per step, every entry tested
+        for (int base = chunk; base < chunk + 256 && base < nseg; base += 64) {
+            const int sgi = base + sl;
+            const int c = sgi < nseg ? (int)krow[sgi] : 0;
+            if (c > kSegCap) s_bad = 1;
+            const int cc = c < kSegCap ? c : kSegCap;
+            const uint2* lst = (const uint2*)(krow + a.list_off + (int64_t)(sgi < nseg ? sgi : 0) * (2 * kSegCap));
+            uint2 ev[16];
+    #pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                const int e = 16 * quarter + u;
+                ev[u] = e < cc ? lst[e] : make_uint2(0u, 0u);
+            }
+            int off = 0, tot = 0;
+    #pragma unroll 1
+            for (int attempt = 0; attempt < 2; ++attempt) {
+                int mine = 0;
+    #pragma unroll
+                for (int u = 0; u < 16; ++u)
+                    mine += 16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr);
+                off = pool + block_scan256(mine, part, tot);
+                if (pool + tot <= cap) break;            // workgroup-uniform
+                thr = compact_to_topk(ckeys, cidx, pool, K, sh);
+                pool = K;
+                strict = true;
+            }
+    #pragma unroll
+            for (int u = 0; u < 16; ++u) {
+                if (16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr)) {
+                    ckeys[off] = ev[u].x;
+                    cidx[off] = (int32_t)ev[u].y;
+                    ++off;
+                }
+            }
+            pool += tot;
+            __syncthreads();
+        }
     }
     if (s_bad || pool < K) {
         if (tid == 0) {
@@ -1178,11 +1193,7 @@ __global__ __launch_bounds__(256) void index_rescore_kernel(SeqTable seqs, Index
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 acc = mfma_16x16x32(af[kk], as_bf16x8(load16(store + r * kIdxDim + 32 * kk)), acc);
-            float s = wv.x * fmaxf(acc[0], 0.f);
-            s += wv.y * fmaxf(acc[1], 0.f);
-            s += wv.z * fmaxf(acc[2], 0.f);
-            s += wv.w * fmaxf(acc[3], 0.f);
-            if (r0 + m < r_hi) keys[r0 + m] = score_key(s);
+            if (r0 + m < r_hi) keys[r0 + m] = score_key_nz(head_score(acc, wv));
         }
     }
 }

@@ -233,6 +233,24 @@ __device__ __forceinline__ uint32_t score_key(float s) {
     return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
 }
 
+// The indexer score of one (query, group, block) from the MFMA result of its
+// four heads: sum_i w_i * max(0, dot_i), accumulated from +0 with fused
+// multiply-adds, so an exactly zero score is +0, never -0 (equal scores
+// compare equal as keys).  max(0, x) is an integer max on the bits (a
+// negative float, -0 included, is a negative integer); the inputs are finite.
+__device__ __forceinline__ float relu_bits(float x) { return __int_as_float(max(__float_as_int(x), 0)); }
+__device__ __forceinline__ float head_score(f32x4 acc, float4 w) {
+    float s = fmaf(w.x, relu_bits(acc[0]), 0.0f);
+    s = fmaf(w.y, relu_bits(acc[1]), s);
+    s = fmaf(w.z, relu_bits(acc[2]), s);
+    return fmaf(w.w, relu_bits(acc[3]), s);
+}
+// score_key for a score that is not -0 (head_score's results)
+__device__ __forceinline__ uint32_t score_key_nz(float s) {
+    const uint32_t u = __float_as_uint(s);
+    return u ^ ((uint32_t)((int32_t)u >> 31) | 0x80000000u);
+}
+
 __device__ __forceinline__ float key_score(uint32_t k) {
     uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
     return __uint_as_float(u);
