@@ -225,6 +225,48 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                  const void* k_cache, const void* v_cache, void* out, float* lse, void* ws,
                  size_t ws_bytes, void* hip_stream);
 
+/*
+ * Paged caches (page section "Cache capacity: 4,104 reads do not mean 4,104
+ * stored tokens": global capacity rounded up to 16-token pages, with page
+ * tables).  The per-token tensors live in a pool of n_pages pages of 16
+ * positions each:
+ *   k_pages, v_pages       bf16 [n_pages, 16, G, D]
+ *   proxy_pages            bf16 [n_pages, 16, Di]
+ *   logit_pages            fp32 [n_pages, 16, Di]
+ * page_table: int32 [page_table_len], device memory, owned by the caller.
+ * For a sequence, kv_offset is the index in page_table of its logical page 0:
+ * position u lives in physical page page_table[kv_offset + u / 16], slot
+ * u % 16 (the same table serves all four tensors).  kv_capacity (tokens) must
+ * satisfy kv_offset + ceil(kv_capacity / 16) <= page_table_len, else
+ * SGQA_ERR_CAPACITY; n_pages must be at most 2^27.  Page ids are read on the
+ * device only: an id outside [0, n_pages) is clamped into the pool, so it never
+ * reads outside it (the results are then meaningless).  A block never
+ * straddles two pages (B divides 16).  The store, queries, selections and
+ * outputs keep the layouts above, and the results equal those of the
+ * contiguous calls for the same logical contents.  Workspace: as the
+ * corresponding contiguous call (sgqa_workspace_size with SGQA_OP_COMPRESS,
+ * SGQA_OP_SPARSE_ATTN or SGQA_OP_FORWARD).
+ */
+int sgqa_compress_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                        const void* proxy_pages, const float* logit_pages, const int32_t* page_table,
+                        int64_t page_table_len, int64_t n_pages, const void* ln_gamma,
+                        const void* ln_beta, void* store, void* ws, size_t ws_bytes,
+                        void* hip_stream);
+
+int sgqa_sparse_attn_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                           const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* page_table, int64_t page_table_len, int64_t n_pages,
+                           const int32_t* sel, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* hip_stream);
+
+int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                       const void* proxy_pages, const float* logit_pages, const void* ln_gamma,
+                       const void* ln_beta, void* store, const void* q_idx, const float* w,
+                       const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
+                       const void* k_pages, const void* v_pages, const int32_t* page_table,
+                       int64_t page_table_len, int64_t n_pages, void* out, float* lse, void* ws,
+                       size_t ws_bytes, void* hip_stream);
+
 /* Static name of a status code. */
 const char* sgqa_status_string(int status);
 

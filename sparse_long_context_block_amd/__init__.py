@@ -28,8 +28,8 @@ import torch
 
 __all__ = [
     "Config", "Seq", "SgqaError", "config", "seq", "lib", "workspace_size", "compress",
-    "index_topk", "sparse_attn", "forward", "LIB_PATH", "OP_COMPRESS", "OP_INDEX_TOPK",
-    "OP_SPARSE_ATTN", "OP_FORWARD",
+    "index_topk", "sparse_attn", "forward", "compress_paged", "sparse_attn_paged", "forward_paged",
+    "LIB_PATH", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_SPARSE_ATTN", "OP_FORWARD",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgqa.so")
@@ -128,6 +128,14 @@ def lib() -> ctypes.CDLL:
     L.sgqa_forward.argtypes = [cfgp, seqp, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                P, SZ, P]
     L.sgqa_forward.restype = ctypes.c_int
+    I64 = ctypes.c_int64
+    L.sgqa_compress_paged.argtypes = [cfgp, seqp, I32, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    L.sgqa_compress_paged.restype = ctypes.c_int
+    L.sgqa_sparse_attn_paged.argtypes = [cfgp, seqp, I32, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    L.sgqa_sparse_attn_paged.restype = ctypes.c_int
+    L.sgqa_forward_paged.argtypes = [cfgp, seqp, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                     I64, I64, P, P, P, SZ, P]
+    L.sgqa_forward_paged.restype = ctypes.c_int
     L.sgqa_status_string.argtypes = [ctypes.c_int]
     L.sgqa_status_string.restype = ctypes.c_char_p
     L.sgqa_last_error.argtypes = []
@@ -242,3 +250,56 @@ def forward(cfg: Config, seqs: Sequence[Seq], proxy_k, comp_logits, store, q_idx
         _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
         _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", False), wsp, wsn,
         _stream_ptr(stream)))
+
+
+# ---------------------------------------------------------------------------
+# paged caches: per-token tensors in pools of 16-position pages, a sequence's
+# kv_offset indexing its first page-table entry (include/sgqa.h)
+# ---------------------------------------------------------------------------
+
+def _pages(page_table, pool):
+    ptp = _ptr(page_table, torch.int32, "page_table")
+    return ptp, int(page_table.numel()), int(pool.shape[0])
+
+
+def compress_paged(cfg: Config, seqs: Sequence[Seq], proxy_pages, logit_pages, page_table, store,
+                   ln_gamma=None, ln_beta=None, stream=None) -> None:
+    arr, n = _seq_array(seqs)
+    ptp, ptn, npg = _pages(page_table, proxy_pages)
+    _check(lib().sgqa_compress_paged(
+        ctypes.byref(cfg), arr, n, _ptr(proxy_pages, torch.bfloat16, "proxy_pages"),
+        _ptr(logit_pages, torch.float32, "logit_pages"), ptp, ptn, npg,
+        _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
+        _ptr(ln_beta, torch.bfloat16, "ln_beta", False),
+        _ptr(store, torch.bfloat16, "store"), None, 0, _stream_ptr(stream)))
+
+
+def sparse_attn_paged(cfg: Config, seqs: Sequence[Seq], q, k_pages, v_pages, page_table, sel, out,
+                      lse=None, ws=None, stream=None) -> None:
+    arr, n = _seq_array(seqs)
+    wsp, wsn, _own = _workspace(cfg, seqs, OP_SPARSE_ATTN, q.device, ws, stream)
+    ptp, ptn, npg = _pages(page_table, k_pages)
+    _check(lib().sgqa_sparse_attn_paged(
+        ctypes.byref(cfg), arr, n, _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_pages, torch.bfloat16, "k_pages"), _ptr(v_pages, torch.bfloat16, "v_pages"),
+        ptp, ptn, npg, _ptr(sel, torch.int32, "sel"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(lse, torch.float32, "lse", False), wsp, wsn, _stream_ptr(stream)))
+
+
+def forward_paged(cfg: Config, seqs: Sequence[Seq], proxy_pages, logit_pages, store, q_idx, w, sel,
+                  q, k_pages, v_pages, page_table, out, lse=None, sel_scores=None, ln_gamma=None,
+                  ln_beta=None, rms_gamma=None, ws=None, stream=None) -> None:
+    arr, n = _seq_array(seqs)
+    wsp, wsn, _own = _workspace(cfg, seqs, OP_FORWARD, q.device, ws, stream)
+    ptp, ptn, npg = _pages(page_table, k_pages)
+    _check(lib().sgqa_forward_paged(
+        ctypes.byref(cfg), arr, n, _ptr(proxy_pages, torch.bfloat16, "proxy_pages"),
+        _ptr(logit_pages, torch.float32, "logit_pages"),
+        _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
+        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _ptr(store, torch.bfloat16, "store"),
+        _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"),
+        _ptr(rms_gamma, torch.bfloat16, "rms_gamma", False), _ptr(sel, torch.int32, "sel"),
+        _ptr(sel_scores, torch.float32, "sel_scores", False), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_pages, torch.bfloat16, "k_pages"), _ptr(v_pages, torch.bfloat16, "v_pages"),
+        ptp, ptn, npg, _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", False),
+        wsp, wsn, _stream_ptr(stream)))

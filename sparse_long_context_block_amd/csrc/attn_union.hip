@@ -49,8 +49,10 @@ struct KVStage {
 };
 
 struct UnionCtx {
-    const uint16_t* kb;
+    const uint16_t* kb;        // group slice of the sequence's row 0, or of the page pool
     const uint16_t* vb;
+    const int32_t* pt;         // paged: the sequence's page table
+    int64_t n_pages;
     int64_t t_last;
     bool vwave;        // this wavefront carries V slots (wave-uniform)
     int o, pr;         // V slot: token octet, dim pair
@@ -95,8 +97,49 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
     return __builtin_amdgcn_make_buffer_rsrc((void*)(base + tile0 * kRowElems), (short)0, nrec, 0x00020000);
 }
 
+// Paged caches: rows 0..15 and 16..31 of a tile are two 16-token pages, and
+// every load of a wavefront falls in one of them (the V slots of octets 0
+// and 1 and the one K chunk of each V wavefront: rows 0..15, V wavefronts 0
+// to 2; octets 2 and 3: rows 16..31, V wavefronts 3 to 5; the three K chunks
+// of wavefronts 6 and 7: rows 16..31), so a wavefront takes one page's
+// resource.  Its records end at the group's slice of row t_last as in
+// tile_rsrc; a page wholly past t_last gets no records (reads zeros) and its
+// page-table entry is not read.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* pool, const UnionCtx& u, int64_t p0) {
+    const int64_t rows = u.t_last - p0 + 1;
+    if (rows <= 0) return __builtin_amdgcn_make_buffer_rsrc((void*)pool, (short)0, 0, 0x00020000);
+    int64_t pid = u.pt[p0 / kPageTokens];
+    pid = pid < 0 ? 0 : (pid >= u.n_pages ? u.n_pages - 1 : pid);
+    const int nrec = rows >= kPageTokens ? kPageTokens * kRowBytes : (int)(rows - 1) * kRowBytes + kHeadDim * 2;
+    return __builtin_amdgcn_make_buffer_rsrc((void*)(pool + pid * kPageTokens * kRowElems), (short)0, nrec,
+                                             0x00020000);
+}
+
+template <bool PAGED>
 __device__ __forceinline__ void gload(const UnionCtx& u, int tile, KVStage& r) {
     const int64_t tile0 = (int64_t)tile * kTileTok;
+    if (PAGED) {
+        constexpr uint32_t kHalf = kPageTokens * kRowBytes;
+        if (u.vwave) {
+            const bool hi = u.o >= 2;                // wave-uniform: V wavefronts 3..5
+            const __amdgpu_buffer_rsrc_t vr = page_rsrc(u.vb, u, tile0 + (hi ? kPageTokens : 0));
+            const __amdgpu_buffer_rsrc_t kr = page_rsrc(u.kb, u, tile0);
+            const uint32_t vo = u.voff - (hi ? kHalf : 0u);
+            uint32_t d[8];
+#pragma unroll
+            for (int e = 0; e < 8; ++e)
+                d[e] = __builtin_amdgcn_raw_buffer_load_b32(vr, (int)(vo + octet_token(0, e) * kRowBytes), 0, 0);
+            r.a = make_uint4(d[0], d[1], d[2], d[3]);
+            r.b = make_uint4(d[4], d[5], d[6], d[7]);
+            r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)u.koff[0], 0, 0));
+        } else {
+            const __amdgpu_buffer_rsrc_t kr = page_rsrc(u.kb, u, tile0 + kPageTokens);
+            r.a = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)(u.koff[0] - kHalf), 0, 0));
+            r.b = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)(u.koff[1] - kHalf), 0, 0));
+            r.c = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(kr, (int)(u.koff[2] - kHalf), 0, 0));
+        }
+        return;
+    }
     const __amdgpu_buffer_rsrc_t kr = tile_rsrc(u.kb, tile0, u.t_last);
     if (u.vwave) {
         const __amdgpu_buffer_rsrc_t vr = tile_rsrc(u.vb, tile0, u.t_last);
@@ -270,7 +313,7 @@ __device__ __forceinline__ void union_vector(UnionState& st, int ti, int n_tiles
 // read as zeros) and stored at its end.  The output is staged through LDS so
 // each query's 16 heads leave as one contiguous 6 KB row block.
 // ---------------------------------------------------------------------------
-template <int LOG2B>
+template <int LOG2B, bool PAGED>
 __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs a, int words) {
     constexpr int NW = 8, TQ = 16, NT = 512;
     extern __shared__ uint32_t bitmap[];                         // [TQ][words]
@@ -292,13 +335,16 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
     const int K = a.topk;
 
     UnionCtx u;
-    u.kb = a.k + (sq.kv_offset * kGroups + g) * kHeadDim;
-    u.vb = a.v + (sq.kv_offset * kGroups + g) * kHeadDim;
+    const int64_t row0 = PAGED ? 0 : sq.kv_offset;
+    u.kb = a.k + (row0 * kGroups + g) * kHeadDim;
+    u.vb = a.v + (row0 * kGroups + g) * kHeadDim;
+    u.pt = PAGED ? a.page_table + sq.kv_offset : nullptr;
+    u.n_pages = a.n_pages;
     u.t_last = t_last;
     union_ctx_init(u, tid);
     const int n_tiles = (int)(t_last / kTileTok) + 1;
     KVStage rs;
-    gload(u, 0, rs);
+    gload<PAGED>(u, 0, rs);
 
     // ---- per-query bitmaps of the selected blocks and the current block ----
     for (int i = tid; i < TQ * nwords; i += NT) bitmap[(i / nwords) * words + i % nwords] = 0u;
@@ -363,7 +409,7 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
     //      (past the end the last tile is fetched again into a buffer no
     //      longer read, which keeps loads and stores unconditional) ----
     lstore(kv_lds, u, rs);
-    gload(u, n_tiles > 1 ? 1 : 0, rs);
+    gload<PAGED>(u, n_tiles > 1 ? 1 : 0, rs);
     lstore(kv_lds + kBufElems, u, rs);
     __syncthreads();
     st.s = tile_scores(kv_lds, qf, lane);
@@ -371,7 +417,7 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
     for (int i = 0; i < n_tiles; ++i) {
         const int b_nxt = b_cur == 2 ? 0 : b_cur + 1;
         const int b_new = b_nxt == 2 ? 0 : b_nxt + 1;
-        gload(u, i + 2 < n_tiles ? i + 2 : n_tiles - 1, rs);
+        gload<PAGED>(u, i + 2 < n_tiles ? i + 2 : n_tiles - 1, rs);
         union_vector<LOG2B>(st, i, n_tiles, ln);
         union_matrix(st, qf, kv_lds + b_nxt * kBufElems, kv_lds + b_cur * kBufElems, ln);
         lstore(kv_lds + b_new * kBufElems, u, rs);
@@ -419,17 +465,30 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
 
 }  // namespace
 
-template <int LOG2B>
+template <int LOG2B, bool PAGED>
 static hipError_t launch_union_t(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                                  int words, hipStream_t stream) {
     const size_t lds = (size_t)16 * words * sizeof(uint32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)attn_union_kernel<LOG2B>,
+    hipError_t e = hipFuncSetAttribute((const void*)attn_union_kernel<LOG2B, PAGED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     const int64_t n_qt = (max_nq + 15) / 16;
     dim3 grid((unsigned)(n_qt * kGroups), (unsigned)seqs.n);
-    hipLaunchKernelGGL((attn_union_kernel<LOG2B>), grid, dim3(512), lds, stream, seqs, a, words);
+    hipLaunchKernelGGL((attn_union_kernel<LOG2B, PAGED>), grid, dim3(512), lds, stream, seqs, a, words);
     return hipGetLastError();
+}
+
+template <bool PAGED>
+static hipError_t launch_union_b(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a, int words,
+                                 hipStream_t stream) {
+    switch (a.block_size) {
+        case 1: return launch_union_t<0, PAGED>(seqs, max_nq, a, words, stream);
+        case 2: return launch_union_t<1, PAGED>(seqs, max_nq, a, words, stream);
+        case 4: return launch_union_t<2, PAGED>(seqs, max_nq, a, words, stream);
+        case 8: return launch_union_t<3, PAGED>(seqs, max_nq, a, words, stream);
+        case 16: return launch_union_t<4, PAGED>(seqs, max_nq, a, words, stream);
+        default: return hipErrorInvalidValue;
+    }
 }
 
 int union_queries_per_block() { return 16; }
@@ -437,14 +496,8 @@ int union_queries_per_block() { return 16; }
 hipError_t launch_attn_union(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                              int words, hipStream_t stream) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
-    switch (a.block_size) {
-        case 1: return launch_union_t<0>(seqs, max_nq, a, words, stream);
-        case 2: return launch_union_t<1>(seqs, max_nq, a, words, stream);
-        case 4: return launch_union_t<2>(seqs, max_nq, a, words, stream);
-        case 8: return launch_union_t<3>(seqs, max_nq, a, words, stream);
-        case 16: return launch_union_t<4>(seqs, max_nq, a, words, stream);
-        default: return hipErrorInvalidValue;
-    }
+    return a.page_table ? launch_union_b<true>(seqs, max_nq, a, words, stream)
+                        : launch_union_b<false>(seqs, max_nq, a, words, stream);
 }
 
 }  // namespace sgqa

@@ -55,11 +55,15 @@ __global__ __launch_bounds__(256) void compress_kernel(SeqTable seqs, CompressAr
     const double th0 = in_rope ? a.theta[pair_j] : 0.0;
     const double th1 = in_rope ? a.theta[pair_j + 1] : 0.0;
 
+    // the block's B tokens are consecutive rows (a 16-token page holds whole
+    // blocks: B divides 16)
+    const int64_t row0 = a.page_table ? paged_row(a.page_table + sq.kv_offset, a.n_pages, (int64_t)B * r)
+                                      : sq.kv_offset + (int64_t)B * r;
     float k0[B], k1[B], c0[B], c1[B];
 #pragma unroll
     for (int j = 0; j < B; ++j) {
         const int64_t pos = (int64_t)B * r + j;
-        const int64_t row = sq.kv_offset + pos;
+        const int64_t row = row0 + j;
         uint32_t xx = *(const uint32_t*)(a.proxy_k + row * kIdxDim + d0);
         float2 cc = *(const float2*)(a.logits + row * kIdxDim + d0);
         c0[j] = cc.x;

@@ -91,6 +91,31 @@ int check_seqs(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     return SGQA_OK;
 }
 
+// Paged per-token tensors: a page table of int32 physical page ids (device
+// memory), table_len entries, over a pool of n_pages pages of 16 positions.
+struct Paging {
+    const int32_t* table = nullptr;     // null: contiguous caches
+    int64_t n_pages = 0;
+};
+
+int check_paging(const sgqa_seq* s, int32_t n, const int32_t* table, int64_t table_len, int64_t n_pages) {
+    if (!table) return fail(SGQA_ERR_NULL, "page_table is NULL");
+    if (table_len <= 0 || n_pages <= 0)
+        return fail(SGQA_ERR_SHAPE, "page_table_len (%lld) and n_pages (%lld) must be positive",
+                    (long long)table_len, (long long)n_pages);
+    if (n_pages > ((int64_t)1 << 31) / sgqa::kPageTokens)
+        return fail(SGQA_ERR_SHAPE, "n_pages %lld above 2^27", (long long)n_pages);
+    for (int32_t i = 0; i < n; ++i) {
+        const int64_t pages = (s[i].kv_capacity + sgqa::kPageTokens - 1) / sgqa::kPageTokens;
+        if (s[i].kv_offset + pages > table_len)
+            return fail(SGQA_ERR_CAPACITY,
+                        "seqs[%d]: page-table entries %lld .. %lld past page_table_len %lld", i,
+                        (long long)s[i].kv_offset, (long long)(s[i].kv_offset + pages - 1),
+                        (long long)table_len);
+    }
+    return SGQA_OK;
+}
+
 // ---------------------------------------------------------------------------
 // launch policy
 // ---------------------------------------------------------------------------
@@ -301,11 +326,13 @@ int64_t fill_table(sgqa::SeqTable& tab, const sgqa_seq* s, int32_t first, int32_
 // the three steps (arguments already validated)
 // ---------------------------------------------------------------------------
 int run_compress(const sgqa_config* c, const sgqa_seq* s, int32_t n, const void* proxy_k,
-                 const float* logits, const void* ln_gamma, const void* ln_beta, void* store,
-                 hipStream_t st) {
+                 const float* logits, const Paging& pg, const void* ln_gamma, const void* ln_beta,
+                 void* store, hipStream_t st) {
     sgqa::CompressArgs a;
     a.proxy_k = (const uint16_t*)proxy_k;
     a.logits = logits;
+    a.page_table = pg.table;
+    a.n_pages = pg.n_pages;
     a.ln_gamma = (const uint16_t*)ln_gamma;
     a.ln_beta = (const uint16_t*)ln_beta;
     a.store = (uint16_t*)store;
@@ -406,12 +433,14 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
 }
 
 int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan& p,
-             const void* q, const void* k_cache, const void* v_cache, const int32_t* sel,
-             void* out, float* lse, void* ws, hipStream_t st) {
+             const void* q, const void* k_cache, const void* v_cache, const Paging& pg,
+             const int32_t* sel, void* out, float* lse, void* ws, hipStream_t st) {
     sgqa::AttnArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k_cache;
     a.v = (const uint16_t*)v_cache;
+    a.page_table = pg.table;
+    a.n_pages = pg.n_pages;
     a.sel = sel;
     a.out = (uint16_t*)out;
     a.lse = lse;
@@ -486,6 +515,24 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
     return SGQA_OK;
 }
 
+// steps 1 -> 2+3 -> 4 on one stream (arguments validated)
+int run_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs, const void* proxy_k,
+                const float* comp_logits, const void* ln_gamma, const void* ln_beta, void* store,
+                const void* q_idx, const float* w, const void* rms_gamma, int32_t* sel, float* sel_scores,
+                const void* q, const void* k_cache, const void* v_cache, const Paging& pg, void* out,
+                float* lse, void* ws, size_t ws_bytes, hipStream_t st) {
+    const IndexPlan ip = plan_index(cfg, seqs, n_seqs);
+    const AttnPlan ap = plan_attn(cfg, seqs, n_seqs);
+    int rc = check_ws(std::max(ip.ws, ap.ws), ws, ws_bytes);
+    if (rc) return rc;
+    if ((rc = run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, pg, ln_gamma, ln_beta, store, st)))
+        return rc;
+    if ((rc = run_index(cfg, seqs, n_seqs, ip, q_idx, w, rms_gamma, store, sel, sel_scores, nullptr, ws,
+                        st)))
+        return rc;
+    return run_attn(cfg, seqs, n_seqs, ap, q, k_cache, v_cache, pg, sel, out, lse, ws, st);
+}
+
 }  // namespace
 
 // ---------------------------------------------------------------------------
@@ -536,7 +583,27 @@ int sgqa_compress(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
     if (!proxy_k || !comp_logits || !store)
         return fail(SGQA_ERR_NULL, "proxy_k, comp_logits and store are required");
-    return run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store,
+    return run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, Paging(), ln_gamma, ln_beta, store,
+                        (hipStream_t)hip_stream);
+}
+
+int sgqa_compress_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                        const void* proxy_pages, const float* logit_pages, const int32_t* page_table,
+                        int64_t page_table_len, int64_t n_pages, const void* ln_gamma,
+                        const void* ln_beta, void* store, void* ws, size_t ws_bytes,
+                        void* hip_stream) {
+    (void)ws;
+    (void)ws_bytes;
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!proxy_pages || !logit_pages || !store)
+        return fail(SGQA_ERR_NULL, "proxy_pages, logit_pages and store are required");
+    if ((rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
+    Paging pg;
+    pg.table = page_table;
+    pg.n_pages = n_pages;
+    return run_compress(cfg, seqs, n_seqs, proxy_pages, logit_pages, pg, ln_gamma, ln_beta, store,
                         (hipStream_t)hip_stream);
 }
 
@@ -566,7 +633,27 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
         return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel and out are required");
     const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
-    return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, sel, out, lse, ws,
+    return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, ws,
+                    (hipStream_t)hip_stream);
+}
+
+int sgqa_sparse_attn_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                           const void* q, const void* k_pages, const void* v_pages,
+                           const int32_t* page_table, int64_t page_table_len, int64_t n_pages,
+                           const int32_t* sel, void* out, float* lse, void* ws, size_t ws_bytes,
+                           void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!q || !k_pages || !v_pages || !sel || !out)
+        return fail(SGQA_ERR_NULL, "q, k_pages, v_pages, sel and out are required");
+    if ((rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
+    const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
+    if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
+    Paging pg;
+    pg.table = page_table;
+    pg.n_pages = n_pages;
+    return run_attn(cfg, seqs, n_seqs, p, q, k_pages, v_pages, pg, sel, out, lse, ws,
                     (hipStream_t)hip_stream);
 }
 
@@ -584,16 +671,33 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
         return fail(SGQA_ERR_NULL,
                     "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache and out "
                     "are required");
-    const IndexPlan ip = plan_index(cfg, seqs, n_seqs);
-    const AttnPlan ap = plan_attn(cfg, seqs, n_seqs);
-    if ((rc = check_ws(std::max(ip.ws, ap.ws), ws, ws_bytes))) return rc;
-    hipStream_t st = (hipStream_t)hip_stream;
-    if ((rc = run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, st)))
-        return rc;
-    if ((rc = run_index(cfg, seqs, n_seqs, ip, q_idx, w, rms_gamma, store, sel, sel_scores,
-                        nullptr, ws, st)))
-        return rc;
-    return run_attn(cfg, seqs, n_seqs, ap, q, k_cache, v_cache, sel, out, lse, ws, st);
+    return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
+                       rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, ws, ws_bytes,
+                       (hipStream_t)hip_stream);
+}
+
+int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                       const void* proxy_pages, const float* logit_pages, const void* ln_gamma,
+                       const void* ln_beta, void* store, const void* q_idx, const float* w,
+                       const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
+                       const void* k_pages, const void* v_pages, const int32_t* page_table,
+                       int64_t page_table_len, int64_t n_pages, void* out, float* lse, void* ws,
+                       size_t ws_bytes, void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!proxy_pages || !logit_pages || !store || !q_idx || !w || !sel || !q || !k_pages ||
+        !v_pages || !out)
+        return fail(SGQA_ERR_NULL,
+                    "proxy_pages, logit_pages, store, q_idx, w, sel, q, k_pages, v_pages and out "
+                    "are required");
+    if ((rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
+    Paging pg;
+    pg.table = page_table;
+    pg.n_pages = n_pages;
+    return run_forward(cfg, seqs, n_seqs, proxy_pages, logit_pages, ln_gamma, ln_beta, store, q_idx, w,
+                       rms_gamma, sel, sel_scores, q, k_pages, v_pages, pg, out, lse, ws, ws_bytes,
+                       (hipStream_t)hip_stream);
 }
 
 }  // extern "C"

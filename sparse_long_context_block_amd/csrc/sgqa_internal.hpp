@@ -45,9 +45,17 @@ struct SeqTable {
 // ---------------------------------------------------------------------------
 // launch parameter blocks (host-chosen, passed by value)
 // ---------------------------------------------------------------------------
+// Paged caches (per-token tensors in pages of 16 positions): position pos of
+// a sequence lives in row page_table[kv_offset + pos / 16] * 16 + pos % 16 of
+// the page pool; the kv_offset of a sequence is the index of its first page
+// table entry.  page_table == nullptr: contiguous, row kv_offset + pos.
+constexpr int kPageTokens = 16;
+
 struct CompressArgs {
     const uint16_t* proxy_k;
     const float* logits;
+    const int32_t* page_table;  // paged proxy keys / logits, or null
+    int64_t n_pages;
     const uint16_t* ln_gamma;  // may be null
     const uint16_t* ln_beta;   // may be null
     uint16_t* store;
@@ -85,8 +93,10 @@ struct IndexArgs {
 
 struct AttnArgs {
     const uint16_t* q;
-    const uint16_t* k;
+    const uint16_t* k;          // cache, or page pool [n_pages, 16, G, D]
     const uint16_t* v;
+    const int32_t* page_table;  // paged K/V, or null
+    int64_t n_pages;
     const int32_t* sel;
     uint16_t* out;
     float* lse;            // may be null
@@ -196,6 +206,14 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// pool row of position pos through a sequence's page table pt (ids outside
+// [0, n_pages) are clamped, so a bad table never reads outside the pool)
+__device__ __forceinline__ int64_t paged_row(const int32_t* pt, int64_t n_pages, int64_t pos) {
+    int64_t p = pt[pos / kPageTokens];
+    p = p < 0 ? 0 : (p >= n_pages ? n_pages - 1 : p);
+    return p * kPageTokens + pos % kPageTokens;
+}
 
 __device__ __forceinline__ float bf16_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 

@@ -38,27 +38,34 @@ constexpr int kGVStride = kHeadDim + 8;             // bf16 per row of a wave's 
 constexpr int kWaveBufFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;
 static_assert(16 * kGVStride * 2 <= kWaveBufFloats * 4, "a wave's V tile fits its merge buffer");
 
-__device__ __forceinline__ int64_t token_at(int64_t i, int n_sel, int shift_b, int B,
-                                            const int32_t* sel, int64_t cur_first) {
+// Cache row of entry i of the query's token list.  Contiguous caches:
+// sel[j] holds selected block ids, rows are positions (cur0 = first position
+// of the current block).  Paged caches: sel[j] already holds the pool row of
+// block j's first position, cur0 the pool row of the current block's (a
+// block never straddles a 16-token page).
+__device__ __forceinline__ int64_t token_at(int64_t i, int n_sel, int shift_b, int B, bool paged,
+                                            const int32_t* sel, int64_t cur0) {
     const int64_t j = i >> shift_b;
-    if (j < n_sel) return (int64_t)sel[j] * B + (i & (B - 1));
-    return cur_first + (i - ((int64_t)n_sel << shift_b));
+    if (j < n_sel) return (paged ? (int64_t)sel[j] : (int64_t)sel[j] * B) + (i & (B - 1));
+    return cur0 + (i - ((int64_t)n_sel << shift_b));
 }
 
 // K/V rows of chunk c for this lane (token 16c + m; K dims 32kk + 8qq, V
-// dims 8(qq + 4j)); chunks past the token list read the current token, whose
-// values stay finite and are masked
+// dims 8(qq + 4j)); chunks past the token list read the current token (row
+// t_row), whose values stay finite and are masked.  Rows are clamped to
+// [0, row_max], so malformed ids never read outside the cache or pool.
 struct GatherRegs {
     uint4 k[6], v[6];
 };
 
 __device__ __forceinline__ GatherRegs gather_chunk(int64_t c, int m, int qq, int64_t n_tok, int n_sel, int shift_b,
-                                                   int B, const int32_t* sel_lds, int64_t cur_first, int64_t t,
-                                                   const uint16_t* kbase, const uint16_t* vbase) {
+                                                   int B, bool paged, const int32_t* sel_lds, int64_t cur0,
+                                                   int64_t t_row, int64_t row_max, const uint16_t* kbase,
+                                                   const uint16_t* vbase) {
     constexpr int64_t kRowStride = (int64_t)kGroups * kHeadDim;
     const int64_t ti = 16 * c + m;
-    int64_t tok = ti < n_tok ? token_at(ti, n_sel, shift_b, B, sel_lds, cur_first) : t;
-    tok = tok < 0 ? 0 : (tok > t ? t : tok);   // malformed ids never read past the cache
+    int64_t tok = ti < n_tok ? token_at(ti, n_sel, shift_b, B, paged, sel_lds, cur0) : t_row;
+    tok = tok < 0 ? 0 : (tok > row_max ? row_max : tok);
     const uint16_t* krow = kbase + tok * kRowStride + 8 * qq;
     const uint16_t* vrow = vbase + tok * kRowStride;
     GatherRegs r;
@@ -138,6 +145,7 @@ __device__ __forceinline__ void gather_step(GatherState& st, const GatherRegs& r
     wave_lds_sync();
 }
 
+template <bool PAGED>
 __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArgs a) {
     extern __shared__ int32_t sel_lds[];                        // [K]
     __shared__ float wave_buf[4][kWaveBufFloats];
@@ -171,6 +179,23 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
     }
     __syncthreads();
     const int n_sel = s_nsel;
+    // rows: positions of the contiguous cache, or pool rows through the
+    // sequence's page table (the selection list becomes pool rows; block ids
+    // outside [0, floor(t/B)] are clamped first, so the table is read only
+    // inside the sequence's pages)
+    int64_t cur0 = cur_first, t_row = t, row_max = t;
+    if (PAGED) {
+        const int32_t* pt = a.page_table + sq.kv_offset;
+        const int64_t b_max = t / B;
+        for (int j = threadIdx.x; j < n_sel; j += 256) {
+            const int64_t r = sel_lds[j] > b_max ? b_max : sel_lds[j];
+            sel_lds[j] = (int32_t)paged_row(pt, a.n_pages, r * B);
+        }
+        cur0 = paged_row(pt, a.n_pages, cur_first);
+        t_row = cur0 + (t - cur_first);
+        row_max = a.n_pages * kPageTokens - 1;
+        __syncthreads();
+    }
     const int64_t n_tok = ((int64_t)n_sel << shift_b) + (t - cur_first + 1);
     const int64_t n_chunks = (n_tok + 15) >> 4;
     const int64_t c_lo = (int64_t)split * a.chunks_per_split;
@@ -199,19 +224,21 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
     gl.qq = qq;
     gl.n_tok = n_tok;
     gl.sl2 = a.scale_log2;
-    const uint16_t* kbase = a.k + (sq.kv_offset * kGroups + g) * kHeadDim;
-    const uint16_t* vbase = a.v + (sq.kv_offset * kGroups + g) * kHeadDim;
+    const int64_t row0 = PAGED ? 0 : sq.kv_offset;
+    const uint16_t* kbase = a.k + (row0 * kGroups + g) * kHeadDim;
+    const uint16_t* vbase = a.v + (row0 * kGroups + g) * kHeadDim;
 
     // two register sets alternate: one chunk's rows are in flight while the
     // other chunk is processed
     if (c_lo + w < c_hi) {
-        GatherRegs ra = gather_chunk(c_lo + w, m, qq, n_tok, n_sel, shift_b, B, sel_lds, cur_first, t, kbase, vbase);
+        GatherRegs ra = gather_chunk(c_lo + w, m, qq, n_tok, n_sel, shift_b, B, PAGED, sel_lds, cur0, t_row, row_max, kbase,
+                                     vbase);
         for (int64_t c = c_lo + w; c < c_hi; c += 8) {
             const GatherRegs rb =
-                gather_chunk(c + 4, m, qq, n_tok, n_sel, shift_b, B, sel_lds, cur_first, t, kbase, vbase);
+                gather_chunk(c + 4, m, qq, n_tok, n_sel, shift_b, B, PAGED, sel_lds, cur0, t_row, row_max, kbase, vbase);
             gather_step(st, ra, qf, c, gl);
             if (c + 4 >= c_hi) break;
-            ra = gather_chunk(c + 8, m, qq, n_tok, n_sel, shift_b, B, sel_lds, cur_first, t, kbase, vbase);
+            ra = gather_chunk(c + 8, m, qq, n_tok, n_sel, shift_b, B, PAGED, sel_lds, cur0, t_row, row_max, kbase, vbase);
             gather_step(st, rb, qf, c + 4, gl);
         }
     }
@@ -312,16 +339,23 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(SeqTable seqs, AttnMerg
 
 }  // namespace
 
-hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
-                              hipStream_t stream) {
-    if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
+template <bool PAGED>
+static hipError_t launch_sparse_attn_t(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
+                                       hipStream_t stream) {
     const size_t lds = (size_t)a.topk * sizeof(int32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel,
+    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<PAGED>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(max_nq * kGroups * a.n_split), (unsigned)seqs.n);
-    hipLaunchKernelGGL(sparse_attn_kernel, grid, dim3(256), lds, stream, seqs, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<PAGED>), grid, dim3(256), lds, stream, seqs, a);
     return hipGetLastError();
+}
+
+hipError_t launch_sparse_attn(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
+                              hipStream_t stream) {
+    if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
+    return a.page_table ? launch_sparse_attn_t<true>(seqs, max_nq, a, stream)
+                        : launch_sparse_attn_t<false>(seqs, max_nq, a, stream);
 }
 
 hipError_t launch_attn_merge(const SeqTable& seqs, int64_t max_nq, const AttnMergeArgs& a,

@@ -197,6 +197,31 @@ def test_workspace_ignores_query_row_offsets(L):
     assert sg.workspace_size(cfg, spread, sg.OP_INDEX_TOPK) == 64 * 4 * 25024 * 4
 
 
+def test_paged_calls_validate_the_page_table(L):
+    # kv_offset indexes the sequence's first page-table entry; its
+    # ceil(kv_capacity / 16) entries must lie inside the table
+    cfg = sg.config()
+    P = ctypes.c_void_p(FAKE)
+    s = sg.seq(100, pos0=900, kv_offset=10, kv_capacity=1000)   # 63 pages: entries 10..72
+    arr, n = _seqs(s)
+    attn = lambda pt, ln, npg: L.sgqa_sparse_attn_paged(ctypes.byref(cfg), arr, n, P, P, P, pt, ln,
+                                                        npg, P, P, None, None, 0, None)
+    assert attn(None, 73, 8) == E_NULL
+    assert attn(P, 72, 8) == E_CAPACITY
+    assert "page-table entries 10 .. 72" in L.sgqa_last_error().decode()
+    assert attn(P, 73, 0) == E_SHAPE
+    assert attn(P, 0, 8) == E_SHAPE
+    assert attn(P, 73, (1 << 27) + 1) == E_SHAPE
+    comp = lambda pt, ln: L.sgqa_compress_paged(ctypes.byref(cfg), arr, n, P, P, pt, ln, 8, None, None,
+                                                P, None, 0, None)
+    assert comp(None, 73) == E_NULL
+    assert comp(P, 72) == E_CAPACITY
+    args = [ctypes.byref(cfg), arr, n] + [P] * 13 + [P, 72, 8, P, None, None, 0, None]
+    assert L.sgqa_forward_paged(*args) == E_CAPACITY
+    args[16] = None
+    assert L.sgqa_forward_paged(*args) == E_NULL
+
+
 def test_binding_rejects_wrong_tensors():
     import torch
     cfg = sg.config()
