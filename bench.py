@@ -203,6 +203,8 @@ def main() -> int:
     ap.add_argument("--kernel-reps", type=int, default=20)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one 512 MiB device-to-device copy (HBM byte-counter scale)")
+    ap.add_argument("--paged", action="store_true",
+                    help="per-token caches as pools of 16-token pages behind a random page table")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); "
@@ -216,14 +218,28 @@ def main() -> int:
     from tests.gpu_checks import lib_seq, lib_seqs, prepare
 
     wl = W.make(args.workload)
+    if args.paged and wl.loop_steps:
+        print("bench.py --paged takes workloads of one call", file=sys.stderr)
+        return 2
     print(f"[bench] workload {wl.name}: preparing inputs", file=sys.stderr, flush=True)
     di, cfg = prepare(wl)
+    pools = table = None
+    if args.paged:
+        # the same logical contents in page pools; the contiguous copies go
+        pools, table, layouts = W.paginate(wl, di, np.random.default_rng(0))
+        for name in ("k", "v", "proxy_k", "logits"):
+            di.t[name] = None
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
     # a loop of calls (a decode loop: one token per sequence per call; a
     # chained prefill: one chunk per call) runs call k at step k, wrapping
     # around; repeating a call recomputes the same outputs
     if wl.loop_steps:
         loop = [[lib_seq(s) for s in wl.step_seqs(k)] for k in range(wl.loop_steps)]
         ws_n = max(sg.workspace_size(cfg, sq, sg.OP_FORWARD) for sq in loop)
+    elif args.paged:
+        loop = [[lib_seq(s) for s in layouts]]
+        ws_n = sg.workspace_size(cfg, loop[0], sg.OP_FORWARD)
     else:
         loop = [lib_seqs(wl)]
         ws_n = sg.workspace_size(cfg, loop[0], sg.OP_FORWARD)
@@ -235,11 +251,20 @@ def main() -> int:
     def step():
         sq = loop[step_no[0] % len(loop)]
         step_no[0] += 1
+        if pools is not None:
+            sg.forward_paged(cfg, sq, pools["proxy_k"], pools["logits"], di["store"], di["q_idx"],
+                             di["w"], di["sel"], di["q"], pools["k"], pools["v"], table, di["out"],
+                             lse=di["lse"], ws=ws_view, stream=stream)
+            return
         sg.forward(cfg, sq, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
                    di["sel"], di["q"], di["k"], di["v"], di["out"], lse=di["lse"],
                    ws=ws_view, stream=stream)
 
     def op_compress():
+        if pools is not None:
+            sg.compress_paged(cfg, seqs, pools["proxy_k"], pools["logits"], table, di["store"],
+                              stream=stream)
+            return
         sg.compress(cfg, seqs, di["proxy_k"], di["logits"], di["store"], stream=stream)
 
     def op_index():
@@ -247,6 +272,10 @@ def main() -> int:
                       ws=ws_view, stream=stream)
 
     def op_attn():
+        if pools is not None:
+            sg.sparse_attn_paged(cfg, seqs, di["q"], pools["k"], pools["v"], table, di["sel"],
+                                 di["out"], lse=di["lse"], ws=ws_view, stream=stream)
+            return
         sg.sparse_attn(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"],
                        lse=di["lse"], ws=ws_view, stream=stream)
 
@@ -310,7 +339,7 @@ def main() -> int:
         kern = (f"attn_union_kernel<{wl.block_size.bit_length() - 1}>" if dense == wm["queries"]
                 else f"attn_union_kernel<{wl.block_size.bit_length() - 1}> + sparse_attn_kernel "
                      f"({dense} of {wm['queries']} queries tiled)")
-        traffic = recorded_traffic(wl.name) if dense == wm["queries"] else None
+        traffic = recorded_traffic(wl.name) if dense == wm["queries"] and not args.paged else None
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16_FLOPS / 1e12), "traffic": traffic,
                 "kernel": kern,
@@ -327,7 +356,8 @@ def main() -> int:
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name, "queries": wm["queries"], "block_size": wl.block_size,
+        "config": {"workload": wl.name + ("+paged" if args.paged else ""), "queries": wm["queries"],
+                   "block_size": wl.block_size,
                    "topk_blocks": wl.topk, "store_q8": wl.store_q8,
                    "heads": H, "kv_groups": G, "head_dim": D},
         "per_op_ms": k_ms,

@@ -108,7 +108,8 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t tile_rsrc(const uint16_t* base
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t page_rsrc(const uint16_t* pool, const UnionCtx& u, int64_t p0) {
     const int64_t rows = u.t_last - p0 + 1;
     if (rows <= 0) return __builtin_amdgcn_make_buffer_rsrc((void*)pool, (short)0, 0, 0x00020000);
-    int64_t pid = u.pt[p0 / kPageTokens];
+    // p0 is wave-uniform: one scalar load, and the resource stays in SGPRs
+    int64_t pid = __builtin_amdgcn_readfirstlane(u.pt[p0 / kPageTokens]);
     pid = pid < 0 ? 0 : (pid >= u.n_pages ? u.n_pages - 1 : pid);
     const int nrec = rows >= kPageTokens ? kPageTokens * kRowBytes : (int)(rows - 1) * kRowBytes + kHeadDim * 2;
     return __builtin_amdgcn_make_buffer_rsrc((void*)(pool + pid * kPageTokens * kRowElems), (short)0, nrec,
@@ -121,7 +122,7 @@ __device__ __forceinline__ void gload(const UnionCtx& u, int tile, KVStage& r) {
     if (PAGED) {
         constexpr uint32_t kHalf = kPageTokens * kRowBytes;
         if (u.vwave) {
-            const bool hi = u.o >= 2;                // wave-uniform: V wavefronts 3..5
+            const bool hi = __builtin_amdgcn_readfirstlane(u.o) >= 2;   // V wavefronts 3..5
             const __amdgpu_buffer_rsrc_t vr = page_rsrc(u.vb, u, tile0 + (hi ? kPageTokens : 0));
             const __amdgpu_buffer_rsrc_t kr = page_rsrc(u.kb, u, tile0);
             const uint32_t vo = u.voff - (hi ? kHalf : 0u);

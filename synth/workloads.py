@@ -282,3 +282,41 @@ def host_proxy(wl: Workload, kv_rows) -> np.ndarray:
 
 def host_logits(wl: Workload, kv_rows) -> np.ndarray:
     return normal_f32(wl.seed, TID_LOGITS, _flat(kv_rows, DI)).reshape(-1, DI)
+
+
+# ---------------------------------------------------------------------------
+# paged layout of the per-token tensors
+# ---------------------------------------------------------------------------
+PAGE_TOKENS = 16
+
+
+def paginate(wl: Workload, di, rng):
+    """The per-token tensors of ``di`` (K, V, proxy keys, logits) scattered
+    into pools of 16-position pages through a random page table with seven
+    spare pages; every pool slot that holds no position below a sequence's
+    capacity is NaN.  Returns (pools by name, int32 page table on the device,
+    per-sequence layouts whose kv_offset is the first page-table entry)."""
+    import torch
+    P = PAGE_TOKENS
+    n_log = [(s.kv_capacity + P - 1) // P for s in wl.seqs]
+    total = sum(n_log)
+    n_pages = total + 7
+    phys = rng.permutation(n_pages)[:total]
+    table = np.zeros(total + 3, dtype=np.int32)          # trailing entries unused
+    pools = {}
+    for name in ("k", "v", "proxy_k", "logits"):
+        t = di[name]
+        pools[name] = torch.full((n_pages, P) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype,
+                                 device=t.device)
+    seqs, off = [], 0
+    for s, n in zip(wl.seqs, n_log):
+        ids = phys[off:off + n]
+        table[off:off + n] = ids
+        pos = torch.arange(s.kv_capacity, device=di["k"].device)
+        prow = torch.as_tensor(ids, device=pos.device).long()[pos // P]
+        for name in pools:
+            pools[name][prow, pos % P] = di[name][s.kv_offset:s.kv_offset + s.kv_capacity]
+        seqs.append(SeqLayout(s.q_offset, s.n_q, s.pos0, off, s.kv_capacity, s.store_offset,
+                              s.store_capacity))
+        off += n
+    return pools, torch.as_tensor(table, device=di["k"].device), seqs

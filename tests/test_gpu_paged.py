@@ -17,39 +17,9 @@ import torch
 import sparse_long_context_block_amd as sg
 from synth import workloads as W
 
-from .gpu_checks import Checker, lib_seqs, log, prepare, stratified_rows
+from .gpu_checks import Checker, lib_seq, lib_seqs, log, prepare, stratified_rows
 
 pytestmark = pytest.mark.gpu
-
-PAGE = 16
-
-
-def _paginate(wl, di, rng):
-    """Pools and page table holding the same logical rows as di's caches."""
-    n_log = [(s.kv_capacity + PAGE - 1) // PAGE for s in wl.seqs]
-    total = sum(n_log)
-    n_pages = total + 7                                  # spare pages, never referenced
-    phys = rng.permutation(n_pages)[:total]
-    table = np.zeros(total + 3, dtype=np.int32)          # trailing entries unused
-    pools = {}
-    for name, t in (("k", di["k"]), ("v", di["v"]), ("proxy_k", di["proxy_k"]), ("logits", di["logits"])):
-        pools[name] = torch.full((n_pages, PAGE) + tuple(t.shape[1:]), float("nan"), dtype=t.dtype,
-                                 device=t.device)
-    seqs, off = [], 0
-    for s, n in zip(wl.seqs, n_log):
-        ids = phys[off:off + n]
-        table[off:off + n] = ids
-        pos = torch.arange(s.kv_capacity, device="cuda")
-        prow = torch.as_tensor(ids, device="cuda").long()[pos // PAGE]
-        for name in pools:
-            src = di[name][s.kv_offset:s.kv_offset + s.kv_capacity]
-            pools[name][prow, pos % PAGE] = src
-        seqs.append(sg.Seq(q_offset=s.q_offset, n_q=s.n_q, pos0=s.pos0, cache_len=s.cache_len,
-                           kv_offset=off, kv_capacity=s.kv_capacity, store_offset=s.store_offset,
-                           store_capacity=s.store_capacity))
-        off += n
-    return pools, torch.as_tensor(table, device="cuda"), seqs
-
 
 @pytest.mark.parametrize("name", ["chunk_1003_997_b8_k64", "decode_small", "prefill_2000_b1_k64",
                                   "prefill_1003_b16_k8"])
@@ -63,7 +33,8 @@ def test_paged_forward_matches_contiguous(name):
     torch.cuda.synchronize()
     ref = {k: di[k].clone() for k in ("store", "sel", "sel_scores", "out", "lse")}
 
-    pools, table, pseqs = _paginate(wl, di, np.random.default_rng(3))
+    pools, table, players = W.paginate(wl, di, np.random.default_rng(3))
+    pseqs = [lib_seq(p) for p in players]
     # the history's store rows through the paged merge too
     pre = [sg.Seq(q_offset=0, n_q=s.pos0, pos0=0, cache_len=s.pos0, kv_offset=p.kv_offset,
                   kv_capacity=s.kv_capacity, store_offset=s.store_offset, store_capacity=s.store_capacity)
