@@ -42,6 +42,12 @@ Readings where the pages are silent (each listed in the design notes):
 * Selection emitted in ascending block ID, padded with -1; "equal" is IEEE
   equality (-0 == +0).
 * A token in block 0 (t < B) has no historical candidates.
+* Neighbours of the path: the main Q/K RMSNorm is per head over D with one
+  gamma shared by the heads, epsilon eps_rms; the main rotary span uses the
+  indexer's convention (half-split pairs, base**(-2j/span)) with span and
+  base as parameters; the gate is elementwise over the head vector with
+  caller-supplied logits.  Parity unpinned against the real model (span,
+  gate shape); the norm, rotation and sigmoid are pinned.
 
 Conventions: bf16 tensors arrive as uint16 bit arrays, fp32 tensors as
 float32 arrays; everything is widened exactly to float64 and computed in
@@ -230,6 +236,34 @@ def attend(q: np.ndarray, k: np.ndarray, v: np.ndarray, scale: float):
     l = e.sum(axis=1, keepdims=True)
     o = (e @ v) / l
     return o, (m + np.log(l))[:, 0]
+
+
+# --------------------------------------------------------------------------
+# the path's neighbours.  P1 "Two paths leave the same hidden state": the
+# main path normalizes Q and K and applies the layer's partial RoPE (its
+# span is head_dim times a partial-rotary factor the pages do not give, so
+# it is a parameter).  P1 "Main attention still reads original K/V": each
+# head's output vector is sigmoid-gated before concatenation and the output
+# projection.
+# --------------------------------------------------------------------------
+
+def main_qk(x_bits: np.ndarray, positions: np.ndarray, rope_dim: int, rope_base: float,
+            eps: float, gamma_bits=None) -> np.ndarray:
+    """Main-path Q (or K) rows: x [n, heads, D] bf16 bits at token positions
+    [n]; RMSNorm over each head's D dims (one gamma [D] shared by the heads),
+    then the rotary span [0, rope_dim) at the token's position.  Exact
+    (float64, not rounded)."""
+    x = bf16_bits_to_f64(x_bits)
+    g = bf16_bits_to_f64(gamma_bits) if gamma_bits is not None else None
+    y = rms_norm(x, eps, g)
+    pos = np.broadcast_to(np.asarray(positions, dtype=np.float64)[:, None], y.shape[:2])
+    return rope(y, pos, rope_dim, rope_base)
+
+
+def gate(o: np.ndarray, gate_bits: np.ndarray) -> np.ndarray:
+    """A head's output vector times sigmoid of its gate logits, elementwise."""
+    g = bf16_bits_to_f64(gate_bits)
+    return o / (1.0 + np.exp(-g))
 
 
 # --------------------------------------------------------------------------

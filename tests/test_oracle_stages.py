@@ -427,3 +427,55 @@ def test_page_counts():
     assert store == pc["summary_store_mib"]["value"] * 2 ** 20
     total = (2 * (global_kv + local_kv) + 8 * store) / 2 ** 30
     assert round(total, 6) == pc["payload_tp8_gib"]["value"]
+
+
+# ---------------------------------------------------------------------------
+# the path's neighbours: main Q/K norm + partial rotary span, sigmoid gate
+# ---------------------------------------------------------------------------
+
+def test_main_qk_is_library_rms_norm_then_rotation():
+    rng = np.random.default_rng(21)
+    x = rng.standard_normal((5, 7, 192)).astype(np.float32)
+    xb = _bf16_bits(x)
+    gam = _bf16_bits(rng.uniform(0.5, 1.5, 192))
+    pos = np.array([0, 3, 100, 4095, 262143])
+    xf = torch.from_numpy(nu.bf16_bits_to_f64(xb))
+    gf = torch.from_numpy(nu.bf16_bits_to_f64(gam))
+    normed = F.rms_norm(xf, (192,), weight=gf, eps=1e-6).numpy()
+    # span 0: the library norm alone
+    assert np.allclose(O.main_qk(xb, pos, 0, 10000.0, 1e-6, gam), normed, rtol=1e-13, atol=1e-13)
+    for span, base in [(64, 10000.0), (96, 1e6), (192, 500.0)]:
+        out = O.main_qk(xb, pos, span, base, 1e-6, gam)
+        ref = _rope_complex(normed, np.broadcast_to(pos[:, None], normed.shape[:2]), span, base)
+        # the two frequency formulas differ by an ulp of theta: a phase error
+        # of about pos * 2.2e-16 (6e-11 rad at position 262143)
+        assert np.allclose(out, ref, rtol=0, atol=1e-9)
+        assert np.array_equal(out[..., span:], normed[..., span:])       # dims past the span pass through
+        assert np.allclose(np.linalg.norm(out[..., :span], axis=-1),
+                           np.linalg.norm(normed[..., :span], axis=-1), rtol=1e-12)
+
+
+def test_main_qk_scores_depend_on_relative_position():
+    rng = np.random.default_rng(22)
+    q = _bf16_bits(rng.standard_normal((1, 1, 192)))
+    k = _bf16_bits(rng.standard_normal((1, 1, 192)))
+    span = 64
+    dots = []
+    for t, s in [(10, 3), (1007, 1000), (65543, 65536)]:
+        qa = O.main_qk(q, np.array([t]), span, 10000.0, 1e-6)
+        ka = O.main_qk(k, np.array([s]), span, 10000.0, 1e-6)
+        dots.append(float((qa[0, 0, :span] * ka[0, 0, :span]).sum()))
+    assert np.allclose(dots, dots[0], rtol=1e-9, atol=1e-9)
+
+
+def test_gate_is_library_sigmoid_and_exact_at_zero():
+    rng = np.random.default_rng(23)
+    o = rng.standard_normal((3, 16, 192))
+    g = _bf16_bits(rng.standard_normal((3, 16, 192)) * 4)
+    ref = o * torch.sigmoid(torch.from_numpy(nu.bf16_bits_to_f64(g))).numpy()
+    assert np.allclose(O.gate(o, g), ref, rtol=1e-13, atol=1e-15)
+    zero = np.zeros((3, 16, 192), dtype=np.uint16)
+    assert np.array_equal(O.gate(o, zero), o / 2)                        # sigmoid(0) = 1/2 exactly
+    big = _bf16_bits(np.full((3, 16, 192), 64.0))
+    assert np.allclose(O.gate(o, big), o, rtol=1e-27)
+    assert np.allclose(O.gate(o, _bf16_bits(np.full((3, 16, 192), -64.0))), 0.0, atol=1e-27)
