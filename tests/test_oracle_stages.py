@@ -443,14 +443,15 @@ def test_main_qk_is_library_rms_norm_then_rotation():
     gf = torch.from_numpy(nu.bf16_bits_to_f64(gam))
     normed = F.rms_norm(xf, (192,), weight=gf, eps=1e-6).numpy()
     # span 0: the library norm alone
-    assert np.allclose(O.main_qk(xb, pos, 0, 10000.0, 1e-6, gam), normed, rtol=1e-13, atol=1e-13)
+    plain = O.main_qk(xb, pos, 0, 10000.0, 1e-6, gam)
+    assert np.allclose(plain, normed, rtol=1e-13, atol=1e-13)
     for span, base in [(64, 10000.0), (96, 1e6), (192, 500.0)]:
         out = O.main_qk(xb, pos, span, base, 1e-6, gam)
         ref = _rope_complex(normed, np.broadcast_to(pos[:, None], normed.shape[:2]), span, base)
         # the two frequency formulas differ by an ulp of theta: a phase error
         # of about pos * 2.2e-16 (6e-11 rad at position 262143)
         assert np.allclose(out, ref, rtol=0, atol=1e-9)
-        assert np.array_equal(out[..., span:], normed[..., span:])       # dims past the span pass through
+        assert np.array_equal(out[..., span:], plain[..., span:])        # dims past the span pass through
         assert np.allclose(np.linalg.norm(out[..., :span], axis=-1),
                            np.linalg.norm(normed[..., :span], axis=-1), rtol=1e-12)
 
