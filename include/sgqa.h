@@ -256,16 +256,70 @@ int sgqa_compress_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_
 int sgqa_sparse_attn_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                            const void* q, const void* k_pages, const void* v_pages,
                            const int32_t* page_table, int64_t page_table_len, int64_t n_pages,
-                           const int32_t* sel, void* out, float* lse, void* ws, size_t ws_bytes,
-                           void* hip_stream);
+                           const int32_t* sel, void* out, float* lse, const void* gate, void* ws,
+                           size_t ws_bytes, void* hip_stream);
 
 int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                        const void* proxy_pages, const float* logit_pages, const void* ln_gamma,
                        const void* ln_beta, void* store, const void* q_idx, const float* w,
                        const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
                        const void* k_pages, const void* v_pages, const int32_t* page_table,
-                       int64_t page_table_len, int64_t n_pages, void* out, float* lse, void* ws,
-                       size_t ws_bytes, void* hip_stream);
+                       int64_t page_table_len, int64_t n_pages, void* out, float* lse,
+                       const void* gate, void* ws, size_t ws_bytes, void* hip_stream);
+
+/*
+ * The neighbours of the path, fused into it (page sections "Two paths leave
+ * the same hidden state" and "Main attention still reads original K/V").
+ *
+ * Output gate: each head's output vector is sigmoid-gated before the heads
+ * are concatenated; here elementwise,
+ *   out[t,h,d] = bf16( o[t,h,d] * 1 / (1 + exp(-gate[t,h,d])) )
+ * with o the attention result of sgqa_sparse_attn in fp32 and gate bf16
+ * [Nq, H, D] logits from the caller (the projection needs trained weights),
+ * applied in the attention kernels before rounding; lse is the attention's,
+ * unchanged.  The _paged entry points above take the same gate (NULL: no
+ * gate).  Everything else as sgqa_sparse_attn / sgqa_forward.
+ */
+int sgqa_sparse_attn_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                           const void* q, const void* k_cache, const void* v_cache, const int32_t* sel,
+                           void* out, float* lse, const void* gate, void* ws, size_t ws_bytes,
+                           void* hip_stream);
+
+int sgqa_forward_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                       const void* proxy_k, const float* comp_logits, const void* ln_gamma,
+                       const void* ln_beta, void* store, const void* q_idx, const float* w,
+                       const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
+                       const void* k_cache, const void* v_cache, void* out, float* lse, const void* gate,
+                       void* ws, size_t ws_bytes, void* hip_stream);
+
+/* Main-path Q/K producer parameters (sgqa_qk_prep). */
+typedef struct {
+    int32_t rope_dim;   /* rotary span of the main Q/K: even, 0 .. head_dim       */
+    float rope_base;    /* finite, > 0                                            */
+    float eps;          /* RMSNorm epsilon, finite, >= 0                          */
+    int32_t reserved;   /* 0                                                      */
+} sgqa_qk_config;
+
+/*
+ * Main-path Q/K producer: the main path normalizes Q and K and applies the
+ * layer's partial rotary span (its width is head_dim times a partial-rotary
+ * factor the page names but does not give: rope_dim and rope_base are the
+ * caller's).  For every new token t of each sequence (rows as in the calls
+ * above: q rows at q_offset, cache rows at kv_offset + t, or through
+ * page_table when it is not NULL, with the paged checks above):
+ *   q_out[t, h]   = bf16(RoPE_t(RMSNorm(q_raw[t, h]) * q_gamma))    h < H
+ *   k_cache[t, g] = bf16(RoPE_t(RMSNorm(k_raw[t, g]) * k_gamma))    g < G
+ *   v_cache[t, g] = v_raw[t, g]               (when v_raw is not NULL)
+ * RMSNorm over each head's D dims with one gamma [D] per tensor (NULL: 1),
+ * epsilon qk->eps, fp32; RoPE_t rotates pairs (j, j + rope_dim/2) of dims
+ * [0, rope_dim) by t * rope_base^(-2j/rope_dim) (the indexer's convention).
+ * q_raw bf16 [Nq, H, D], k_raw / v_raw bf16 [Nq, G, D], q_out bf16 [Nq, H, D].
+ * v_raw and v_cache are both NULL or both set.  No workspace.
+ */
+int sgqa_qk_prep(const sgqa_config* cfg, const sgqa_qk_config* qk, const sgqa_seq* seqs, int32_t n_seqs,
+                 const void* q_raw, const void* k_raw, const void* v_raw, const void* q_gamma,
+                 const void* k_gamma, void* q_out, void* k_cache, void* v_cache, const int32_t* page_table,
+                 int64_t page_table_len, int64_t n_pages, void* hip_stream);
 
 /* Static name of a status code. */
 const char* sgqa_status_string(int status);

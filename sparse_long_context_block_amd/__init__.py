@@ -29,6 +29,7 @@ import torch
 __all__ = [
     "Config", "Seq", "SgqaError", "config", "seq", "lib", "workspace_size", "compress",
     "index_topk", "sparse_attn", "forward", "compress_paged", "sparse_attn_paged", "forward_paged",
+    "QkConfig", "qk_config", "qk_prep", "sparse_attn_gated", "forward_gated",
     "LIB_PATH", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_SPARSE_ATTN", "OP_FORWARD",
 ]
 
@@ -86,6 +87,21 @@ def config(block_size: int = 8, topk_blocks: int = 512, store_q8: bool = True, *
     return c
 
 
+class QkConfig(ctypes.Structure):
+    _fields_ = [
+        ("rope_dim", ctypes.c_int32),
+        ("rope_base", ctypes.c_float),
+        ("eps", ctypes.c_float),
+        ("reserved", ctypes.c_int32),
+    ]
+
+
+def qk_config(rope_dim: int = 64, rope_base: float = 10000.0, eps: float = 1e-6) -> QkConfig:
+    """Main-path Q/K producer parameters (the rotary span is a parameter: the
+    page names the layer's partial-rotary factor without giving it)."""
+    return QkConfig(rope_dim=rope_dim, rope_base=rope_base, eps=eps, reserved=0)
+
+
 def seq(n_q: int, pos0: int = 0, q_offset: int = 0, kv_offset: int = 0,
         kv_capacity: Optional[int] = None, store_offset: int = 0,
         store_capacity: Optional[int] = None, block_size: int = 8) -> Seq:
@@ -131,11 +147,19 @@ def lib() -> ctypes.CDLL:
     I64 = ctypes.c_int64
     L.sgqa_compress_paged.argtypes = [cfgp, seqp, I32, P, P, P, I64, I64, P, P, P, P, SZ, P]
     L.sgqa_compress_paged.restype = ctypes.c_int
-    L.sgqa_sparse_attn_paged.argtypes = [cfgp, seqp, I32, P, P, P, P, I64, I64, P, P, P, P, SZ, P]
+    L.sgqa_sparse_attn_paged.argtypes = [cfgp, seqp, I32, P, P, P, P, I64, I64, P, P, P, P, P, SZ, P]
     L.sgqa_sparse_attn_paged.restype = ctypes.c_int
     L.sgqa_forward_paged.argtypes = [cfgp, seqp, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
-                                     I64, I64, P, P, P, SZ, P]
+                                     I64, I64, P, P, P, P, SZ, P]
     L.sgqa_forward_paged.restype = ctypes.c_int
+    L.sgqa_sparse_attn_gated.argtypes = [cfgp, seqp, I32, P, P, P, P, P, P, P, P, SZ, P]
+    L.sgqa_sparse_attn_gated.restype = ctypes.c_int
+    L.sgqa_forward_gated.argtypes = [cfgp, seqp, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                     P, P, SZ, P]
+    L.sgqa_forward_gated.restype = ctypes.c_int
+    L.sgqa_qk_prep.argtypes = [cfgp, ctypes.POINTER(QkConfig), seqp, I32, P, P, P, P, P, P, P, P, P,
+                               I64, I64, P]
+    L.sgqa_qk_prep.restype = ctypes.c_int
     L.sgqa_status_string.argtypes = [ctypes.c_int]
     L.sgqa_status_string.restype = ctypes.c_char_p
     L.sgqa_last_error.argtypes = []
@@ -275,7 +299,7 @@ def compress_paged(cfg: Config, seqs: Sequence[Seq], proxy_pages, logit_pages, p
 
 
 def sparse_attn_paged(cfg: Config, seqs: Sequence[Seq], q, k_pages, v_pages, page_table, sel, out,
-                      lse=None, ws=None, stream=None) -> None:
+                      lse=None, gate=None, ws=None, stream=None) -> None:
     arr, n = _seq_array(seqs)
     wsp, wsn, _own = _workspace(cfg, seqs, OP_SPARSE_ATTN, q.device, ws, stream)
     ptp, ptn, npg = _pages(page_table, k_pages)
@@ -283,12 +307,13 @@ def sparse_attn_paged(cfg: Config, seqs: Sequence[Seq], q, k_pages, v_pages, pag
         ctypes.byref(cfg), arr, n, _ptr(q, torch.bfloat16, "q"),
         _ptr(k_pages, torch.bfloat16, "k_pages"), _ptr(v_pages, torch.bfloat16, "v_pages"),
         ptp, ptn, npg, _ptr(sel, torch.int32, "sel"), _ptr(out, torch.bfloat16, "out"),
-        _ptr(lse, torch.float32, "lse", False), wsp, wsn, _stream_ptr(stream)))
+        _ptr(lse, torch.float32, "lse", False), _ptr(gate, torch.bfloat16, "gate", False), wsp, wsn,
+        _stream_ptr(stream)))
 
 
 def forward_paged(cfg: Config, seqs: Sequence[Seq], proxy_pages, logit_pages, store, q_idx, w, sel,
                   q, k_pages, v_pages, page_table, out, lse=None, sel_scores=None, ln_gamma=None,
-                  ln_beta=None, rms_gamma=None, ws=None, stream=None) -> None:
+                  ln_beta=None, rms_gamma=None, gate=None, ws=None, stream=None) -> None:
     arr, n = _seq_array(seqs)
     wsp, wsn, _own = _workspace(cfg, seqs, OP_FORWARD, q.device, ws, stream)
     ptp, ptn, npg = _pages(page_table, k_pages)
@@ -302,4 +327,54 @@ def forward_paged(cfg: Config, seqs: Sequence[Seq], proxy_pages, logit_pages, st
         _ptr(sel_scores, torch.float32, "sel_scores", False), _ptr(q, torch.bfloat16, "q"),
         _ptr(k_pages, torch.bfloat16, "k_pages"), _ptr(v_pages, torch.bfloat16, "v_pages"),
         ptp, ptn, npg, _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", False),
-        wsp, wsn, _stream_ptr(stream)))
+        _ptr(gate, torch.bfloat16, "gate", False), wsp, wsn, _stream_ptr(stream)))
+
+
+# ---------------------------------------------------------------------------
+# the path's neighbours: main Q/K producer, sigmoid output gate
+# ---------------------------------------------------------------------------
+
+def qk_prep(cfg: Config, qk: QkConfig, seqs: Sequence[Seq], q_raw, k_raw, q_out, k_cache,
+            v_raw=None, v_cache=None, q_gamma=None, k_gamma=None, page_table=None,
+            stream=None) -> None:
+    arr, n = _seq_array(seqs)
+    if page_table is not None:
+        ptp, ptn, npg = _pages(page_table, k_cache)
+    else:
+        ptp, ptn, npg = None, 0, 0
+    _check(lib().sgqa_qk_prep(
+        ctypes.byref(cfg), ctypes.byref(qk), arr, n, _ptr(q_raw, torch.bfloat16, "q_raw"),
+        _ptr(k_raw, torch.bfloat16, "k_raw"), _ptr(v_raw, torch.bfloat16, "v_raw", False),
+        _ptr(q_gamma, torch.bfloat16, "q_gamma", False), _ptr(k_gamma, torch.bfloat16, "k_gamma", False),
+        _ptr(q_out, torch.bfloat16, "q_out"), _ptr(k_cache, torch.bfloat16, "k_cache"),
+        _ptr(v_cache, torch.bfloat16, "v_cache", False), ptp, ptn, npg, _stream_ptr(stream)))
+
+
+def sparse_attn_gated(cfg: Config, seqs: Sequence[Seq], q, k_cache, v_cache, sel, out, gate, lse=None,
+                      ws=None, stream=None) -> None:
+    arr, n = _seq_array(seqs)
+    wsp, wsn, _own = _workspace(cfg, seqs, OP_SPARSE_ATTN, q.device, ws, stream)
+    _check(lib().sgqa_sparse_attn_gated(
+        ctypes.byref(cfg), arr, n, _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(sel, torch.int32, "sel"), _ptr(out, torch.bfloat16, "out"),
+        _ptr(lse, torch.float32, "lse", False), _ptr(gate, torch.bfloat16, "gate"), wsp, wsn,
+        _stream_ptr(stream)))
+
+
+def forward_gated(cfg: Config, seqs: Sequence[Seq], proxy_k, comp_logits, store, q_idx, w, sel, q,
+                  k_cache, v_cache, out, gate, lse=None, sel_scores=None, ln_gamma=None, ln_beta=None,
+                  rms_gamma=None, ws=None, stream=None) -> None:
+    arr, n = _seq_array(seqs)
+    wsp, wsn, _own = _workspace(cfg, seqs, OP_FORWARD, q.device, ws, stream)
+    _check(lib().sgqa_forward_gated(
+        ctypes.byref(cfg), arr, n, _ptr(proxy_k, torch.bfloat16, "proxy_k"),
+        _ptr(comp_logits, torch.float32, "comp_logits"),
+        _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
+        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _ptr(store, torch.bfloat16, "store"),
+        _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"),
+        _ptr(rms_gamma, torch.bfloat16, "rms_gamma", False), _ptr(sel, torch.int32, "sel"),
+        _ptr(sel_scores, torch.float32, "sel_scores", False), _ptr(q, torch.bfloat16, "q"),
+        _ptr(k_cache, torch.bfloat16, "k_cache"), _ptr(v_cache, torch.bfloat16, "v_cache"),
+        _ptr(out, torch.bfloat16, "out"), _ptr(lse, torch.float32, "lse", False),
+        _ptr(gate, torch.bfloat16, "gate"), wsp, wsn, _stream_ptr(stream)))

@@ -437,13 +437,26 @@ __global__ __launch_bounds__(512) void attn_union_kernel(SeqTable seqs, AttnArgs
     for (int phase = 0; phase < 2; ++phase) {
         if ((col >> 4) == phase) {
             uint16_t* orow = kv_lds + (wave * 16 + head) * kOutStride;
+            // output gate (sigmoid of the logits), applied before rounding
+            const uint16_t* grow =
+                a.gate && q_ok ? a.gate + (qrow * kHeads + g * kHeadsPerGroup + head) * kHeadDim : nullptr;
 #pragma unroll
             for (int dt = 0; dt < 6; ++dt)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) {
+                    float v[4];
+#pragma unroll
+                    for (int i = 0; i < 4; ++i) v[i] = o[dt][4 * j + i] * inv;
+                    if (grow) {
+                        const uint2 gw = *(const uint2*)(grow + 32 * dt + 8 * j + 4 * hgrp);
+                        v[0] *= gate_sigmoid((uint16_t)(gw.x & 0xFFFFu));
+                        v[1] *= gate_sigmoid((uint16_t)(gw.x >> 16));
+                        v[2] *= gate_sigmoid((uint16_t)(gw.y & 0xFFFFu));
+                        v[3] *= gate_sigmoid((uint16_t)(gw.y >> 16));
+                    }
                     uint2 pk;
-                    pk.x = pack_bf16(o[dt][4 * j] * inv, o[dt][4 * j + 1] * inv);
-                    pk.y = pack_bf16(o[dt][4 * j + 2] * inv, o[dt][4 * j + 3] * inv);
+                    pk.x = pack_bf16(v[0], v[1]);
+                    pk.y = pack_bf16(v[2], v[3]);
                     *(uint2*)(orow + 32 * dt + 8 * j + 4 * hgrp) = pk;
                 }
         }

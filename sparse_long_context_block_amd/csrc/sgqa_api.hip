@@ -434,13 +434,14 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
 
 int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan& p,
              const void* q, const void* k_cache, const void* v_cache, const Paging& pg,
-             const int32_t* sel, void* out, float* lse, void* ws, hipStream_t st) {
+             const int32_t* sel, void* out, float* lse, const void* gate, void* ws, hipStream_t st) {
     sgqa::AttnArgs a;
     a.q = (const uint16_t*)q;
     a.k = (const uint16_t*)k_cache;
     a.v = (const uint16_t*)v_cache;
     a.page_table = pg.table;
     a.n_pages = pg.n_pages;
+    a.gate = (const uint16_t*)gate;
     a.sel = sel;
     a.out = (uint16_t*)out;
     a.lse = lse;
@@ -505,6 +506,7 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
             sgqa::AttnMergeArgs ma;
             ma.part_o = a.part_o;
             ma.part_ml = a.part_ml;
+            ma.gate = a.gate;
             ma.out = (uint16_t*)out;
             ma.lse = lse;
             ma.n_split = p.n_split;
@@ -520,7 +522,7 @@ int run_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs, co
                 const float* comp_logits, const void* ln_gamma, const void* ln_beta, void* store,
                 const void* q_idx, const float* w, const void* rms_gamma, int32_t* sel, float* sel_scores,
                 const void* q, const void* k_cache, const void* v_cache, const Paging& pg, void* out,
-                float* lse, void* ws, size_t ws_bytes, hipStream_t st) {
+                float* lse, const void* gate, void* ws, size_t ws_bytes, hipStream_t st) {
     const IndexPlan ip = plan_index(cfg, seqs, n_seqs);
     const AttnPlan ap = plan_attn(cfg, seqs, n_seqs);
     int rc = check_ws(std::max(ip.ws, ap.ws), ws, ws_bytes);
@@ -530,7 +532,7 @@ int run_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs, co
     if ((rc = run_index(cfg, seqs, n_seqs, ip, q_idx, w, rms_gamma, store, sel, sel_scores, nullptr, ws,
                         st)))
         return rc;
-    return run_attn(cfg, seqs, n_seqs, ap, q, k_cache, v_cache, pg, sel, out, lse, ws, st);
+    return run_attn(cfg, seqs, n_seqs, ap, q, k_cache, v_cache, pg, sel, out, lse, gate, ws, st);
 }
 
 }  // namespace
@@ -633,15 +635,30 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
         return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel and out are required");
     const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
-    return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, ws,
+    return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, nullptr, ws,
+                    (hipStream_t)hip_stream);
+}
+
+int sgqa_sparse_attn_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                           const void* q, const void* k_cache, const void* v_cache, const int32_t* sel,
+                           void* out, float* lse, const void* gate, void* ws, size_t ws_bytes,
+                           void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!q || !k_cache || !v_cache || !sel || !out || !gate)
+        return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel, out and gate are required");
+    const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
+    if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
+    return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, gate, ws,
                     (hipStream_t)hip_stream);
 }
 
 int sgqa_sparse_attn_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                            const void* q, const void* k_pages, const void* v_pages,
                            const int32_t* page_table, int64_t page_table_len, int64_t n_pages,
-                           const int32_t* sel, void* out, float* lse, void* ws, size_t ws_bytes,
-                           void* hip_stream) {
+                           const int32_t* sel, void* out, float* lse, const void* gate, void* ws,
+                           size_t ws_bytes, void* hip_stream) {
     int rc = check_config(cfg);
     if (rc) return rc;
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
@@ -653,7 +670,7 @@ int sgqa_sparse_attn_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
     Paging pg;
     pg.table = page_table;
     pg.n_pages = n_pages;
-    return run_attn(cfg, seqs, n_seqs, p, q, k_pages, v_pages, pg, sel, out, lse, ws,
+    return run_attn(cfg, seqs, n_seqs, p, q, k_pages, v_pages, pg, sel, out, lse, gate, ws,
                     (hipStream_t)hip_stream);
 }
 
@@ -672,8 +689,27 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                     "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache and out "
                     "are required");
     return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
-                       rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, ws, ws_bytes,
-                       (hipStream_t)hip_stream);
+                       rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, nullptr, ws,
+                       ws_bytes, (hipStream_t)hip_stream);
+}
+
+int sgqa_forward_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                       const void* proxy_k, const float* comp_logits, const void* ln_gamma,
+                       const void* ln_beta, void* store, const void* q_idx, const float* w,
+                       const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
+                       const void* k_cache, const void* v_cache, void* out, float* lse, const void* gate,
+                       void* ws, size_t ws_bytes, void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!proxy_k || !comp_logits || !store || !q_idx || !w || !sel || !q || !k_cache ||
+        !v_cache || !out || !gate)
+        return fail(SGQA_ERR_NULL,
+                    "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache, out and gate "
+                    "are required");
+    return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
+                       rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, gate, ws,
+                       ws_bytes, (hipStream_t)hip_stream);
 }
 
 int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
@@ -681,8 +717,8 @@ int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_s
                        const void* ln_beta, void* store, const void* q_idx, const float* w,
                        const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
                        const void* k_pages, const void* v_pages, const int32_t* page_table,
-                       int64_t page_table_len, int64_t n_pages, void* out, float* lse, void* ws,
-                       size_t ws_bytes, void* hip_stream) {
+                       int64_t page_table_len, int64_t n_pages, void* out, float* lse,
+                       const void* gate, void* ws, size_t ws_bytes, void* hip_stream) {
     int rc = check_config(cfg);
     if (rc) return rc;
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
@@ -696,8 +732,51 @@ int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_s
     pg.table = page_table;
     pg.n_pages = n_pages;
     return run_forward(cfg, seqs, n_seqs, proxy_pages, logit_pages, ln_gamma, ln_beta, store, q_idx, w,
-                       rms_gamma, sel, sel_scores, q, k_pages, v_pages, pg, out, lse, ws, ws_bytes,
+                       rms_gamma, sel, sel_scores, q, k_pages, v_pages, pg, out, lse, gate, ws, ws_bytes,
                        (hipStream_t)hip_stream);
+}
+
+int sgqa_qk_prep(const sgqa_config* cfg, const sgqa_qk_config* qk, const sgqa_seq* seqs, int32_t n_seqs,
+                 const void* q_raw, const void* k_raw, const void* v_raw, const void* q_gamma,
+                 const void* k_gamma, void* q_out, void* k_cache, void* v_cache, const int32_t* page_table,
+                 int64_t page_table_len, int64_t n_pages, void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if (!qk) return fail(SGQA_ERR_NULL, "qk is NULL");
+    if (qk->rope_dim < 0 || qk->rope_dim > cfg->head_dim || qk->rope_dim % 2 != 0)
+        return fail(SGQA_ERR_CONFIG, "qk rope_dim %d must be even and in [0, %d]", qk->rope_dim,
+                    cfg->head_dim);
+    if (!(isfinite(qk->rope_base) && qk->rope_base > 0.f) || !(isfinite(qk->eps) && qk->eps >= 0.f))
+        return fail(SGQA_ERR_CONFIG, "qk rope_base must be finite and positive, eps finite and >= 0");
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if (!q_raw || !k_raw || !q_out || !k_cache)
+        return fail(SGQA_ERR_NULL, "q_raw, k_raw, q_out and k_cache are required");
+    if ((v_raw == nullptr) != (v_cache == nullptr))
+        return fail(SGQA_ERR_NULL, "v_raw and v_cache go together");
+    if (page_table && (rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
+    sgqa::QkPrepArgs a;
+    a.q_raw = (const uint16_t*)q_raw;
+    a.k_raw = (const uint16_t*)k_raw;
+    a.v_raw = (const uint16_t*)v_raw;
+    a.q_gamma = (const uint16_t*)q_gamma;
+    a.k_gamma = (const uint16_t*)k_gamma;
+    a.q_out = (uint16_t*)q_out;
+    a.k_cache = (uint16_t*)k_cache;
+    a.v_cache = (uint16_t*)v_cache;
+    a.page_table = page_table;
+    a.n_pages = page_table ? n_pages : 0;
+    a.log_base = log((double)qk->rope_base);
+    a.rope_dim = qk->rope_dim;
+    a.eps = qk->eps;
+    for (int32_t first = 0; first < n_seqs; first += sgqa::kMaxSeqsPerLaunch) {
+        const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n_seqs - first);
+        sgqa::SeqTable tab;
+        const int64_t mx = fill_table(tab, seqs, first, cnt, [](const sgqa_seq& q) { return q.n_q; });
+        if (tab.n == 0) continue;
+        hipError_t e = sgqa::launch_qk_prep(tab, mx, a, (hipStream_t)hip_stream);
+        if (e != hipSuccess) return hip_fail(e, "qk_prep launch");
+    }
+    return SGQA_OK;
 }
 
 }  // extern "C"

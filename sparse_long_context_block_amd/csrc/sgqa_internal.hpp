@@ -97,6 +97,7 @@ struct AttnArgs {
     const uint16_t* v;
     const int32_t* page_table;  // paged K/V, or null
     int64_t n_pages;
+    const uint16_t* gate;       // bf16 [Nq, H, D] output-gate logits, or null
     const int32_t* sel;
     uint16_t* out;
     float* lse;            // may be null
@@ -112,6 +113,7 @@ struct AttnArgs {
 struct AttnMergeArgs {
     const float* part_o;
     const float* part_ml;
+    const uint16_t* gate;       // as AttnArgs::gate
     uint16_t* out;
     float* lse;
     int32_t n_split;
@@ -158,6 +160,26 @@ __host__ __device__ inline int list_rank(int64_t n0, int k) {
 // segments, with room to spare
 __host__ __device__ constexpr int list_capacity(int k) { return k < 1024 ? 8192 : 16384; }
 
+// Main-path Q/K producer: RMSNorm over each head's D dims (one gamma per
+// tensor, shared by the heads), the rotary span [0, rope_dim) at the token's
+// position, bf16; V rows copied.  Q rows go to q_out, K/V rows into the
+// caches (contiguous, or paged as in CompressArgs).
+struct QkPrepArgs {
+    const uint16_t* q_raw;      // [Nq, H, D]
+    const uint16_t* k_raw;      // [Nq, G, D]
+    const uint16_t* v_raw;      // [Nq, G, D] or null
+    const uint16_t* q_gamma;    // [D] or null
+    const uint16_t* k_gamma;    // [D] or null
+    uint16_t* q_out;
+    uint16_t* k_cache;
+    uint16_t* v_cache;
+    const int32_t* page_table;
+    int64_t n_pages;
+    double log_base;            // ln(rope base)
+    int32_t rope_dim;
+    float eps;
+};
+
 // a launch table travels in the kernel arguments, which hold at most 4 KiB
 static_assert(sizeof(SeqTable) + sizeof(IndexArgs) <= 4096, "index kernel arguments fit");
 static_assert(sizeof(SeqTable) + sizeof(AttnArgs) + 8 <= 4096, "attention kernel arguments fit");
@@ -168,6 +190,7 @@ static_assert(sizeof(SeqTable) + sizeof(CompressArgs) <= 4096, "compress kernel 
 // ---------------------------------------------------------------------------
 hipError_t launch_compress(const SeqTable& seqs, int64_t max_blocks, const CompressArgs& a,
                            hipStream_t stream);
+hipError_t launch_qk_prep(const SeqTable& seqs, int64_t max_nq, const QkPrepArgs& a, hipStream_t stream);
 size_t index_lds_bytes(int cap);
 constexpr size_t kMaxLds = 160 * 1024;
 hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
@@ -206,6 +229,11 @@ typedef __attribute__((ext_vector_type(4))) short i16x4;
 typedef __attribute__((ext_vector_type(4))) float f32x4;
 
 __device__ __forceinline__ int lane_id() { return threadIdx.x & 63; }
+
+// sigmoid of a bf16 gate logit (fp32; 0 and 1 at the extremes)
+__device__ __forceinline__ float gate_sigmoid(uint16_t bits) {
+    return 1.0f / (1.0f + __expf(-__uint_as_float((uint32_t)bits << 16)));
+}
 
 // pool row of position pos through a sequence's page table pt (ids outside
 // [0, n_pages) are clamped, so a bad table never reads outside the pool)

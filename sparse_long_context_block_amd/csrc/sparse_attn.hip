@@ -284,8 +284,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
         }
         const int d = e - head * kHeadDim;
         if (a.n_split == 1) {
-            a.out[(row * kHeads + g * kHeadsPerGroup + head) * kHeadDim + d] =
-                (uint16_t)f32_to_bf16(O / L);
+            const int64_t oi = (row * kHeads + g * kHeadsPerGroup + head) * kHeadDim + d;
+            a.out[oi] = (uint16_t)f32_to_bf16(a.gate ? O / L * gate_sigmoid(a.gate[oi]) : O / L);
             if (a.lse && d == 0) a.lse[row * kHeads + g * kHeadsPerGroup + head] = (M + log2f(L)) * kLn2;
         } else {
             const int64_t part = rg * a.n_split + split;
@@ -333,7 +333,8 @@ __global__ __launch_bounds__(256) void attn_merge_kernel(SeqTable seqs, AttnMerg
         float O = 0.f;
         for (int s = 0; s < a.n_split; ++s)
             O += wsc[s][head] * a.part_o[((rg * a.n_split + s) * kHeadsPerGroup) * kHeadDim + e];
-        a.out[(row * kHeads + g * kHeadsPerGroup) * kHeadDim + e] = (uint16_t)f32_to_bf16(O);
+        const int64_t oi = (row * kHeads + g * kHeadsPerGroup) * kHeadDim + e;
+        a.out[oi] = (uint16_t)f32_to_bf16(a.gate ? O * gate_sigmoid(a.gate[oi]) : O);
     }
 }
 

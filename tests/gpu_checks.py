@@ -143,7 +143,11 @@ class Checker:
         return st
 
     # -- one sequence ----------------------------------------------------------
-    def check_seq(self, si: int, qs: np.ndarray, store_exact=None, check_attn: bool = True):
+    def check_seq(self, si: int, qs: np.ndarray, store_exact=None, check_attn: bool = True,
+                  gate_bits=None):
+        """Check query rows qs (0-based in sequence si): scores, selection
+        and, unless check_attn is False, attention; gate_bits (bf16 bits
+        [Nq, H, D]) makes the reference the sigmoid-gated output."""
         wl, ocfg = self.wl, self.ocfg
         s = wl.seqs[si]
         B, K = wl.block_size, wl.topk
@@ -202,6 +206,8 @@ class Checker:
                 u = np.searchsorted(toks, sets[g])
                 heads = slice(16 * g, 16 * g + 16)
                 o, l = O.attend(q[heads], kk[u, g], vv[u, g], ocfg.softmax_scale)
+                if gate_bits is not None:
+                    o = O.gate(o, gate_bits[row, heads])
                 self._o_ref.append(o)
                 self._l_ref.append(l)
                 self._o_gpu.append(self.out[row, heads])

@@ -205,7 +205,7 @@ def test_paged_calls_validate_the_page_table(L):
     s = sg.seq(100, pos0=900, kv_offset=10, kv_capacity=1000)   # 63 pages: entries 10..72
     arr, n = _seqs(s)
     attn = lambda pt, ln, npg: L.sgqa_sparse_attn_paged(ctypes.byref(cfg), arr, n, P, P, P, pt, ln,
-                                                        npg, P, P, None, None, 0, None)
+                                                        npg, P, P, None, None, None, 0, None)
     assert attn(None, 73, 8) == E_NULL
     assert attn(P, 72, 8) == E_CAPACITY
     assert "page-table entries 10 .. 72" in L.sgqa_last_error().decode()
@@ -216,10 +216,37 @@ def test_paged_calls_validate_the_page_table(L):
                                                 P, None, 0, None)
     assert comp(None, 73) == E_NULL
     assert comp(P, 72) == E_CAPACITY
-    args = [ctypes.byref(cfg), arr, n] + [P] * 13 + [P, 72, 8, P, None, None, 0, None]
+    args = [ctypes.byref(cfg), arr, n] + [P] * 13 + [P, 72, 8, P, None, None, None, 0, None]
     assert L.sgqa_forward_paged(*args) == E_CAPACITY
     args[16] = None
     assert L.sgqa_forward_paged(*args) == E_NULL
+
+
+def test_neighbour_calls_validate(L):
+    cfg = sg.config()
+    P = ctypes.c_void_p(FAKE)
+    arr, n = _seqs(sg.seq(16, pos0=48))
+    qk = sg.qk_config(rope_dim=64)
+    prep = lambda qkc, *ptrs: L.sgqa_qk_prep(ctypes.byref(cfg), ctypes.byref(qkc) if qkc else None, arr, n,
+                                             *ptrs, None, 0, 0, None)
+    full = [P, P, P, None, None, P, P, P]
+    assert prep(None, *full) == E_NULL
+    assert prep(sg.qk_config(rope_dim=63), *full) == E_CONFIG
+    assert prep(sg.qk_config(rope_dim=194), *full) == E_CONFIG
+    assert prep(sg.qk_config(rope_base=0.0), *full) == E_CONFIG
+    assert prep(sg.qk_config(eps=-1.0), *full) == E_CONFIG
+    assert prep(qk, None, P, P, None, None, P, P, P) == E_NULL                    # q_raw
+    assert prep(qk, P, P, None, None, None, P, P, P) == E_NULL                    # v_raw without v_cache's pair
+    assert "together" in L.sgqa_last_error().decode()
+    # a paged producer checks the table like the other paged calls
+    assert L.sgqa_qk_prep(ctypes.byref(cfg), ctypes.byref(qk), arr, n, P, P, None, None, None, P, P, None,
+                          P, 3, 8, None) == E_CAPACITY
+    # the gate is required by the gated calls
+    assert L.sgqa_sparse_attn_gated(ctypes.byref(cfg), arr, n, P, P, P, P, P, None, None, None, 0,
+                                    None) == E_NULL
+    args = [ctypes.byref(cfg), arr, n] + [P] * 15 + [None, None, 0, None]     # gate NULL
+    assert L.sgqa_forward_gated(*args) == E_NULL
+    assert "gate" in L.sgqa_last_error().decode()
 
 
 def test_binding_rejects_wrong_tensors():
