@@ -7,11 +7,15 @@ seeded synthetic input already resident in HBM.  Default workload: the
 single-layer prefill of 8,192 tokens (64 heads / 4 KV groups / head_dim 192,
 indexer 4 x 128 per group, B=8, k = 512 blocks = 4,096 tokens).
 
-Prints one JSON line with whole-step throughput, the roofline of the dominant
-kernel (its per-launch time measured with HIP events on the stream it runs
-on) and the CPU oracle timed on a bounded sample of the same workload.
+Prints one JSON line with whole-step throughput, the distribution of single
+step times (warm, and cold: a 512 MiB write between steps evicts the caches),
+the roofline of the dominant kernel (its per-launch time measured with HIP
+events on the stream it runs on, against AMD's published peak and against
+what this GPU reaches on a plain copy and a bf16 GEMM), and the CPU oracle
+timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+                    [--paged] [--neighbours] [--store-bf16] [--no-cold] [--no-peaks]
 """
 from __future__ import annotations
 
@@ -155,29 +159,82 @@ def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def recorded_traffic(workload: str):
-    """HBM bytes per launch of the dominant kernel from the committed counter
-    summary (FETCH_SIZE + WRITE_SIZE, calibrated against a device copy), or
-    None when that summary is for another workload or the kernel's source
-    has changed since the counters were taken."""
+def recorded_counters(workload: str, kernel: str):
+    """HBM bytes per launch of `kernel` on `workload` from a committed counter
+    summary under profiles/ (FETCH_SIZE and WRITE_SIZE, calibrated against a
+    device copy), or None when no summary covers that pair or the kernel's
+    source has changed since the counters were taken."""
+    import glob
     import hashlib
-    path = os.path.join(ROOT, "profiles", "attn_union_prefill_8k.md")
-    if not os.path.exists(path):
-        return None
-    rec = {}
-    for line in open(path):
-        parts = line.strip().split(": ", 1)
-        if len(parts) == 2 and parts[0] in ("traffic_workload", "traffic_bytes_per_launch",
-                                            "source_file", "source_sha256"):
-            rec[parts[0]] = parts[1]
-    if rec.get("traffic_workload") != workload or "source_file" not in rec:
-        return None
-    src = os.path.join(ROOT, rec["source_file"])
-    if not os.path.exists(src):
-        return None
-    if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
-        return None
-    return int(rec["traffic_bytes_per_launch"])
+    for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
+        rec = {}
+        for line in open(path):
+            parts = line.strip().split(": ", 1)
+            if len(parts) == 2 and parts[0].startswith(("traffic_", "source_")):
+                rec[parts[0]] = parts[1]
+        if rec.get("traffic_workload") != workload or rec.get("traffic_kernel") != kernel:
+            continue
+        src = os.path.join(ROOT, rec.get("source_file", ""))
+        if not os.path.isfile(src):
+            return None
+        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+            return None
+        return {"fetch": int(rec["traffic_fetch_bytes_per_launch"]),
+                "write": int(rec["traffic_write_bytes_per_launch"])}
+    return None
+
+
+def measured_peaks(stream) -> dict:
+    """What this GPU reaches on plain work: a 1 GiB device-to-device copy
+    (bytes read + written per second), a 1 GiB fp32 sum (bytes read per
+    second) and a bf16 8192^3 matrix product, all through torch."""
+    import torch
+    out = {}
+    with torch.cuda.stream(stream):
+        a = torch.empty(1 << 30, dtype=torch.uint8, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        ms = event_time_ms(lambda: b.copy_(a), stream, 10)
+        out["hbm_copy_GBps"] = 2 * a.numel() / (ms * 1e-3) / 1e9
+        f = a.view(torch.float32).zero_()
+        for _ in range(3):
+            f.sum()
+        ms = event_time_ms(lambda: f.sum(), stream, 10)
+        out["hbm_read_GBps"] = a.numel() / (ms * 1e-3) / 1e9
+        del a, b, f
+        n = 8192
+        x = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        y = torch.randn(n, n, dtype=torch.bfloat16, device="cuda")
+        for _ in range(3):
+            torch.matmul(x, y)
+        ms = event_time_ms(lambda: torch.matmul(x, y), stream, 10)
+        out["bf16_gemm_TFLOPs"] = 2 * n ** 3 / (ms * 1e-3) / 1e12
+        del x, y
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return out
+
+
+def step_times(step, stream, n: int, flush=None) -> dict:
+    """Per-step HIP-event times over n steps on the launch stream: median,
+    10th and 90th percentile.  With `flush` (cold mode) a 512 MiB buffer is
+    written before every step, outside the timed interval, so the step starts
+    with the L2s and the Infinity Cache holding none of its inputs."""
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+          for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(i & 0x7F)
+            ev[i][0].record(stream)
+            step()
+            ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    ms = np.array([a.elapsed_time(b) for a, b in ev])
+    return {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+            "p90_ms": float(np.percentile(ms, 90)), "n": n}
 
 
 def event_time_ms(fn, stream, reps: int) -> float:
@@ -205,6 +262,14 @@ def main() -> int:
                     help="also run one 512 MiB device-to-device copy (HBM byte-counter scale)")
     ap.add_argument("--paged", action="store_true",
                     help="per-token caches as pools of 16-token pages behind a random page table")
+    ap.add_argument("--neighbours", action="store_true",
+                    help="each step also runs the main Q/K producer (RMSNorm, partial rotary span, "
+                         "cache writes) before the path and the sigmoid output gate in the attention")
+    ap.add_argument("--store-bf16", action="store_true",
+                    help="keep the store in bf16 (no E4M3 rounding: the ablation)")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache step times")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring this GPU's copy bandwidth and bf16 GEMM rate")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (the path has no multi-GPU part); "
@@ -215,9 +280,9 @@ def main() -> int:
 
     import sparse_long_context_block_amd as sg
     from synth import workloads as W
-    from tests.gpu_checks import lib_seq, lib_seqs, prepare
+    from tests.gpu_setup import lib_seq, lib_seqs, prepare
 
-    wl = W.make(args.workload)
+    wl = W.make(args.workload, store_q8=not args.store_bf16)
     if args.paged and wl.loop_steps:
         print("bench.py --paged takes workloads of one call", file=sys.stderr)
         return 2
@@ -231,6 +296,17 @@ def main() -> int:
             di.t[name] = None
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
+    nb = None
+    if args.neighbours:
+        # raw main Q/K/V of the new tokens (bf16 unit normal) and gate logits;
+        # the producer writes Q and the new tokens' K/V cache rows every step
+        gen = torch.Generator(device="cuda")
+        gen.manual_seed(0)
+        nq_rows = di["q"].shape[0]
+        bf = dict(dtype=torch.bfloat16, device="cuda", generator=gen)
+        nb = {"q_raw": torch.randn(nq_rows, H, D, **bf), "k_raw": torch.randn(nq_rows, G, D, **bf),
+              "v_raw": torch.randn(nq_rows, G, D, **bf), "gate": torch.randn(nq_rows, H, D, **bf),
+              "qk": sg.qk_config()}
     # a loop of calls (a decode loop: one token per sequence per call; a
     # chained prefill: one chunk per call) runs call k at step k, wrapping
     # around; repeating a call recomputes the same outputs
@@ -248,17 +324,31 @@ def main() -> int:
     ws_view = ws[(-ws.data_ptr()) % 256:][:max(ws_n, 1)]
     step_no = [0]
 
+    k_cache = pools["k"] if pools is not None else di["k"]
+    v_cache = pools["v"] if pools is not None else di["v"]
+    gate = nb["gate"] if nb else None
+
+    def op_qk_prep(sq):
+        sg.qk_prep(cfg, nb["qk"], sq, nb["q_raw"], nb["k_raw"], di["q"], k_cache, v_raw=nb["v_raw"],
+                   v_cache=v_cache, page_table=table, stream=stream)
+
     def step():
         sq = loop[step_no[0] % len(loop)]
         step_no[0] += 1
+        if nb:
+            op_qk_prep(sq)
         if pools is not None:
             sg.forward_paged(cfg, sq, pools["proxy_k"], pools["logits"], di["store"], di["q_idx"],
                              di["w"], di["sel"], di["q"], pools["k"], pools["v"], table, di["out"],
-                             lse=di["lse"], ws=ws_view, stream=stream)
-            return
-        sg.forward(cfg, sq, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
-                   di["sel"], di["q"], di["k"], di["v"], di["out"], lse=di["lse"],
-                   ws=ws_view, stream=stream)
+                             lse=di["lse"], gate=gate, ws=ws_view, stream=stream)
+        elif nb:
+            sg.forward_gated(cfg, sq, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
+                             di["sel"], di["q"], di["k"], di["v"], di["out"], gate, lse=di["lse"],
+                             ws=ws_view, stream=stream)
+        else:
+            sg.forward(cfg, sq, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
+                       di["sel"], di["q"], di["k"], di["v"], di["out"], lse=di["lse"],
+                       ws=ws_view, stream=stream)
 
     def op_compress():
         if pools is not None:
@@ -274,10 +364,13 @@ def main() -> int:
     def op_attn():
         if pools is not None:
             sg.sparse_attn_paged(cfg, seqs, di["q"], pools["k"], pools["v"], table, di["sel"],
-                                 di["out"], lse=di["lse"], ws=ws_view, stream=stream)
-            return
-        sg.sparse_attn(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"],
-                       lse=di["lse"], ws=ws_view, stream=stream)
+                                 di["out"], lse=di["lse"], gate=gate, ws=ws_view, stream=stream)
+        elif nb:
+            sg.sparse_attn_gated(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"], gate,
+                                 lse=di["lse"], ws=ws_view, stream=stream)
+        else:
+            sg.sparse_attn(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"],
+                           lse=di["lse"], ws=ws_view, stream=stream)
 
     for _ in range(args.warmup):
         step()
@@ -292,6 +385,15 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     timed = [loop[k % len(loop)] for k in range(first_timed, step_no[0])]
+    # the distribution of single steps (after the timed region): warm, and
+    # for workloads of one call also cold; a loop's steps are different calls
+    n_dist = min(args.steps, 20)
+    dist = {"warm": step_times(step, stream, n_dist)} if n_dist > 0 else {}
+    if not args.no_cold and not wl.loop_steps and n_dist > 0:
+        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        dist["cold"] = step_times(step, stream, n_dist, flush)
+        del flush
+    print(f"[bench] step times {dist}", file=sys.stderr, flush=True)
     # per-op timings and the roofline use the loop's last call (its longest
     # context), or the step itself
     seqs = loop[-1]
@@ -302,8 +404,11 @@ def main() -> int:
         "index_topk": event_time_ms(op_index, stream, reps),
         "sparse_attn": event_time_ms(op_attn, stream, reps),
     }
+    if nb:
+        k_ms["qk_prep"] = event_time_ms(lambda: op_qk_prep(seqs), stream, reps)
     print(f"[bench] per-op ms {k_ms}", file=sys.stderr, flush=True)
 
+    peaks = None if args.no_peaks else measured_peaks(stream)
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dst = torch.empty_like(src)
@@ -332,19 +437,37 @@ def main() -> int:
                 "kernel": "sparse_attn_kernel + attn_merge_kernel (one sgqa_sparse_attn call)",
                 "algorithmic_bytes_per_launch": wm["attn_gather_bytes"],
                 "launch_ms": k_ms["sparse_attn"]}
+        if peaks:
+            roof["measured_peak"] = max(peaks["hbm_copy_GBps"], peaks["hbm_read_GBps"])
+            roof["frac_of_measured"] = achieved / roof["measured_peak"]
         queries = wm_loop_queries / args.steps if wm_loop_queries else wm["queries"]
         value, unit = queries / (ms_step * 1e-3), "queries/s"
     else:
         achieved = wm["attn_flops"] / (k_ms["sparse_attn"] * 1e-3) / 1e12
-        kern = (f"attn_union_kernel<{wl.block_size.bit_length() - 1}>" if dense == wm["queries"]
-                else f"attn_union_kernel<{wl.block_size.bit_length() - 1}> + sparse_attn_kernel "
-                     f"({dense} of {wm['queries']} queries tiled)")
-        traffic = recorded_traffic(wl.name) if dense == wm["queries"] and not args.paged else None
+        lb = wl.block_size.bit_length() - 1
+        kern = (f"attn_union_kernel<{lb}>" if dense == wm["queries"]
+                else "sparse_attn_kernel" if dense == 0
+                else f"attn_union_kernel<{lb}> + sparse_attn_kernel ({dense} of {wm['queries']} "
+                     f"queries tiled)")
+        # counters were taken on the plain (contiguous, ungated) call that
+        # runs one attention kernel
+        ctr_kernel = ("attn_union_kernel<%d, false>" % (wl.block_size.bit_length() - 1)
+                      if dense == wm["queries"] else "sparse_attn_kernel<false>" if dense == 0 else None)
+        ctr = (recorded_counters(wl.name, ctr_kernel)
+               if ctr_kernel and not args.paged and not nb and wl.store_q8 else None)
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16_FLOPS / 1e12), "traffic": traffic,
+                "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16_FLOPS / 1e12),
+                "traffic": ctr["fetch"] + ctr["write"] if ctr else None,
                 "kernel": kern,
                 "algorithmic_flops_per_launch": wm["attn_flops"],
                 "launch_ms": k_ms["sparse_attn"]}
+        if peaks:
+            roof["measured_peak"] = peaks["bf16_gemm_TFLOPs"]
+            roof["frac_of_measured"] = achieved / peaks["bf16_gemm_TFLOPs"]
+        if ctr:
+            # K/V bytes a gather per (query, group) would move over the bytes
+            # the kernel fetched from HBM
+            roof["reuse"] = wm["attn_gather_bytes"] / ctr["fetch"]
         if dense < wm["queries"]:
             # gathered K/V rows (768 B per query, group and attended token):
             # the rate the gather kernel moves them at, against HBM peak
@@ -356,13 +479,17 @@ def main() -> int:
         "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
         "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name + ("+paged" if args.paged else ""), "queries": wm["queries"],
+        "config": {"workload": wl.name + ("+paged" if args.paged else "")
+                   + ("+neighbours" if nb else ""), "queries": wm["queries"],
                    "block_size": wl.block_size,
                    "topk_blocks": wl.topk, "store_q8": wl.store_q8,
                    "heads": H, "kv_groups": G, "head_dim": D},
         "per_op_ms": k_ms,
+        "step_times": dist,
         "roofline": roof,
     }
+    if peaks:
+        res["measured_peaks"] = peaks
     if wl.loop_steps:
         res["config"]["loop_calls"] = wl.loop_steps
         res["config"]["per_op_call"] = wl.loop_steps - 1

@@ -23,7 +23,9 @@
  * Memory.   Every tensor pointer is a DEVICE pointer to memory the caller
  *           owns (allocated e.g. by PyTorch); the library never allocates,
  *           frees or synchronises.  Tensors are dense, row-major, without
- *           padding.  bf16 is the 16-bit brain-float bit pattern.  Scratch
+ *           padding, and start at a 16-byte aligned address (every torch
+ *           allocation does; a misaligned pointer returns SGQA_ERR_SHAPE).
+ *           bf16 is the 16-bit brain-float bit pattern.  Scratch
  *           memory comes from the caller as (ws, ws_bytes) of at least
  *           sgqa_workspace_size(...) bytes, 256-byte aligned; ws may be NULL
  *           when that size is 0.  Workspace contents need no initialisation
@@ -64,7 +66,7 @@ typedef enum sgqa_status {
     SGQA_OK = 0,
     SGQA_ERR_NULL = -1,        /* a required pointer is NULL                          */
     SGQA_ERR_CONFIG = -2,      /* inconsistent or out-of-range sgqa_config field      */
-    SGQA_ERR_SHAPE = -3,       /* bad sequence descriptor (negative or overflowing)   */
+    SGQA_ERR_SHAPE = -3,       /* bad sequence descriptor, or a misaligned tensor     */
     SGQA_ERR_CAUSAL = -4,      /* cache_len != pos0 + n_q                             */
     SGQA_ERR_CAPACITY = -5,    /* cache_len exceeds kv_capacity, or store too small  */
     SGQA_ERR_WORKSPACE = -6,   /* ws_bytes below sgqa_workspace_size, or misaligned  */

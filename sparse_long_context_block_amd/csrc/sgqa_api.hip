@@ -9,6 +9,8 @@
 #include <string.h>
 
 #include <algorithm>
+#include <initializer_list>
+#include <utility>
 #include <string>
 
 #include "sgqa.h"
@@ -286,6 +288,14 @@ AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split * sgqa::kHeadsPerGroup;
     p.ws = align_up(parts * sgqa::kHeadDim * 4) + align_up(parts * 2 * 4);
     return p;
+}
+
+// Tensor rows are read and written with vector accesses of up to 16 bytes.
+int check_aligned(std::initializer_list<std::pair<const void*, const char*>> ptrs) {
+    for (const auto& p : ptrs)
+        if (p.first && ((uintptr_t)p.first & 15u))
+            return fail(SGQA_ERR_SHAPE, "%s is not 16-byte aligned", p.second);
+    return SGQA_OK;
 }
 
 int check_ws(size_t need, void* ws, size_t ws_bytes) {
@@ -585,6 +595,7 @@ int sgqa_compress(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
     if (!proxy_k || !comp_logits || !store)
         return fail(SGQA_ERR_NULL, "proxy_k, comp_logits and store are required");
+    if ((rc = check_aligned({{proxy_k, "proxy_k"}, {comp_logits, "comp_logits"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}}))) return rc;
     return run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, Paging(), ln_gamma, ln_beta, store,
                         (hipStream_t)hip_stream);
 }
@@ -601,6 +612,7 @@ int sgqa_compress_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
     if (!proxy_pages || !logit_pages || !store)
         return fail(SGQA_ERR_NULL, "proxy_pages, logit_pages and store are required");
+    if ((rc = check_aligned({{proxy_pages, "proxy_pages"}, {logit_pages, "logit_pages"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}}))) return rc;
     if ((rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
     Paging pg;
     pg.table = page_table;
@@ -618,6 +630,7 @@ int sgqa_index_topk(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
     if (!q_idx || !w || !store || !sel)
         return fail(SGQA_ERR_NULL, "q_idx, w, store and sel are required");
+    if ((rc = check_aligned({{q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {store, "store"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q_hat_out, "q_hat_out"}}))) return rc;
     const IndexPlan p = plan_index(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
     return run_index(cfg, seqs, n_seqs, p, q_idx, w, rms_gamma, store, sel, sel_scores,
@@ -633,6 +646,7 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
     if (!q || !k_cache || !v_cache || !sel || !out)
         return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel and out are required");
+    if ((rc = check_aligned({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {sel, "sel"}, {out, "out"}, {lse, "lse"}}))) return rc;
     const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
     return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, nullptr, ws,
@@ -648,6 +662,7 @@ int sgqa_sparse_attn_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
     if (!q || !k_cache || !v_cache || !sel || !out || !gate)
         return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel, out and gate are required");
+    if ((rc = check_aligned({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {sel, "sel"}, {out, "out"}, {lse, "lse"}, {gate, "gate"}}))) return rc;
     const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
     return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, gate, ws,
@@ -664,6 +679,7 @@ int sgqa_sparse_attn_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
     if (!q || !k_pages || !v_pages || !sel || !out)
         return fail(SGQA_ERR_NULL, "q, k_pages, v_pages, sel and out are required");
+    if ((rc = check_aligned({{q, "q"}, {k_pages, "k_pages"}, {v_pages, "v_pages"}, {sel, "sel"}, {out, "out"}, {lse, "lse"}, {gate, "gate"}}))) return rc;
     if ((rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
     const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
@@ -688,6 +704,7 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
         return fail(SGQA_ERR_NULL,
                     "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache and out "
                     "are required");
+    if ((rc = check_aligned({{proxy_k, "proxy_k"}, {comp_logits, "comp_logits"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}, {q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {out, "out"}, {lse, "lse"}}))) return rc;
     return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
                        rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, nullptr, ws,
                        ws_bytes, (hipStream_t)hip_stream);
@@ -707,6 +724,7 @@ int sgqa_forward_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_s
         return fail(SGQA_ERR_NULL,
                     "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache, out and gate "
                     "are required");
+    if ((rc = check_aligned({{proxy_k, "proxy_k"}, {comp_logits, "comp_logits"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}, {q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {out, "out"}, {lse, "lse"}, {gate, "gate"}}))) return rc;
     return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
                        rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, gate, ws,
                        ws_bytes, (hipStream_t)hip_stream);
@@ -727,6 +745,7 @@ int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_s
         return fail(SGQA_ERR_NULL,
                     "proxy_pages, logit_pages, store, q_idx, w, sel, q, k_pages, v_pages and out "
                     "are required");
+    if ((rc = check_aligned({{proxy_pages, "proxy_pages"}, {logit_pages, "logit_pages"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}, {q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q, "q"}, {k_pages, "k_pages"}, {v_pages, "v_pages"}, {out, "out"}, {lse, "lse"}, {gate, "gate"}}))) return rc;
     if ((rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
     Paging pg;
     pg.table = page_table;
@@ -753,6 +772,7 @@ int sgqa_qk_prep(const sgqa_config* cfg, const sgqa_qk_config* qk, const sgqa_se
         return fail(SGQA_ERR_NULL, "q_raw, k_raw, q_out and k_cache are required");
     if ((v_raw == nullptr) != (v_cache == nullptr))
         return fail(SGQA_ERR_NULL, "v_raw and v_cache go together");
+    if ((rc = check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {q_gamma, "q_gamma"}, {k_gamma, "k_gamma"}, {q_out, "q_out"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}}))) return rc;
     if (page_table && (rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
     sgqa::QkPrepArgs a;
     a.q_raw = (const uint16_t*)q_raw;

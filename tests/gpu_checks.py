@@ -6,9 +6,6 @@ the GPU.  See tests/parity.py for the comparison rules.
 """
 from __future__ import annotations
 
-import sys
-import time
-
 import numpy as np
 import torch
 
@@ -18,53 +15,12 @@ from oracle import sgqa as O
 from synth import workloads as W
 
 from . import parity as P
-
-
-def log(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
-
-
-def lib_config(wl: W.Workload) -> sg.Config:
-    return sg.config(block_size=wl.block_size, topk_blocks=wl.topk, store_q8=wl.store_q8)
+from .gpu_setup import lib_config, lib_seq, lib_seqs, log, prepare, setup_seqs  # noqa: F401
 
 
 def oracle_config(wl: W.Workload) -> O.Config:
     return O.Config(block_size=wl.block_size, topk_blocks=wl.topk, store_q8=wl.store_q8,
                     softmax_scale=float(np.float32(1.0 / np.sqrt(192.0))))
-
-
-def lib_seqs(wl: W.Workload):
-    return [sg.Seq(q_offset=s.q_offset, n_q=s.n_q, pos0=s.pos0, cache_len=s.cache_len,
-                   kv_offset=s.kv_offset, kv_capacity=s.kv_capacity,
-                   store_offset=s.store_offset, store_capacity=s.store_capacity)
-            for s in wl.seqs]
-
-
-def setup_seqs(wl: W.Workload):
-    """Descriptors that write the store blocks of the cached history (before
-    the measured step's new tokens; for a decode loop, before its first step)."""
-    seqs = wl.step_seqs(0) if wl.loop_steps else wl.seqs
-    return [sg.Seq(q_offset=0, n_q=s.pos0, pos0=0, cache_len=s.pos0, kv_offset=s.kv_offset,
-                   kv_capacity=s.kv_capacity, store_offset=s.store_offset,
-                   store_capacity=s.store_capacity)
-            for s in seqs if s.pos0 > 0]
-
-
-def lib_seq(s: W.SeqLayout) -> sg.Seq:
-    return sg.Seq(q_offset=s.q_offset, n_q=s.n_q, pos0=s.pos0, cache_len=s.cache_len,
-                  kv_offset=s.kv_offset, kv_capacity=s.kv_capacity,
-                  store_offset=s.store_offset, store_capacity=s.store_capacity)
-
-
-def prepare(wl: W.Workload):
-    di = W.device_inputs(wl)
-    cfg = lib_config(wl)
-    pre = setup_seqs(wl)
-    if pre:
-        sg.compress(cfg, pre, di["proxy_k"], di["logits"], di["store"])
-    torch.cuda.synchronize()
-    return di, cfg
 
 
 def run_steps(wl: W.Workload, di, cfg, use_forward: bool = False):

@@ -249,6 +249,37 @@ def test_neighbour_calls_validate(L):
     assert "gate" in L.sgqa_last_error().decode()
 
 
+def test_misaligned_tensors(L):
+    # every tensor pointer must be 16-byte aligned; the message names the tensor
+    cfg = sg.config()
+    P, M = ctypes.c_void_p(FAKE), ctypes.c_void_p(FAKE + 8)
+    arr, n = _seqs(sg.seq(16, pos0=48))
+    err = lambda: L.sgqa_last_error().decode()
+    assert L.sgqa_compress(ctypes.byref(cfg), arr, n, P, P, None, None, M, None, 0, None) == E_SHAPE
+    assert "store" in err() and "aligned" in err()
+    assert L.sgqa_index_topk(ctypes.byref(cfg), arr, n, P, P, None, P, P, M, None, None, 0,
+                             None) == E_SHAPE
+    assert "sel_scores" in err()
+    assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, P, P, P, P, P, ctypes.c_void_p(FAKE + 4),
+                              None, 0, None) == E_SHAPE
+    assert "lse" in err()
+    assert L.sgqa_sparse_attn_gated(ctypes.byref(cfg), arr, n, P, P, P, P, P, None, M, None, 0,
+                                    None) == E_SHAPE
+    assert "gate" in err()
+    req = [3, 4, 7, 8, 9, 11, 13, 14, 15, 16]
+    args = [ctypes.byref(cfg), arr, n] + [None] * 18
+    for i in req:
+        args[i] = P
+    args[19] = 0
+    args[13] = M                                  # q
+    assert L.sgqa_forward(*args) == E_SHAPE
+    assert "q is" in err()
+    qk = sg.qk_config()
+    assert L.sgqa_qk_prep(ctypes.byref(cfg), ctypes.byref(qk), arr, n, P, M, None, None, None, P, P, None,
+                          None, 0, 0, None) == E_SHAPE
+    assert "k_raw" in err()
+
+
 def test_binding_rejects_wrong_tensors():
     import torch
     cfg = sg.config()
