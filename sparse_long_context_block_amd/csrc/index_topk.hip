@@ -448,8 +448,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
     __shared__ float4 wlds[kScoreTileQueries][kGroups];
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t n_qt = (sq.n_q + kScoreTileQueries - 1) / kScoreTileQueries;
-    const int64_t qt = blockIdx.x / a.n_split;
-    const int split = blockIdx.x % a.n_split;
+    // Keyed tiles: a query tile's candidate ranges in dispatch order, so
+    // neighbouring workgroups write neighbouring pieces of the same key rows.
+    // Listed tiles (long rows, few writes, the store read once per query
+    // tile): workgroups go out round-robin over the 8 XCDs, and each XCD
+    // takes a contiguous run of the range-major order, so the query tiles
+    // that read one store range run on one XCD close together in time and
+    // find it in that XCD's L2 (the remap is a bijection on the first
+    // multiple of 8 workgroups and the identity on the rest).
+    const uint32_t nwg = gridDim.x, full = nwg / 8 * 8, b = blockIdx.x;
+    const uint32_t n_qt_grid = nwg / (uint32_t)a.n_split;
+    const uint32_t l = b < full ? (b % 8) * (full / 8) + b / 8 : b;
+    const int64_t qt = LISTED ? l % n_qt_grid : b / (uint32_t)a.n_split;
+    const int split = (int)(LISTED ? l / n_qt_grid : b % (uint32_t)a.n_split);
     if (qt >= n_qt) return;
     const int64_t q0 = qt * kScoreTileQueries;
     if ((a.listed && list_tile((sq.pos0 + q0) / a.block_size, a.topk)) != LISTED) return;
@@ -1052,115 +1063,180 @@ __device__ __forceinline__ int block_scan256(int v, int* part, int& total) {
     return before + incl - v;
 }
 
-// Listed rows: the top k from the candidate lists.  The segments' lists are
-// streamed into an LDS pool in block order.  While the threshold is still
-// tau every listed entry passes, so 256 segments at a time go in whole (one
-// thread per segment, offsets from one workgroup scan of the counts).
-// Otherwise -- or when those 256 would overflow the pool -- they go 64 at a
-// time with every entry tested (four threads per segment); a step that would
-// overflow the pool first cuts it to its top k and raises the threshold to
-// the k-th key, as the long-row select does (rows whose scores tie at the
-// threshold can list many more than k entries).  The pool is then selected
-// exactly.  A row whose lists cannot give the exact answer -- a
-// segment that dropped entries, or fewer than k entries (the threshold was
-// above the k-th score) -- is appended to the launch's failed rows instead,
-// to be scored again in full.
+// Listed rows: the top k from the candidate lists.  Thread i takes the
+// contiguous segments [i*spt, (i+1)*spt) of the row, reads their counts, and one workgroup scan gives each thread the offset
+// of its entries in block order.  Then:
+//  * the row's entries fit the LDS pool: each thread copies its entries
+//    there (several loads in flight), and the pool is selected exactly;
+//  * they do not (scores tied at the threshold tau: a row whose indexer
+//    weights are all negative scores 0 on every block whose four dot
+//    products are <= 0, and its tau is that 0): the entries are streamed
+//    again, counting the keys > tau.  With at least k of them (and no more
+//    than the pool holds) only those go to the pool and are selected; with
+//    fewer, the answer is every key > tau plus the first keys == tau in
+//    block order, written straight to the output in block order.
+// A row whose lists cannot give the exact answer -- a segment that dropped
+// entries, fewer than k entries (tau was above the k-th score), or more
+// than the pool holds above tau -- is appended to the launch's failed rows
+// instead, to be scored again in full.
+// f(entry) for the entries of segments [s0, s1), in block order.  A
+// segment's count and its first 8 entries (two 16-byte loads per 4 entries;
+// a segment owns all kSegCap slots, so reading past its count stays inside
+// its list) are loaded together, the next segment's while this one's are
+// used; longer segments take their remaining entries 8 at a time.
+template <class F>
+__device__ __forceinline__ void list_entries(const uint32_t* krow, const uint2* lists, int s0, int s1, F&& f) {
+    if (s0 >= s1) return;
+    int c_nx = (int)krow[s0];
+    uint4 e_nx[4];
+#pragma unroll
+    for (int x = 0; x < 4; ++x) e_nx[x] = ((const uint4*)(lists + (int64_t)s0 * kSegCap))[x];
+    for (int sg = s0; sg < s1; ++sg) {
+        const int c = c_nx < kSegCap ? c_nx : kSegCap;
+        uint4 e[4];
+#pragma unroll
+        for (int x = 0; x < 4; ++x) e[x] = e_nx[x];
+        if (sg + 1 < s1) {
+            c_nx = (int)krow[sg + 1];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) e_nx[x] = ((const uint4*)(lists + (int64_t)(sg + 1) * kSegCap))[x];
+        }
+#pragma unroll
+        for (int x = 0; x < 4; ++x) {
+            if (2 * x < c) f(make_uint2(e[x].x, e[x].y));
+            if (2 * x + 1 < c) f(make_uint2(e[x].z, e[x].w));
+        }
+        for (int e0 = 8; e0 < c; e0 += 8) {
+            const uint4* l = (const uint4*)(lists + (int64_t)sg * kSegCap + e0);
+            uint4 r[4];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) r[x] = l[x];
+#pragma unroll
+            for (int x = 0; x < 4; ++x) {
+                if (e0 + 2 * x < c) f(make_uint2(r[x].x, r[x].y));
+                if (e0 + 2 * x + 1 < c) f(make_uint2(r[x].z, r[x].w));
+            }
+        }
+    }
+}
+
 __global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, IndexArgs a) {
     extern __shared__ uint32_t lds[];            // keys [cap], block ids [cap]
     __shared__ SelectShared<4> sh;
     __shared__ int part[4];
-    __shared__ int s_bad;
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = blockIdx.x / kGroups;
     const int g = blockIdx.x % kGroups;
     if (qi >= sq.n_q || !listed_row(sq, qi, a)) return;
     const int K = a.topk;
     const int cap = list_capacity(K);
-    static_assert(64 * kSegCap <= 16384 - 3072 && 64 * kSegCap <= 8192 - 1024,
-                  "a step of 64 full segments fits the pool after a cut to k");
     const int n = (int)((sq.pos0 + qi) / a.block_size);
     const int nseg = (n + kSegBlocks - 1) / kSegBlocks;
     const uint32_t* krow = a.part_key + ((sq.ws_row + qi) * kGroups + g) * a.key_stride;
+    const uint2* lists = (const uint2*)(krow + a.list_off);
     uint32_t* ckeys = lds;
     int32_t* cidx = (int32_t*)(lds + cap);
     const int tid = threadIdx.x;
-    const int sl = tid >> 2, quarter = tid & 3;  // segment of the step, a quarter of its slots
-    if (tid == 0) s_bad = 0;
-    __syncthreads();
-    uint32_t thr = krow[a.tau_off];
-    bool strict = false;        // accept key > thr (after a cut) or key >= thr
-    int pool = 0;
-    for (int chunk = 0; chunk < nseg; chunk += 256) {
-        if (!strict) {
-            const int sg = chunk + tid;
-            const int c = sg < nseg ? (int)krow[sg] : 0;
-            if (c > kSegCap) s_bad = 1;
-            const int cc = c < kSegCap ? c : kSegCap;
-            int tot;
-            const int off = pool + block_scan256(cc, part, tot);
-            if (pool + tot <= cap) {                 // workgroup-uniform
-                const uint2* lst = (const uint2*)(krow + a.list_off + (int64_t)(sg < nseg ? sg : 0) * (2 * kSegCap));
-                for (int e = 0; e < cc; ++e) {
-                    const uint2 kv = lst[e];
-                    ckeys[off + e] = kv.x;
-                    cidx[off + e] = (int32_t)kv.y;
-                }
-                pool += tot;
-                __syncthreads();
-                continue;
+    // contiguous runs of segments per thread: one, or a multiple of 4 (the
+    // counts then come as 16-byte loads; counts past the row's last segment
+    // lie inside its key row and are masked)
+    const int spt0 = (nseg + 255) / 256;
+    const int spt = spt0 == 1 ? 1 : (spt0 + 3) / 4 * 4;
+    const int s0 = tid * spt;
+    const int s1 = s0 + spt < nseg ? s0 + spt : nseg;
+    const int64_t rg = (sq.q_offset + qi) * kGroups + g;
+    int32_t* sel = a.sel + rg * K;
+    float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
+
+    // the thread's entry count
+    int mine = 0, bad = 0;
+    if (spt == 1) {
+        const int c = s0 < nseg ? (int)krow[s0] : 0;
+        bad = c > kSegCap;
+        mine = c < kSegCap ? c : kSegCap;
+    } else {
+        for (int u = 0; u < spt; u += 4) {
+            const uint4 c4 = *(const uint4*)(krow + s0 + u);
+            const int cc[4] = {(int)c4.x, (int)c4.y, (int)c4.z, (int)c4.w};
+#pragma unroll
+            for (int v = 0; v < 4; ++v) {
+                const int c = s0 + u + v < nseg ? cc[v] : 0;
+                bad |= c > kSegCap;
+                mine += c < kSegCap ? c : kSegCap;
             }
-        }
-        // 64 segments per step, every entry tested
-        for (int base = chunk; base < chunk + 256 && base < nseg; base += 64) {
-            const int sgi = base + sl;
-            const int c = sgi < nseg ? (int)krow[sgi] : 0;
-            if (c > kSegCap) s_bad = 1;
-            const int cc = c < kSegCap ? c : kSegCap;
-            const uint2* lst = (const uint2*)(krow + a.list_off + (int64_t)(sgi < nseg ? sgi : 0) * (2 * kSegCap));
-            uint2 ev[16];
-    #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                const int e = 16 * quarter + u;
-                ev[u] = e < cc ? lst[e] : make_uint2(0u, 0u);
-            }
-            int off = 0, tot = 0;
-    #pragma unroll 1
-            for (int attempt = 0; attempt < 2; ++attempt) {
-                int mine = 0;
-    #pragma unroll
-                for (int u = 0; u < 16; ++u)
-                    mine += 16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr);
-                off = pool + block_scan256(mine, part, tot);
-                if (pool + tot <= cap) break;            // workgroup-uniform
-                thr = compact_to_topk(ckeys, cidx, pool, K, sh);
-                pool = K;
-                strict = true;
-            }
-    #pragma unroll
-            for (int u = 0; u < 16; ++u) {
-                if (16 * quarter + u < cc && (strict ? ev[u].x > thr : ev[u].x >= thr)) {
-                    ckeys[off] = ev[u].x;
-                    cidx[off] = (int32_t)ev[u].y;
-                    ++off;
-                }
-            }
-            pool += tot;
-            __syncthreads();
         }
     }
-    if (s_bad || pool < K) {
+    int total;
+    const int off = block_scan256(mine, part, total);
+    bad = __syncthreads_or(bad);
+    auto fail = [&]() {
         if (tid == 0) {
             const uint32_t slot = atomicAdd(&a.ctl[0], 1u);
             a.ctl[1 + slot] = ((uint32_t)qi << 8) | ((uint32_t)blockIdx.y << 2) | (uint32_t)g;
         }
+    };
+    if (bad || total < K) {
+        fail();
         return;
     }
     uint32_t prefix, pmask;
     int krem;
-    radix_kth(ckeys, pool, K, sh, prefix, pmask, krem);
-    const int64_t rg = (sq.q_offset + qi) * kGroups + g;
-    select_ordered_output(ckeys, cidx, pool, prefix, pmask, krem, a.sel + rg * K,
-                          a.sel_scores ? a.sel_scores + rg * K : nullptr, sh);
+    if (total <= cap) {
+        int o = off;
+        list_entries(krow, lists, s0, s1, [&](uint2 kv) {
+            ckeys[o] = kv.x;
+            cidx[o] = (int32_t)kv.y;
+            ++o;
+        });
+        __syncthreads();
+        radix_kth(ckeys, total, K, sh, prefix, pmask, krem);
+        select_ordered_output(ckeys, cidx, total, prefix, pmask, krem, sel, ssc, sh);
+        return;
+    }
+
+    // more entries than the pool holds: the keys strictly above tau
+    const uint32_t thr = krow[a.tau_off];
+    int gt = 0;
+    list_entries(krow, lists, s0, s1, [&](uint2 kv) { gt += kv.x > thr; });
+    int n_gt;
+    const int gt_off = block_scan256(gt, part, n_gt);
+    if (n_gt >= K) {
+        if (n_gt > cap) {
+            fail();
+            return;
+        }
+        int o = gt_off;
+        list_entries(krow, lists, s0, s1, [&](uint2 kv) {
+            if (kv.x > thr) {
+                ckeys[o] = kv.x;
+                cidx[o] = (int32_t)kv.y;
+                ++o;
+            }
+        });
+        __syncthreads();
+        radix_kth(ckeys, n_gt, K, sh, prefix, pmask, krem);
+        select_ordered_output(ckeys, cidx, n_gt, prefix, pmask, krem, sel, ssc, sh);
+        return;
+    }
+    // every key > tau and the first K - n_gt keys == tau, in block order: an
+    // entry's output slot is the number of kept entries before it
+    const int quota = K - n_gt;
+    int gt_run = gt_off, eq_run = off - gt_off;   // every listed key is >= tau
+    list_entries(krow, lists, s0, s1, [&](uint2 kv) {
+        if (kv.x > thr) {
+            const int pos = gt_run + (eq_run < quota ? eq_run : quota);
+            sel[pos] = (int32_t)kv.y;
+            if (ssc) ssc[pos] = key_score(kv.x);
+            ++gt_run;
+        } else {
+            if (eq_run < quota) {
+                const int pos = gt_run + eq_run;
+                sel[pos] = (int32_t)kv.y;
+                if (ssc) ssc[pos] = key_score(kv.x);
+            }
+            ++eq_run;
+        }
+    });
 }
 
 // Failed listed rows, again in full: every key of the row's query (all four

@@ -146,3 +146,61 @@ def test_listed_threshold_above_kth_falls_back_exactly():
     assert (ssc[:, :, ~is_hot] == 0.0).all()
     hs = ssc[:, :, is_hot]
     assert (hs > 100.0).all() and (hs == hs[0, 0, 0]).all()
+
+
+@pytest.mark.parametrize("w0", [-1.0, 1.0])
+def test_listed_rows_with_tied_mass_above_the_pool(w0):
+    """Listed rows whose entries at the threshold outnumber the LDS pool.
+
+    Every query's indexer heads are one-hot on dims 40..43 (past the rotary
+    span), so a block's score is sum_i w_i * c * relu(store[r, 40 + i]) with
+    c = bf16(RMSNorm(one-hot)).  Blocks r with r % 256 < 40 have all four
+    dims <= 0 (score exactly 0: 40 per segment, about 9,400 per row, more
+    than the 8,192-entry pool, none of the 256-block segment lists
+    overflowing); 300 blocks carry a distinct positive value on dim 40 and
+    the rest a positive value on dim 41.  With w = (-1, -1, -1, -1) no score
+    is positive and the answer is the first k zero-score blocks (the tie
+    rule); with w = (+1, -1, -1, -1) the 300 positive scores are the only
+    ones above the zero threshold and the answer is the k largest of them.
+    """
+    n_q, pos0, B, K = 1100, 60000, 1, 256
+    log("case tied mass", w0)
+    rng = np.random.default_rng(17)
+    cache = pos0 + n_q
+    n_blocks = cache // B
+    store = -np.abs(rng.standard_normal((n_blocks, 128))).astype(np.float32)
+    store[:, :40] = rng.standard_normal((n_blocks, 40))
+    store[:, 44:] = rng.standard_normal((n_blocks, 84))
+    r = np.arange(n_blocks)
+    zero = r % 256 < 40
+    cand = np.flatnonzero(~zero & (r < pos0))
+    pos = np.sort(rng.choice(cand, 300, replace=False))
+    # distinct bf16 values: consecutive bit patterns from 1.0 upwards
+    vals = (np.uint32(0x3F80) + rng.permutation(300).astype(np.uint32)) << 16
+    store[pos, 40] = vals.view(np.float32)
+    neg = ~zero
+    neg[pos] = False
+    store[neg, 41] = np.abs(rng.standard_normal(int(neg.sum()))) + 0.25
+    store_d = torch.from_numpy(store).to(torch.bfloat16).cuda()
+    q = np.zeros((n_q, 4, 4, 128), dtype=np.float32)
+    for i in range(4):
+        q[:, :, i, 40 + i] = 1.0
+    q_idx = torch.from_numpy(q).to(torch.bfloat16).cuda()
+    w = torch.tensor([w0, -1.0, -1.0, -1.0], dtype=torch.float32).repeat(n_q, 4, 1).cuda()
+    cfg = sg.config(block_size=B, topk_blocks=K)
+    seqs = [sg.seq(n_q, pos0=pos0, kv_capacity=cache, store_capacity=n_blocks)]
+    sel, ssc = _run_index(cfg, seqs, n_q, q_idx, w, store_d)
+    c = float(torch.tensor(1.0 / np.sqrt(1.0 / 128 + 1e-6)).to(torch.bfloat16))
+    if w0 < 0:
+        want = np.flatnonzero(zero)[:K]
+        want_s = np.zeros(K)
+    else:
+        v = store_d[pos, 40].float().cpu().numpy()
+        top = np.sort(pos[np.argsort(-v, kind="stable")[:K]])
+        want = top
+        want_s = c * store_d[top, 40].float().cpu().numpy()
+    for row in (0, 1, 517, n_q - 1):
+        for g in range(4):
+            assert np.array_equal(sel[row, g], want), (row, g)
+            assert np.allclose(ssc[row, g], want_s, rtol=1e-6, atol=0.0), (row, g)
+    assert (sel == want[None, None, :]).all()
