@@ -1129,7 +1129,7 @@ __global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, I
     const int g = blockIdx.x % kGroups;
     if (qi >= sq.n_q || !listed_row(sq, qi, a)) return;
     const int K = a.topk;
-    const int cap = list_capacity(K);
+    const int cap = a.list_cap;
     const int n = (int)((sq.pos0 + qi) / a.block_size);
     const int nseg = (n + kSegBlocks - 1) / kSegBlocks;
     const uint32_t* krow = a.part_key + ((sq.ws_row + qi) * kGroups + g) * a.key_stride;
@@ -1370,12 +1370,14 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
     // which kinds of tiles the launch holds (listed: long rows, candidate
     // lists; keyed: every key written)
     bool any_listed = false, any_keyed = false, keyed_long = false;
+    int64_t n0_listed = 0;        // the largest first-query candidate count of a listed tile
     for (int i = 0; i < seqs.n; ++i) {
         const DevSeq& d = seqs.s[i];
         for (int64_t q0 = 0; q0 < d.n_q; q0 += kScoreTileQueries) {
             const int64_t n0 = (d.pos0 + q0) / a.block_size;
             const bool l = a.listed && list_tile(n0, a.topk);
             any_listed |= l;
+            if (l && n0 > n0_listed) n0_listed = n0;
             any_keyed |= !l;
             const int64_t q1 = q0 + kScoreTileQueries < d.n_q ? q0 + kScoreTileQueries : d.n_q;
             keyed_long |= !l && (d.pos0 + q1 - 1) / a.block_size > kSelectStageKeys;
@@ -1404,11 +1406,13 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
     }
     if (any_keyed && (e = launch_select(seqs, max_nq, a, stream, keyed_long)) != hipSuccess) return e;
     if (!any_listed) return hipSuccess;
-    const size_t lds_l = (size_t)list_capacity(a.topk) * 8;
+    IndexArgs al = a;
+    al.list_cap = list_capacity(n0_listed, a.topk);
+    const size_t lds_l = (size_t)al.list_cap * 8;
     if ((e = hipFuncSetAttribute((const void*)index_list_select_kernel,
                                  hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_l)) != hipSuccess)
         return e;
-    hipLaunchKernelGGL(index_list_select_kernel, rows_grid, dim3(256), lds_l, stream, seqs, a);
+    hipLaunchKernelGGL(index_list_select_kernel, rows_grid, dim3(256), lds_l, stream, seqs, al);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // rows whose lists failed (usually none): scored again, then selected
     // from their keys; grid-stride loops over the count the device holds

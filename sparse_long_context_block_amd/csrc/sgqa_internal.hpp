@@ -87,6 +87,7 @@ struct IndexArgs {
     int32_t cap;                // per-row LDS buffer capacity C (fused kernel)
     int32_t n_split;
     int32_t split_blocks;       // candidate blocks per split (multiple of 16)
+    int32_t list_cap;           // listed rows: entries of the LDS pool (list_capacity)
     float eps;
     double theta[kRopeDim / 2]; // rotary frequencies base^(-2j/32)
 };
@@ -156,9 +157,20 @@ __host__ __device__ inline int list_rank(int64_t n0, int k) {
     const double j = ceil(list_margin(n0, k) * k * S / (double)n0);
     return j < 1.0 ? 1 : (j > S ? S : (int)j);
 }
-// entries of a listed row's LDS pool (8 B each): k plus a step of 64 full
-// segments, with room to spare
-__host__ __device__ constexpr int list_capacity(int k) { return k < 1024 ? 8192 : 16384; }
+// entries of the LDS pool (8 B each) of listed rows whose tiles start at
+// most n0 candidates in: the expected list length (j/S of the row, about
+// m k entries) plus five times its spread (the share of a row above the
+// sample's j-th largest key has relative spread 1/sqrt(j)), at least k +
+// 1024, at most 16384.  A row with more entries takes the list select's
+// other paths.
+__host__ __device__ inline int list_capacity(int64_t n0, int k) {
+    const int j = list_rank(n0, k);
+    const double e = (double)j * (double)n0 / (double)list_sample(n0);
+    int c = (int)((e * (1.0 + 5.0 / sqrt((double)j)) + 1023.0) / 1024.0) * 1024;
+    const int lo = (k + 1024 + 1023) / 1024 * 1024;
+    c = c < lo ? lo : c;
+    return c > 16384 ? 16384 : c;
+}
 
 // Main-path Q/K producer: RMSNorm over each head's D dims (one gamma per
 // tensor, shared by the heads), the rotary span [0, rope_dim) at the token's
