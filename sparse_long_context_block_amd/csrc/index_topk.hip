@@ -932,6 +932,98 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
     select_ordered_output(ckeys, cidx, c, prefix, pmask, krem, sel, ssc, sh);
 }
 
+// Rows of at most kWaveSelectKeys candidates, one wavefront each: the row's
+// keys sit in registers (lane l holds keys l, l + 64, ...); the k-th largest
+// key v comes from four 8-bit digit passes over a wavefront-private LDS
+// histogram (bins scanned from the top by a wavefront prefix sum), and the
+// output goes out in block order from ballots -- no workgroup barrier.
+constexpr int kWaveSelectKeys = 1024;
+
+__global__ __launch_bounds__(256) void index_select_wave_kernel(SeqTable seqs, IndexArgs a) {
+    constexpr int KPL = kWaveSelectKeys / 64;
+    __shared__ uint32_t hist[4][256];
+    const DevSeq sq = seqs.s[blockIdx.y];
+    const int64_t qi = blockIdx.x;
+    const int g = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (qi >= sq.n_q) return;
+    const int n = (int)((sq.pos0 + qi) / a.block_size);
+    if (n > kWaveSelectKeys) return;
+    const int K = a.topk;
+    const int64_t rg = (sq.q_offset + qi) * kGroups + g;
+    int32_t* sel = a.sel + rg * K;
+    float* ssc = a.sel_scores ? a.sel_scores + rg * K : nullptr;
+    const uint32_t* gkeys = a.part_key + ((sq.ws_row + qi) * kGroups + g) * a.key_stride;
+    if (n <= K) {
+        for (int jj = lane; jj < K; jj += 64) {
+            sel[jj] = jj < n ? jj : -1;
+            if (ssc) ssc[jj] = jj < n ? key_score(gkeys[jj]) : 0.0f;
+        }
+        return;
+    }
+    uint32_t key[KPL];
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) key[u] = 64 * u + lane < n ? gkeys[64 * u + lane] : 0u;
+    uint32_t* h = hist[g];
+    uint32_t pref = 0u, pmask = 0u;
+    int need = K;
+#pragma unroll 1
+    for (int shift = 24; shift >= 0; shift -= 8) {
+        wave_lds_sync();                               // the previous pass's bin reads are done
+#pragma unroll
+        for (int j = 0; j < 4; ++j) h[lane + 64 * j] = 0u;
+        wave_lds_sync();
+#pragma unroll
+        for (int u = 0; u < KPL; ++u)
+            if (64 * u + lane < n && (key[u] & pmask) == pref) atomicAdd(&h[(key[u] >> shift) & 255u], 1u);
+        wave_lds_sync();
+        // lane l holds bins 255 - 4l - j; counts above a bin by a prefix sum
+        uint32_t c[4], tot = 0;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            c[j] = h[255 - 4 * lane - j];
+            tot += c[j];
+        }
+        uint32_t incl = tot;
+#pragma unroll
+        for (int o = 1; o < 64; o <<= 1) {
+            const uint32_t up = __shfl_up(incl, o, 64);
+            if (lane >= o) incl += up;
+        }
+        uint32_t above = incl - tot, above_found = 0;
+        int found = -1;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            if (found < 0 && c[j] > 0 && above + c[j] >= (uint32_t)need) {
+                found = 255 - 4 * lane - j;
+                above_found = above;
+            }
+            above += c[j];
+        }
+        const int src = (int)__builtin_ctzll(__ballot(found >= 0));
+        const int digit = __shfl(found, src, 64);
+        need -= (int)__shfl(above_found, src, 64);
+        pref |= (uint32_t)digit << shift;
+        pmask |= 255u << shift;
+    }
+    // keep every key > v and the first `need` keys == v, in block order
+    int out = 0, eq_seen = 0;
+#pragma unroll
+    for (int u = 0; u < KPL; ++u) {
+        const bool ok = 64 * u + lane < n;
+        const bool eq = ok && key[u] == pref;
+        const uint64_t em = __ballot(eq);
+        const bool keep = ok && (key[u] > pref || (eq && eq_seen + (int)lanes_below(em) < need));
+        const uint64_t km = __ballot(keep);
+        if (keep) {
+            const int pos = out + (int)lanes_below(km);
+            sel[pos] = 64 * u + lane;
+            if (ssc) ssc[pos] = key_score(key[u]);
+        }
+        out += __popcll(km);
+        eq_seen += __popcll(em);
+    }
+}
+
 // a listed row of a tiled call (its key row holds candidate lists)
 __device__ __forceinline__ bool listed_row(const DevSeq& sq, int64_t qi, const IndexArgs& a) {
     return a.listed && list_tile((sq.pos0 + (qi & ~(int64_t)(kScoreTileQueries - 1))) / a.block_size, a.topk);
@@ -947,6 +1039,7 @@ __global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, In
     if (qi >= sq.n_q) return;
     const int64_t n = (sq.pos0 + qi) / a.block_size;
     if ((n > kSelectStageKeys) != LONG) return;
+    if (!LONG && n <= kWaveSelectKeys) return;     // one wavefront per row
     if (LONG && listed_row(sq, qi, a)) return;    // selected from its lists
     select_row<LONG, NW>(sq, qi, g, a, lds_keys, sh);
 }
@@ -1314,15 +1407,23 @@ static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const Inde
     const int64_t max_b = a.key_stride;
     dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
     // short rows (skipped when every sequence's first query already has a
-    // long row): the staged row
-    int64_t min_b = INT64_MAX, rows = 0;
+    // long row): a wavefront per row up to kWaveSelectKeys keys, then the
+    // staged row
+    int64_t min_b = INT64_MAX, max_rows_b = 0, rows = 0;
     for (int i = 0; i < seqs.n; ++i) {
         const int64_t b = seqs.s[i].pos0 / a.block_size;
+        const int64_t bl = (seqs.s[i].pos0 + seqs.s[i].n_q - 1) / a.block_size;   // the last query's
         min_b = b < min_b ? b : min_b;
+        max_rows_b = seqs.s[i].n_q > 0 && bl > max_rows_b ? bl : max_rows_b;
         rows += seqs.s[i].n_q * kGroups;
     }
     hipError_t e = hipSuccess;
-    if (min_b <= kSelectStageKeys) {
+    if (min_b <= kWaveSelectKeys) {
+        hipLaunchKernelGGL(index_select_wave_kernel, dim3((unsigned)max_nq, (unsigned)seqs.n), dim3(256), 0,
+                           stream, seqs, a);
+        if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    if (min_b <= kSelectStageKeys && max_rows_b > kWaveSelectKeys) {
         const size_t lds_s = (size_t)(max_b < kSelectStageKeys ? max_b : kSelectStageKeys) * sizeof(uint32_t);
         e = hipFuncSetAttribute((const void*)index_select_kernel<false, 4>,
                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
