@@ -370,34 +370,37 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
     const float4 wv = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
     const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
     uint32_t* keys = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
-    uint4 b0[4], b1[4];
+    // 16-block store tiles, kDepth of them in flight (a ring refilled kDepth
+    // tiles ahead as each is used)
+    constexpr int kDepth = 4;
+    uint4 b[kDepth][4];
     auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * kIdxDim; };
-    {
-        const int64_t o = row_of(r_lo);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b0[kk] = load16(store + o + 32 * kk);
-    }
-    if (r_lo + 16 < r_hi) {
-        const int64_t o = row_of(r_lo + 16);
+    for (int d = 0; d < kDepth; ++d)
+        if (r_lo + 16 * d < r_hi) {
+            const int64_t o = row_of(r_lo + 16 * d);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
-    }
-    for (int64_t r0 = r_lo; r0 < r_hi; r0 += 16) {
-        f32x4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], as_bf16x8(b0[kk]), acc);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b0[kk] = b1[kk];
-        if (r0 + 32 < r_hi) {
-            const int64_t o = row_of(r0 + 32);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
+            for (int kk = 0; kk < 4; ++kk) b[d][kk] = load16(store + o + 32 * kk);
         }
-        float s = wv.x * fmaxf(acc[0], 0.f);
-        s += wv.y * fmaxf(acc[1], 0.f);
-        s += wv.z * fmaxf(acc[2], 0.f);
-        s += wv.w * fmaxf(acc[3], 0.f);
-        if (r0 + m < r_hi) keys[r0 + m] = score_key(s);
+    for (int64_t r00 = r_lo; r00 < r_hi; r00 += 16 * kDepth) {
+#pragma unroll
+        for (int d = 0; d < kDepth; ++d) {
+            const int64_t r0 = r00 + 16 * d;
+            if (r0 >= r_hi) break;                     // wavefront-uniform
+            f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], as_bf16x8(b[d][kk]), acc);
+            if (r0 + 16 * kDepth < r_hi) {
+                const int64_t o = row_of(r0 + 16 * kDepth);
+#pragma unroll
+                for (int kk = 0; kk < 4; ++kk) b[d][kk] = load16(store + o + 32 * kk);
+            }
+            float s = wv.x * fmaxf(acc[0], 0.f);
+            s += wv.y * fmaxf(acc[1], 0.f);
+            s += wv.z * fmaxf(acc[2], 0.f);
+            s += wv.w * fmaxf(acc[3], 0.f);
+            if (r0 + m < r_hi) keys[r0 + m] = score_key(s);
+        }
     }
 }
 

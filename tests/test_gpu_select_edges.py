@@ -5,7 +5,8 @@ highest scores among blocks r < floor(t/B), equal scores to the lower block
 id), so no oracle run is needed:
 
 * every score equal (indexer weights zero): every row keeps blocks
-  0..min(n, k)-1.  Long rows (more than 4096 candidates) then start from a
+  0..min(n, k)-1 -- rows of up to 1024 candidates in the one-wavefront
+  select, longer ones staged in LDS or sampled.  Long rows (more than 4096 candidates) then start from a
   threshold every key passes, so the candidate list overflows and is cut to
   its top k, repeatedly -- the compaction path, with all keys tied;
 * a row whose only positive scores sit at positions the long-row select
@@ -49,6 +50,8 @@ def _run_index(cfg, seqs, n_rows, q_idx, w, store):
     (3, 300000, 8, 2048),         # decode-sized, several queries, k = 2048
     (2, 40000, 1, 512),           # decode-sized, k <= 1024: 16-wavefront select
     (1100, 300000, 8, 512),       # tiled call, listed rows: every segment's list overflows
+    (1100, 4000, 8, 64),          # tiled call, rows of 500..637 candidates: one wavefront per row
+    (1100, 0, 1, 64),             # rows of 0..1099 candidates: per-wavefront rows, then staged
 ])
 def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
     log("case equal scores", n_q, pos0, B, K)
