@@ -244,12 +244,22 @@ __device__ __forceinline__ void union_vector(UnionState& st, int ti, int n_tiles
     const int64_t lim64 = ln.tq - tok0;
     const int lim = ln.q_ok && live ? (lim64 > 64 ? 64 : (int)lim64) : -1;
     float tmax = -INFINITY;
+    if (__ballot(lim < kTileTok - 1) == 0) {
+        // no lane's query lies inside the tile: only the block bits mask
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-        const int mm = 8 * (r >> 2) + 4 * ln.hgrp + (r & 3);
-        const bool valid = ((tb >> (mm >> LOG2B)) & 1u) && mm <= lim;
-        st.s[r] = valid ? st.s[r] : -INFINITY;
-        tmax = fmaxf(tmax, st.s[r]);
+        for (int r = 0; r < 16; ++r) {
+            const int mm = 8 * (r >> 2) + 4 * ln.hgrp + (r & 3);
+            st.s[r] = (tb >> (mm >> LOG2B)) & 1u ? st.s[r] : -INFINITY;
+            tmax = fmaxf(tmax, st.s[r]);
+        }
+    } else {
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+            const int mm = 8 * (r >> 2) + 4 * ln.hgrp + (r & 3);
+            const bool valid = ((tb >> (mm >> LOG2B)) & 1u) && mm <= lim;
+            st.s[r] = valid ? st.s[r] : -INFINITY;
+            tmax = fmaxf(tmax, st.s[r]);
+        }
     }
     tmax = xor32_max(tmax);
     const float sl2 = ln.sl2;
