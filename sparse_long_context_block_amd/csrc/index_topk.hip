@@ -416,6 +416,9 @@ __global__ __launch_bounds__(256) void index_qfrag_kernel(SeqTable seqs, IndexAr
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (qi >= sq.n_q) return;
+    // a row of at most k candidates takes all of them: without score or q_hat
+    // outputs nothing reads its fragments
+    if (!a.sel_scores && !a.q_hat_out && (sq.pos0 + qi) / a.block_size <= a.topk) return;
     const int lane = lane_id();
     bf16x8 af[4];
     index_query_fragments(a, sq.q_offset + qi, sq.pos0 + qi, lane >> 4, lane & 15, true, af);
@@ -468,6 +471,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
     const int64_t q0 = qt * kScoreTileQueries;
     if ((a.listed && list_tile((sq.pos0 + q0) / a.block_size, a.topk)) != LISTED) return;
     const int n_valid = (int)(sq.n_q - q0 < kScoreTileQueries ? sq.n_q - q0 : kScoreTileQueries);
+    // every row of the tile has at most k candidates and takes them all: the
+    // keys are read only for score outputs
+    if (!a.sel_scores && (sq.pos0 + q0 + n_valid - 1) / a.block_size <= a.topk) return;
     const int64_t nb_max = (sq.pos0 + q0 + n_valid - 1) / a.block_size;
     const int64_t r_lo = (int64_t)split * a.split_blocks;
     const int64_t r_hi = nb_max < r_lo + a.split_blocks ? nb_max : r_lo + a.split_blocks;
