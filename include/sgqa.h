@@ -127,7 +127,7 @@ enum {
  * or 0 with sgqa_last_error() set when the arguments are invalid.  What it
  * holds: for SGQA_OP_INDEX_TOPK, the 4-byte score keys of every candidate of
  * the queries processed at once -- calls of 1024+ queries work in passes of
- * at most 1 GiB of keys and also hold each query's prepared indexer rows
+ * at most 4 GiB of keys and also hold each query's prepared indexer rows
  * (4 KiB per query of a pass), smaller calls with long histories keep the queries
  * of 64 consecutive seqs[] entries at a time (at most 1 GiB, else they need
  * none); for SGQA_OP_SPARSE_ATTN, the per-split partial outputs of calls

@@ -145,8 +145,11 @@ constexpr size_t kQueryFragBytes = (size_t)sgqa::kGroups * sgqa::kIdxHeads * sgq
 constexpr int64_t kTiledMaxStride = ((int64_t)1 << 32) / (16 * sgqa::kGroups * 4) - 64;
 
 // key workspace of the tiled mode: query rows are processed in passes whose
-// keys (4 B per row, group and candidate) fit this budget
-constexpr size_t kTiledKeyBudget = (size_t)1 << 30;
+// keys (4 B per row, group and candidate) fit this budget (4 GiB: a 1M-token
+// prefill at B = 1 then runs 192 queries per launch instead of 48, so the
+// launches' fixed costs -- sample, threshold, list select, rescue -- are paid
+// a quarter as often; 8 and 16 GiB measured no faster)
+constexpr size_t kTiledKeyBudget = (size_t)1 << 32;
 constexpr int kTiledSplitBlocks = 512;
 
 struct AttnPlan {

@@ -59,8 +59,8 @@ def test_chunk_on_existing_cache_unaligned():
 
 def test_tiled_index_passes_over_ragged_sequences():
     # 2533 queries at B = 1 over histories up to 180K tokens: the tiled
-    # indexer runs in seven launches of at most 368 queries (one pass over
-    # its 1 GiB key workspace each) that cut through the sequences
+    # indexer runs in two launches of at most 1472 queries (one pass over
+    # its 4 GiB key workspace each) that cut through the sequences
     _run_and_check("multi_b1_passes", n_rows=24, check_all_store=False)
 
 
