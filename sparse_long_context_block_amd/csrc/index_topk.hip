@@ -619,7 +619,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
 // (n <= kSelectStageKeys) are staged in LDS and selected there.  Long rows
 // first bound v from below with a sample (up to 2048 keys, groups of 16
 // consecutive keys spread over the row): the sample's j-th largest key tau,
-// j chosen so that about 3k keys are expected at or above it.  One
+// j chosen so that about m k keys are expected at or above it (m = 1 +
+// 5 / sqrt(k S / n), as for the candidate lists).  One
 // pass over the row then streams every key >= tau, with its block id, into
 // an LDS candidate list kept in block order; when a step would overflow it
 // (the sample misjudged a row whose high keys cluster), the list is cut to
@@ -631,13 +632,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
 constexpr int kSelectStageKeys = 4096;
 constexpr int kSelectSampleMax = 2048;     // sample keys (LDS words) for long rows
 
-__host__ __device__ constexpr int select_region(int k) { return ((k < 512 ? 512 : k) + 63) / 64 * 64; }
-// candidate list capacity: at least the 3k entries expected above the
-// sampled threshold plus a margin, and k plus one step of 1024 keys per
-// wavefront
-__host__ __device__ constexpr int select_capacity(int k, int nw) {
-    return 4 * select_region(k) > k + 1024 * nw ? 4 * select_region(k) : k + 1024 * nw;
-}
+// candidate list capacity: k plus one step of 1024 keys per wavefront (a
+// step always fits after a cut to the top k); the m k entries expected above
+// the sampled threshold (m from 1.2 to 3.5) fit it without a cut on all but
+// the longest rows
+__host__ __device__ constexpr int select_capacity(int k, int nw) { return k + 1024 * nw; }
 
 // shared state of a select workgroup of NW wavefronts
 template <int NW>
@@ -853,7 +852,6 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
 
     // ---- threshold tau: the j-th largest of a sample of S keys taken as
     //      S/16 groups of 16 consecutive keys spread over the row ----
-    const int region = select_region(K);
     const int smax = kSelectSampleMax < n / 4 ? kSelectSampleMax : n / 4;
     const int S = smax / 16 * 16;
     const int ngrp = S / 16;
@@ -863,7 +861,11 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
         lds_keys[i] = gkeys[start + (i & 15)];
     }
     __syncthreads();
-    const int64_t jt = ((int64_t)3 * K * S + n - 1) / n;
+    // j such that about m k keys are expected at or above tau, m = 1 +
+    // 5 / sqrt(k S / n): the sample's estimate of a share has relative spread
+    // 1 / sqrt(j), so fewer than k keys pass only about five spreads out
+    const double ks = (double)K * S / (double)n;
+    const int64_t jt = (int64_t)ceil((1.0 + 5.0 / sqrt(ks)) * ks);
     const int j = (int)(jt < 1 ? 1 : (jt > S ? S : jt));
     uint32_t tau, tmask;
     int trem;
