@@ -70,7 +70,9 @@ __global__ __launch_bounds__(256) void qk_prep_kernel(SeqTable seqs, QkPrepArgs 
             rope_cos_sin(sq.pos0 + i0 + tt, exp(-(2.0 * j / a.rope_dim) * a.log_base), &c, &s);
             rot[tt][j] = make_float2(c, s);
         }
-        if (threadIdx.x < kTokensPerBlock) {
+        // cache rows of the group's tokens (slots past the last token stay
+        // unread: their page-table entries may lie past the sequence's)
+        if (threadIdx.x < kTokensPerBlock && i0 + threadIdx.x < sq.n_q) {
             const int64_t t = sq.pos0 + i0 + threadIdx.x;
             crow_s[threadIdx.x] = a.page_table ? paged_row(a.page_table + sq.kv_offset, a.n_pages, t)
                                                : sq.kv_offset + t;
