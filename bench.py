@@ -159,29 +159,40 @@ def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
 # GPU timing
 # ---------------------------------------------------------------------------
 
-def recorded_counters(workload: str, kernel: str):
-    """HBM bytes per launch of `kernel` on `workload` from a committed counter
-    summary under profiles/ (FETCH_SIZE and WRITE_SIZE, calibrated against a
-    device copy), or None when no summary covers that pair or the kernel's
-    source has changed since the counters were taken."""
+def recorded_counters(workload: str, kernels):
+    """HBM bytes per call of the attention kernels `kernels` on `workload`,
+    summed over them, from committed counter summaries under profiles/
+    (FETCH_SIZE and WRITE_SIZE, calibrated against a device copy), or None
+    when a kernel has no summary for that workload or its source has changed
+    since the counters were taken."""
     import glob
     import hashlib
+    recs = {}
     for path in sorted(glob.glob(os.path.join(ROOT, "profiles", "*.md"))):
         rec = {}
         for line in open(path):
-            parts = line.strip().split(": ", 1)
+            line = line.strip()
+            if line.startswith("traffic_workload: ") and rec:
+                recs[(rec.get("traffic_workload"), rec.get("traffic_kernel"))] = rec
+                rec = {}
+            parts = line.split(": ", 1)
             if len(parts) == 2 and parts[0].startswith(("traffic_", "source_")):
                 rec[parts[0]] = parts[1]
-        if rec.get("traffic_workload") != workload or rec.get("traffic_kernel") != kernel:
-            continue
+        if rec:
+            recs[(rec.get("traffic_workload"), rec.get("traffic_kernel"))] = rec
+    total = {"fetch": 0, "write": 0}
+    for kernel in kernels:
+        rec = recs.get((workload, kernel))
+        if rec is None:
+            return None
         src = os.path.join(ROOT, rec.get("source_file", ""))
         if not os.path.isfile(src):
             return None
         if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
             return None
-        return {"fetch": int(rec["traffic_fetch_bytes_per_launch"]),
-                "write": int(rec["traffic_write_bytes_per_launch"])}
-    return None
+        total["fetch"] += int(rec["traffic_fetch_bytes_per_launch"])
+        total["write"] += int(rec["traffic_write_bytes_per_launch"])
+    return total
 
 
 def measured_peaks(stream) -> dict:
@@ -437,6 +448,11 @@ def main() -> int:
                 "kernel": "sparse_attn_kernel + attn_merge_kernel (one sgqa_sparse_attn call)",
                 "algorithmic_bytes_per_launch": wm["attn_gather_bytes"],
                 "launch_ms": k_ms["sparse_attn"]}
+        ctr = (recorded_counters(wl.name, ["sparse_attn_kernel<false>"])
+               if not args.paged and not nb and wl.store_q8 and not wl.loop_steps else None)
+        if ctr:
+            roof["traffic"] = ctr["fetch"] + ctr["write"]
+            roof["reuse"] = wm["attn_gather_bytes"] / ctr["fetch"]
         if peaks:
             roof["measured_peak"] = max(peaks["hbm_copy_GBps"], peaks["hbm_read_GBps"])
             roof["frac_of_measured"] = achieved / roof["measured_peak"]
@@ -451,10 +467,11 @@ def main() -> int:
                      f"queries tiled)")
         # counters were taken on the plain (contiguous, ungated) call that
         # runs one attention kernel
-        ctr_kernel = ("attn_union_kernel<%d, false>" % (wl.block_size.bit_length() - 1)
-                      if dense == wm["queries"] else "sparse_attn_kernel<false>" if dense == 0 else None)
-        ctr = (recorded_counters(wl.name, ctr_kernel)
-               if ctr_kernel and not args.paged and not nb and wl.store_q8 else None)
+        union_k = "attn_union_kernel<%d, false>" % (wl.block_size.bit_length() - 1)
+        ctr_kernels = ([union_k] if dense == wm["queries"] else ["sparse_attn_kernel<false>"] if dense == 0
+                       else [union_k, "sparse_attn_kernel<false>"])
+        ctr = (recorded_counters(wl.name, ctr_kernels)
+               if not args.paged and not nb and wl.store_q8 and not wl.loop_steps else None)
         roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12,
                 "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16_FLOPS / 1e12),
                 "traffic": ctr["fetch"] + ctr["write"] if ctr else None,
