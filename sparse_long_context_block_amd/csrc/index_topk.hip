@@ -648,10 +648,12 @@ struct SelectShared {
 };
 
 // v (as prefix under pmask) and krem of the k-th largest of keys[0..n),
-// 1 <= k <= n.  Called by all 64*NW threads.
+// 1 <= k <= n.  Called by all 64*NW threads.  With stop_bit > 0 only the
+// key bits >= stop_bit are resolved: prefix (its lower bits zero) is then a
+// lower bound of the k-th largest key that at least k keys reach.
 template <int NW>
 __device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared<NW>& sh, uint32_t& prefix,
-                          uint32_t& pmask, int& krem) {
+                          uint32_t& pmask, int& krem, int stop_bit = 0) {
     constexpr int NT = 64 * NW;
     const int tid = threadIdx.x, w = tid >> 6, lane = tid & 63;
     krem = k;
@@ -671,8 +673,8 @@ __device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared<NW>& 
     const int hb = 31 - __builtin_clz(diff);
     pmask = hb == 31 ? 0u : (0xFFFFFFFFu << (hb + 1));
     prefix = k0 & pmask;
-    for (int hi = hb; hi >= 0;) {
-        const int lo = hi >= 7 ? hi - 7 : 0;
+    for (int hi = hb; hi >= stop_bit;) {
+        const int lo = hi - 7 > stop_bit ? hi - 7 : stop_bit;
         const int nbins = 1 << (hi - lo + 1);
         const uint32_t dmask = (uint32_t)nbins - 1u;
         for (int b = lane; b < 256; b += 64) sh.hist[w][b] = 0u;
@@ -867,9 +869,11 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
     const double ks = (double)K * S / (double)n;
     const int64_t jt = (int64_t)ceil((1.0 + 5.0 / sqrt(ks)) * ks);
     const int j = (int)(jt < 1 ? 1 : (jt > S ? S : jt));
+    // (tau only bounds the list: its top 16 bits suffice -- the keys it
+    // admits beyond the exact j-th lie within one part in 128 of it)
     uint32_t tau, tmask;
     int trem;
-    radix_kth(lds_keys, S, j, sh, tau, tmask, trem);
+    radix_kth(lds_keys, S, j, sh, tau, tmask, trem, 16);
 
     // ---- candidates: the wavefronts scan the row in steps of 1024 keys
     //      per wavefront (wavefront w takes the w-th 1024, 16 loads in flight per
