@@ -15,7 +15,7 @@ what this GPU reaches on a plain copy and a bf16 GEMM), and the CPU oracle
 timed on a bounded sample of the same workload.
 
     python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--paged] [--neighbours] [--store-bf16] [--no-cold] [--no-peaks]
+                    [--paged] [--neighbours] [--store-bf16 | --store-e4m3-bf16] [--no-cold] [--no-peaks]
 """
 from __future__ import annotations
 
@@ -83,7 +83,7 @@ def cpu_baseline(wl, budget_s: float = 10.0) -> dict:
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
     except Exception:  # pragma: no cover
         cores = 1
-    cfg = O.Config(block_size=wl.block_size, topk_blocks=wl.topk, store_q8=wl.store_q8)
+    cfg = O.Config(block_size=wl.block_size, topk_blocks=wl.topk, store_q8=bool(wl.store_q8))
     rng = np.random.default_rng(0)
     B = wl.block_size
     total_q = sum(x.n_q for x in wl.seqs)
@@ -278,6 +278,8 @@ def main() -> int:
                          "cache writes) before the path and the sigmoid output gate in the attention")
     ap.add_argument("--store-bf16", action="store_true",
                     help="keep the store in bf16 (no E4M3 rounding: the ablation)")
+    ap.add_argument("--store-e4m3-bf16", action="store_true",
+                    help="hold the E4M3 store values in bf16 (store_q8 = 1) instead of one-byte codes")
     ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache step times")
     ap.add_argument("--no-peaks", action="store_true",
                     help="skip measuring this GPU's copy bandwidth and bf16 GEMM rate")
@@ -293,7 +295,10 @@ def main() -> int:
     from synth import workloads as W
     from tests.gpu_setup import lib_seq, lib_seqs, prepare
 
-    wl = W.make(args.workload, store_q8=not args.store_bf16)
+    if args.store_bf16 and args.store_e4m3_bf16:
+        print("--store-bf16 and --store-e4m3-bf16 exclude each other", file=sys.stderr)
+        return 2
+    wl = W.make(args.workload, store_q8=0 if args.store_bf16 else 1 if args.store_e4m3_bf16 else 2)
     if args.paged and wl.loop_steps:
         print("bench.py --paged takes workloads of one call", file=sys.stderr)
         return 2

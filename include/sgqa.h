@@ -97,7 +97,10 @@ typedef struct sgqa_config {
     float eps_rms;         /* RMSNorm epsilon of the indexer queries (1e-6)         */
     float eps_ln;          /* LayerNorm epsilon of the proxy keys (1e-6)            */
     int32_t store_q8;      /* 1: round summaries fp32 -> bf16 -> E4M3 (held as bf16
-                              values); 0: round to bf16 only                        */
+                              values); 2: the same E4M3 values held as OCP E4M3FN
+                              codes, one byte each (a uint8 store, half the bytes
+                              the scorers stream; the scores are bit-identical to
+                              those of 1); 0: round to bf16 only                    */
 } sgqa_config;
 
 /* One sequence of a call.  All fields are validated on the host. */
@@ -158,7 +161,8 @@ size_t sgqa_workspace_size(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
  *   comp_logits  fp32 [rows, idx_dim]   compression logits, same rows
  *   ln_gamma     bf16 [idx_dim] or NULL (= 1)
  *   ln_beta      bf16 [idx_dim] or NULL (= 0)
- *   store        bf16 [store_rows, idx_dim], row store_offset + r  (written)
+ *   store        bf16 [store_rows, idx_dim], row store_offset + r  (written);
+ *                uint8 E4M3 codes, same shape, when cfg->store_q8 == 2
  */
 int sgqa_compress(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                   const void* proxy_k, const float* comp_logits, const void* ln_gamma,
@@ -181,7 +185,8 @@ int sgqa_compress(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
  *   q_idx       bf16 [Nq, G, idx_heads, idx_dim]   raw indexer queries
  *   w           fp32 [Nq, G, idx_heads]            signed head weights
  *   rms_gamma   bf16 [idx_dim] or NULL (= 1)
- *   store       bf16 [store_rows, idx_dim]
+ *   store       bf16 [store_rows, idx_dim] (uint8 E4M3 codes when
+ *               cfg->store_q8 == 2)
  *   sel         int32 [Nq, G, K]                   (written)
  *   sel_scores  fp32 [Nq, G, K] or NULL: s of each listed block, 0 at padding
  *   q_hat_out   bf16 [Nq, G, idx_heads, idx_dim] or NULL: q_hat (for checking)

@@ -75,13 +75,19 @@ class Seq(ctypes.Structure):
     ]
 
 
-def config(block_size: int = 8, topk_blocks: int = 512, store_q8: bool = True, **kw) -> Config:
+def config(block_size: int = 8, topk_blocks: int = 512, store_q8: int = 2, **kw) -> Config:
     """The page's layer shape (64 heads, 4 groups, head_dim 192, 4x128 indexer,
-    32-dim rotary span, base 1e4, softmax scale 1/sqrt(192)); fields overridable."""
+    32-dim rotary span, base 1e4, softmax scale 1/sqrt(192)); fields overridable.
+
+    store_q8: 2 (default) E4M3 codes in a uint8 store, 1 the same values held
+    in a bf16 store (twice the bytes, identical results), 0 bf16 values
+    (the unrounded ablation)."""
+    if int(store_q8) not in (0, 1, 2):
+        raise ValueError("store_q8 must be 0, 1 or 2")
     c = Config(num_q_heads=64, num_kv_groups=4, head_dim=192, idx_heads=4, idx_dim=128,
                rope_dim=32, rope_base=10000.0, block_size=block_size, topk_blocks=topk_blocks,
                softmax_scale=1.0 / math.sqrt(192.0), eps_rms=1e-6, eps_ln=1e-6,
-               store_q8=int(bool(store_q8)))
+               store_q8=int(store_q8))
     for k, v in kw.items():
         setattr(c, k, v)
     return c
@@ -197,6 +203,11 @@ def _ptr(t: Optional[torch.Tensor], dtype: torch.dtype, name: str, required: boo
     return t.data_ptr()
 
 
+def _store_ptr(cfg: Config, store):
+    """The proxy-key store: uint8 E4M3 codes when cfg.store_q8 == 2, else bf16."""
+    return _ptr(store, torch.uint8 if cfg.store_q8 == 2 else torch.bfloat16, "store")
+
+
 def _stream_ptr(stream) -> Optional[int]:
     if stream is None:
         stream = torch.cuda.current_stream()
@@ -232,7 +243,7 @@ def compress(cfg: Config, seqs: Sequence[Seq], proxy_k, comp_logits, store, ln_g
         _ptr(comp_logits, torch.float32, "comp_logits"),
         _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
         _ptr(ln_beta, torch.bfloat16, "ln_beta", False),
-        _ptr(store, torch.bfloat16, "store"), None, 0, _stream_ptr(stream)))
+        _store_ptr(cfg, store), None, 0, _stream_ptr(stream)))
 
 
 def index_topk(cfg: Config, seqs: Sequence[Seq], q_idx, w, store, sel, sel_scores=None,
@@ -242,7 +253,7 @@ def index_topk(cfg: Config, seqs: Sequence[Seq], q_idx, w, store, sel, sel_score
     _check(lib().sgqa_index_topk(
         ctypes.byref(cfg), arr, n, _ptr(q_idx, torch.bfloat16, "q_idx"),
         _ptr(w, torch.float32, "w"), _ptr(rms_gamma, torch.bfloat16, "rms_gamma", False),
-        _ptr(store, torch.bfloat16, "store"), _ptr(sel, torch.int32, "sel"),
+        _store_ptr(cfg, store), _ptr(sel, torch.int32, "sel"),
         _ptr(sel_scores, torch.float32, "sel_scores", False),
         _ptr(q_hat_out, torch.bfloat16, "q_hat_out", False), wsp, wsn, _stream_ptr(stream)))
 
@@ -267,7 +278,7 @@ def forward(cfg: Config, seqs: Sequence[Seq], proxy_k, comp_logits, store, q_idx
         ctypes.byref(cfg), arr, n, _ptr(proxy_k, torch.bfloat16, "proxy_k"),
         _ptr(comp_logits, torch.float32, "comp_logits"),
         _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
-        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _ptr(store, torch.bfloat16, "store"),
+        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _store_ptr(cfg, store),
         _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"),
         _ptr(rms_gamma, torch.bfloat16, "rms_gamma", False), _ptr(sel, torch.int32, "sel"),
         _ptr(sel_scores, torch.float32, "sel_scores", False), _ptr(q, torch.bfloat16, "q"),
@@ -295,7 +306,7 @@ def compress_paged(cfg: Config, seqs: Sequence[Seq], proxy_pages, logit_pages, p
         _ptr(logit_pages, torch.float32, "logit_pages"), ptp, ptn, npg,
         _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
         _ptr(ln_beta, torch.bfloat16, "ln_beta", False),
-        _ptr(store, torch.bfloat16, "store"), None, 0, _stream_ptr(stream)))
+        _store_ptr(cfg, store), None, 0, _stream_ptr(stream)))
 
 
 def sparse_attn_paged(cfg: Config, seqs: Sequence[Seq], q, k_pages, v_pages, page_table, sel, out,
@@ -321,7 +332,7 @@ def forward_paged(cfg: Config, seqs: Sequence[Seq], proxy_pages, logit_pages, st
         ctypes.byref(cfg), arr, n, _ptr(proxy_pages, torch.bfloat16, "proxy_pages"),
         _ptr(logit_pages, torch.float32, "logit_pages"),
         _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
-        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _ptr(store, torch.bfloat16, "store"),
+        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _store_ptr(cfg, store),
         _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"),
         _ptr(rms_gamma, torch.bfloat16, "rms_gamma", False), _ptr(sel, torch.int32, "sel"),
         _ptr(sel_scores, torch.float32, "sel_scores", False), _ptr(q, torch.bfloat16, "q"),
@@ -371,7 +382,7 @@ def forward_gated(cfg: Config, seqs: Sequence[Seq], proxy_k, comp_logits, store,
         ctypes.byref(cfg), arr, n, _ptr(proxy_k, torch.bfloat16, "proxy_k"),
         _ptr(comp_logits, torch.float32, "comp_logits"),
         _ptr(ln_gamma, torch.bfloat16, "ln_gamma", False),
-        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _ptr(store, torch.bfloat16, "store"),
+        _ptr(ln_beta, torch.bfloat16, "ln_beta", False), _store_ptr(cfg, store),
         _ptr(q_idx, torch.bfloat16, "q_idx"), _ptr(w, torch.float32, "w"),
         _ptr(rms_gamma, torch.bfloat16, "rms_gamma", False), _ptr(sel, torch.int32, "sel"),
         _ptr(sel_scores, torch.float32, "sel_scores", False), _ptr(q, torch.bfloat16, "q"),

@@ -117,7 +117,11 @@ __global__ __launch_bounds__(256) void compress_kernel(SeqTable seqs, CompressAr
         o0 = bf16_to_e4m3_as_bf16(o0);
         o1 = bf16_to_e4m3_as_bf16(o1);
     }
-    *(uint32_t*)(a.store + (sq.store_offset + r) * kIdxDim + d0) = o0 | (o1 << 16);
+    if (a.store_q8 == 2)        // E4M3 codes, one byte per coordinate
+        *(uint16_t*)((uint8_t*)a.store + (sq.store_offset + r) * kIdxDim + d0) =
+            (uint16_t)(e4m3_code(o0) | (e4m3_code(o1) << 8));
+    else
+        *(uint32_t*)(a.store + (sq.store_offset + r) * kIdxDim + d0) = o0 | (o1 << 16);
 }
 
 }  // namespace

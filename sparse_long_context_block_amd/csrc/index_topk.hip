@@ -145,6 +145,47 @@ __device__ uint32_t compact_topk(uint32_t* key, int32_t* idx, int n, int k, uint
 
 __device__ __forceinline__ uint4 load16(const uint16_t* p) { return *(const uint4*)p; }
 
+// Store rows as the score kernels read them: bf16 (256 B per block) or
+// E4M3 codes (128 B per block).  A load leaves Raw in registers; widen()
+// gives the 8 bf16 values of one MFMA operand (E4M3 -> bf16 is exact; the
+// gfx950 conversion takes two codes per instruction, OCP E4M3FN).
+template <bool FP8>
+struct StoreFmt {
+    using Raw = uint4;
+    static constexpr int kRowBytes = kIdxDim * 2;
+    // row 0 of the sequence's store, at coordinate 8 qq
+    __device__ static const uint8_t* rows(const void* store, int64_t store_offset, int qq) {
+        return (const uint8_t*)store + store_offset * kRowBytes + 16 * qq;
+    }
+    // coordinates 32 kk + [0, 8) relative to p (a row as rows() places it)
+    __device__ static Raw load(const uint8_t* p, int kk) { return *(const uint4*)(p + 64 * kk); }
+    __device__ static bf16x8 widen(Raw r) { return as_bf16x8(r); }
+};
+
+// codes of bytes 2 HI, 2 HI + 1 of the word -> two bf16 (low half first)
+template <bool HI>
+__device__ __forceinline__ uint32_t e4m3x2_to_bf16x2(uint32_t codes) {
+    return __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8(codes, 1.0f, HI));
+}
+
+template <>
+struct StoreFmt<true> {
+    using Raw = uint2;
+    static constexpr int kRowBytes = kIdxDim;
+    __device__ static const uint8_t* rows(const void* store, int64_t store_offset, int qq) {
+        return (const uint8_t*)store + store_offset * kRowBytes + 8 * qq;
+    }
+    __device__ static Raw load(const uint8_t* p, int kk) { return *(const uint2*)(p + 32 * kk); }
+    __device__ static bf16x8 widen(Raw r) {
+        uint4 o;
+        o.x = e4m3x2_to_bf16x2<false>(r.x);
+        o.y = e4m3x2_to_bf16x2<true>(r.x);
+        o.z = e4m3x2_to_bf16x2<false>(r.y);
+        o.w = e4m3x2_to_bf16x2<true>(r.y);
+        return as_bf16x8(o);
+    }
+};
+
 // Indexer query of (row, t): RMSNorm, rotary span at position t, bf16; the
 // lane's A-operand fragments (row m = 4*group + head, k-chunk qq).  Writes
 // q_hat when asked.
@@ -219,7 +260,9 @@ __device__ __forceinline__ void index_query_fragments(const IndexArgs& a, int64_
 
 }
 
+template <bool FP8>
 __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs a) {
+    using F = StoreFmt<FP8>;
     extern __shared__ uint32_t lds[];
     const int cap = a.cap;
     uint32_t* keys = lds;                               // [4][cap]
@@ -245,7 +288,7 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
     const int64_t nb = t / a.block_size;
     const int64_t r_lo = (int64_t)split * a.split_blocks;
     const int64_t r_hi = nb < r_lo + a.split_blocks ? nb : r_lo + a.split_blocks;
-    const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
+    const uint8_t* store = F::rows(a.store, sq.store_offset, qq);
 
     uint32_t thr = 0u;             // accept keys above it (0: accept every score)
     int cnt0 = 0, cnt1 = 0, cnt2 = 0, cnt3 = 0;
@@ -253,29 +296,29 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
     int32_t* const myidx = idxs + qq * cap;
 
     // B operand of tile r0: lane holds store[r0 + m][32kk + 8qq .. +7]
-    uint4 b0[4], b1[4];
-    auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * kIdxDim; };
+    typename F::Raw b0[4], b1[4];
+    auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * F::kRowBytes; };
     if (r_lo < r_hi) {
         const int64_t o = row_of(r_lo);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b0[kk] = load16(store + o + 32 * kk);
+        for (int kk = 0; kk < 4; ++kk) b0[kk] = F::load(store + o, kk);
     }
     if (r_lo + 16 < r_hi) {
         const int64_t o = row_of(r_lo + 16);
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
+        for (int kk = 0; kk < 4; ++kk) b1[kk] = F::load(store + o, kk);
     }
     for (int64_t r0 = r_lo; r0 < r_hi; r0 += 16) {
         f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], as_bf16x8(b0[kk]), acc);
+        for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], F::widen(b0[kk]), acc);
         // rotate the two-tile register pipeline: tile r0+32 goes in flight
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) b0[kk] = b1[kk];
         if (r0 + 32 < r_hi) {
             const int64_t o = row_of(r0 + 32);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) b1[kk] = load16(store + o + 32 * kk);
+            for (int kk = 0; kk < 4; ++kk) b1[kk] = F::load(store + o, kk);
         }
         float s = wv.x * fmaxf(acc[0], 0.f);
         s += wv.y * fmaxf(acc[1], 0.f);
@@ -350,7 +393,9 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
 // block ids; one workgroup per (query, group) then selects.  Keys cost 4 B
 // per (query, group, candidate): 33 MB for 64 sequences of 256K tokens.
 // ---------------------------------------------------------------------------
+template <bool FP8>
 __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArgs a) {
+    using F = StoreFmt<FP8>;
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = blockIdx.x / a.n_split;
     const int split = blockIdx.x % a.n_split;
@@ -368,19 +413,19 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
     index_query_fragments(a, row, t, qq, m, split == 0, afrag);
     if (r_lo >= r_hi) return;
     const float4 wv = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
-    const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
+    const uint8_t* store = F::rows(a.store, sq.store_offset, qq);
     uint32_t* keys = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
     // 16-block store tiles, kDepth of them in flight (a ring refilled kDepth
     // tiles ahead as each is used)
     constexpr int kDepth = 4;
-    uint4 b[kDepth][4];
-    auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * kIdxDim; };
+    typename F::Raw b[kDepth][4];
+    auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * F::kRowBytes; };
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
         if (r_lo + 16 * d < r_hi) {
             const int64_t o = row_of(r_lo + 16 * d);
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) b[d][kk] = load16(store + o + 32 * kk);
+            for (int kk = 0; kk < 4; ++kk) b[d][kk] = F::load(store + o, kk);
         }
     for (int64_t r00 = r_lo; r00 < r_hi; r00 += 16 * kDepth) {
 #pragma unroll
@@ -389,11 +434,11 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
             if (r0 >= r_hi) break;                     // wavefront-uniform
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], as_bf16x8(b[d][kk]), acc);
+            for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], F::widen(b[d][kk]), acc);
             if (r0 + 16 * kDepth < r_hi) {
                 const int64_t o = row_of(r0 + 16 * kDepth);
 #pragma unroll
-                for (int kk = 0; kk < 4; ++kk) b[d][kk] = load16(store + o + 32 * kk);
+                for (int kk = 0; kk < 4; ++kk) b[d][kk] = F::load(store + o, kk);
             }
             float s = wv.x * fmaxf(acc[0], 0.f);
             s += wv.y * fmaxf(acc[1], 0.f);
@@ -444,7 +489,7 @@ constexpr int kStoreTile = 64;
 constexpr int kStoreStrideU = kIdxDim + 8;    // bf16 per LDS store row (68 dwords = 4 x 17)
 static_assert(kSegBlocks % kStoreTile == 0, "a store tile lies inside one segment");
 
-template <bool LISTED>
+template <bool LISTED, bool FP8>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void index_score_tile_kernel(
     SeqTable seqs, IndexArgs a) {
     __shared__ __attribute__((aligned(16))) uint16_t tiles[2][kStoreTile * kStoreStrideU];
@@ -521,27 +566,41 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
         (int)(uint32_t)(kScoreTileQueries * kGroups * a.key_stride * 4), 0x00020000);
     constexpr uint32_t kDropped = 0xFFFFFFF0u;
 
-    // ---- store tiles: 64 rows x 16 chunks of 16 B, four chunks per thread;
-    //      rows past the range read as zero (their scores are dropped) ----
+    // ---- store tiles: 64 rows of 16 B chunks (16 per bf16 row, four per
+    //      thread; 8 per E4M3 row, two per thread, widened to bf16 on the way
+    //      into LDS); rows past the range read as zero (their scores are
+    //      dropped) ----
+    constexpr int kRowBytes = FP8 ? kIdxDim : kIdxDim * 2;
+    constexpr int kChunkShift = FP8 ? 3 : 4;        // log2 chunks per row
+    constexpr int kStage = FP8 ? 2 : 4;             // chunks per thread
     const __amdgpu_buffer_rsrc_t srs = __builtin_amdgcn_make_buffer_rsrc(
-        (void*)(a.store + (sq.store_offset + r_lo) * kIdxDim), (short)0,
-        (int)((r_hi - r_lo) * kIdxDim * 2), 0x00020000);
-    auto gload = [&](int rt, uint4 (&v)[4]) {
+        (void*)((const uint8_t*)a.store + (sq.store_offset + r_lo) * kRowBytes), (short)0,
+        (int)((r_hi - r_lo) * kRowBytes), 0x00020000);
+    auto gload = [&](int rt, uint4 (&v)[kStage]) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kStage; ++k) {
             const int c = tid + 256 * k;
+            const int ch = c & ((1 << kChunkShift) - 1);
             v[k] = __builtin_bit_cast(uint4, __builtin_amdgcn_raw_buffer_load_b128(
-                                                 srs, (rt + (c >> 4)) * (kIdxDim * 2) + 16 * (c & 15), 0, 0));
+                                                 srs, (rt + (c >> kChunkShift)) * kRowBytes + 16 * ch, 0, 0));
         }
     };
-    auto lstore = [&](uint16_t* buf, const uint4 (&v)[4]) {
+    auto lstore = [&](uint16_t* buf, const uint4 (&v)[kStage]) {
 #pragma unroll
-        for (int k = 0; k < 4; ++k) {
+        for (int k = 0; k < kStage; ++k) {
             const int c = tid + 256 * k;
-            *(uint4*)(buf + (c >> 4) * kStoreStrideU + 8 * (c & 15)) = v[k];
+            const int ch = c & ((1 << kChunkShift) - 1);
+            uint16_t* dst = buf + (c >> kChunkShift) * kStoreStrideU;
+            if constexpr (FP8) {
+                *(uint4*)(dst + 16 * ch) = __builtin_bit_cast(uint4, StoreFmt<true>::widen(uint2{v[k].x, v[k].y}));
+                *(uint4*)(dst + 16 * ch + 8) =
+                    __builtin_bit_cast(uint4, StoreFmt<true>::widen(uint2{v[k].z, v[k].w}));
+            } else {
+                *(uint4*)(dst + 8 * ch) = v[k];
+            }
         }
     };
-    uint4 stage[4];
+    uint4 stage[kStage];
     gload(0, stage);
     lstore(tiles[0], stage);
     int cur = 0;
@@ -1069,7 +1128,9 @@ __global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, In
 // ---------------------------------------------------------------------------
 constexpr int kSampleParts = 8;
 
+template <bool FP8>
 __global__ __launch_bounds__(256) void index_sample_kernel(SeqTable seqs, IndexArgs a) {
+    using F = StoreFmt<FP8>;
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t n_qt = (sq.n_q + kScoreTileQueries - 1) / kScoreTileQueries;
     const int64_t qt = blockIdx.x / kSampleParts;
@@ -1097,22 +1158,22 @@ __global__ __launch_bounds__(256) void index_sample_kernel(SeqTable seqs, IndexA
         sk[j] = qo < n_valid ? a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride + a.samp_off
                              : nullptr;
     }
-    const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
+    const uint8_t* store = F::rows(a.store, sq.store_offset, qq);
     auto start = [&](int gi) { return (int64_t)gi * (n0 - 16) / (ngrp > 1 ? ngrp - 1 : 1); };
-    uint4 b[4];
+    typename F::Raw b[4];
     if (g_lo < g_hi) {
-        const uint16_t* src = store + (start(g_lo) + m) * kIdxDim;
+        const uint8_t* src = store + (start(g_lo) + m) * F::kRowBytes;
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) b[kk] = load16(src + 32 * kk);
+        for (int kk = 0; kk < 4; ++kk) b[kk] = F::load(src, kk);
     }
     for (int gi = g_lo; gi < g_hi; ++gi) {
         bf16x8 bf[4];
 #pragma unroll
-        for (int kk = 0; kk < 4; ++kk) bf[kk] = as_bf16x8(b[kk]);
+        for (int kk = 0; kk < 4; ++kk) bf[kk] = F::widen(b[kk]);
         if (gi + 1 < g_hi) {
-            const uint16_t* src = store + (start(gi + 1) + m) * kIdxDim;
+            const uint8_t* src = store + (start(gi + 1) + m) * F::kRowBytes;
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) b[kk] = load16(src + 32 * kk);
+            for (int kk = 0; kk < 4; ++kk) b[kk] = F::load(src, kk);
         }
         f32x4 acc[4];
 #pragma unroll
@@ -1351,7 +1412,9 @@ __global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, I
 // groups, one wavefront per range of split_blocks candidates) into its key
 // rows, over the launch's failed-row list (a grid-stride loop: the count is
 // known only on the device).
+template <bool FP8>
 __global__ __launch_bounds__(256) void index_rescore_kernel(SeqTable seqs, IndexArgs a) {
+    using F = StoreFmt<FP8>;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int qq = lane >> 4, m = lane & 15;
     const int64_t units = (int64_t)a.ctl[0] * a.n_split;
@@ -1369,14 +1432,14 @@ __global__ __launch_bounds__(256) void index_rescore_kernel(SeqTable seqs, Index
 #pragma unroll
         for (int kk = 0; kk < 4; ++kk) af[kk] = as_bf16x8(qf[kk * 64 + lane]);
         const float4 wv = *(const float4*)(a.w + ((sq.q_offset + qi) * kGroups + qq) * kIdxHeads);
-        const uint16_t* store = a.store + sq.store_offset * kIdxDim + 8 * qq;
+        const uint8_t* store = F::rows(a.store, sq.store_offset, qq);
         uint32_t* keys = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
         for (int64_t r0 = r_lo; r0 < r_hi; r0 += 16) {
             const int64_t r = r0 + m < r_hi ? r0 + m : r_lo;
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
-                acc = mfma_16x16x32(af[kk], as_bf16x8(load16(store + r * kIdxDim + 32 * kk)), acc);
+                acc = mfma_16x16x32(af[kk], F::widen(F::load(store + r * F::kRowBytes, kk)), acc);
             if (r0 + m < r_hi) keys[r0 + m] = score_key_nz(head_score(acc, wv));
         }
     }
@@ -1461,11 +1524,14 @@ hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexAr
                              hipStream_t stream) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
     const size_t lds = index_lds_bytes(a.cap);
-    hipError_t e = hipFuncSetAttribute((const void*)index_topk_kernel,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    const void* fn = a.store_fp8 ? (const void*)index_topk_kernel<true> : (const void*)index_topk_kernel<false>;
+    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(max_nq * a.n_split), (unsigned)seqs.n);
-    hipLaunchKernelGGL(index_topk_kernel, grid, dim3(64), lds, stream, seqs, a);
+    if (a.store_fp8)
+        hipLaunchKernelGGL(index_topk_kernel<true>, grid, dim3(64), lds, stream, seqs, a);
+    else
+        hipLaunchKernelGGL(index_topk_kernel<false>, grid, dim3(64), lds, stream, seqs, a);
     return hipGetLastError();
 }
 
@@ -1473,7 +1539,10 @@ hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexA
                               hipStream_t stream) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
     dim3 grid((unsigned)(max_nq * a.n_split), (unsigned)seqs.n);
-    hipLaunchKernelGGL(index_score_kernel, grid, dim3(64), 0, stream, seqs, a);
+    if (a.store_fp8)
+        hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(64), 0, stream, seqs, a);
+    else
+        hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(64), 0, stream, seqs, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     return launch_select(seqs, max_nq, a, stream);
@@ -1505,19 +1574,28 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const dim3 rows_grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
     if (any_listed) {
-        hipLaunchKernelGGL(index_sample_kernel, dim3((unsigned)(n_qt * kSampleParts), (unsigned)seqs.n), dim3(256), 0,
-                           stream, seqs, a);
+        const dim3 sgrid((unsigned)(n_qt * kSampleParts), (unsigned)seqs.n);
+        if (a.store_fp8)
+            hipLaunchKernelGGL(index_sample_kernel<true>, sgrid, dim3(256), 0, stream, seqs, a);
+        else
+            hipLaunchKernelGGL(index_sample_kernel<false>, sgrid, dim3(256), 0, stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
         hipLaunchKernelGGL(index_tau_kernel, rows_grid, dim3(256), 0, stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     const dim3 grid((unsigned)(n_qt * a.n_split), (unsigned)seqs.n);
     if (any_keyed) {
-        hipLaunchKernelGGL(index_score_tile_kernel<false>, grid, dim3(256), 0, stream, seqs, a);
+        if (a.store_fp8)
+            hipLaunchKernelGGL((index_score_tile_kernel<false, true>), grid, dim3(256), 0, stream, seqs, a);
+        else
+            hipLaunchKernelGGL((index_score_tile_kernel<false, false>), grid, dim3(256), 0, stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (any_listed) {
-        hipLaunchKernelGGL(index_score_tile_kernel<true>, grid, dim3(256), 0, stream, seqs, a);
+        if (a.store_fp8)
+            hipLaunchKernelGGL((index_score_tile_kernel<true, true>), grid, dim3(256), 0, stream, seqs, a);
+        else
+            hipLaunchKernelGGL((index_score_tile_kernel<true, false>), grid, dim3(256), 0, stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
     if (any_keyed && (e = launch_select(seqs, max_nq, a, stream, keyed_long)) != hipSuccess) return e;
@@ -1532,7 +1610,10 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
     if ((e = hipGetLastError()) != hipSuccess) return e;
     // rows whose lists failed (usually none): scored again, then selected
     // from their keys; grid-stride loops over the count the device holds
-    hipLaunchKernelGGL(index_rescore_kernel, dim3(1024), dim3(256), 0, stream, seqs, a);
+    if (a.store_fp8)
+        hipLaunchKernelGGL(index_rescore_kernel<true>, dim3(1024), dim3(256), 0, stream, seqs, a);
+    else
+        hipLaunchKernelGGL(index_rescore_kernel<false>, dim3(1024), dim3(256), 0, stream, seqs, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds_r = select_long_lds<4>(a);
     if ((e = hipFuncSetAttribute((const void*)index_select_rescue_kernel,

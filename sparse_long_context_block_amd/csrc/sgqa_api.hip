@@ -55,8 +55,8 @@ int check_config(const sgqa_config* c) {
         return fail(SGQA_ERR_CONFIG, "softmax_scale must be finite and positive");
     if (!(isfinite(c->eps_rms) && c->eps_rms >= 0.f && isfinite(c->eps_ln) && c->eps_ln >= 0.f))
         return fail(SGQA_ERR_CONFIG, "eps_rms / eps_ln must be finite and >= 0");
-    if (c->store_q8 != 0 && c->store_q8 != 1)
-        return fail(SGQA_ERR_CONFIG, "store_q8 must be 0 or 1");
+    if (c->store_q8 < 0 || c->store_q8 > 2)
+        return fail(SGQA_ERR_CONFIG, "store_q8 must be 0, 1 or 2");
     if (c->num_q_heads != sgqa::kHeads || c->num_kv_groups != sgqa::kGroups ||
         c->head_dim != sgqa::kHeadDim || c->idx_heads != sgqa::kIdxHeads ||
         c->idx_dim != sgqa::kIdxDim || c->rope_dim != sgqa::kRopeDim)
@@ -375,6 +375,7 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     a.w = w;
     a.rms_gamma = (const uint16_t*)rms_gamma;
     a.store = (const uint16_t*)store;
+    a.store_fp8 = c->store_q8 == 2;
     a.sel = sel;
     a.sel_scores = sel_scores;
     a.q_hat_out = (uint16_t*)q_hat_out;

@@ -69,7 +69,7 @@ struct IndexArgs {
     const uint16_t* q_idx;
     const float* w;
     const uint16_t* rms_gamma;  // may be null
-    const uint16_t* store;
+    const uint16_t* store;      // bf16 rows, or E4M3 codes when store_fp8 (128 B rows)
     int32_t* sel;
     float* sel_scores;          // may be null
     uint16_t* q_hat_out;        // may be null
@@ -88,6 +88,7 @@ struct IndexArgs {
     int32_t n_split;
     int32_t split_blocks;       // candidate blocks per split (multiple of 16)
     int32_t list_cap;           // listed rows: entries of the LDS pool (list_capacity)
+    int32_t store_fp8;          // store rows hold E4M3 codes
     float eps;
     double theta[kRopeDim / 2]; // rotary frequencies base^(-2j/32)
 };
@@ -281,6 +282,19 @@ __device__ __forceinline__ uint32_t bf16_to_e4m3_as_bf16(uint32_t b) {
     r = fminf(r, 448.0f);
     r = copysignf(r, x);
     return __float_as_uint(r) >> 16;             // exactly representable in bf16
+}
+
+// OCP E4M3FN code of a bf16 value that E4M3 represents exactly (what
+// bf16_to_e4m3_as_bf16 returns): normals (bf16 exponent >= 121, i.e. >= 2^-6)
+// take the exponent rebiased by -120 and the top three mantissa bits;
+// smaller values are multiples of 2^-9 (the code's low bits), zero included.
+__device__ __forceinline__ uint32_t e4m3_code(uint32_t h) {
+    const uint32_t sign = (h >> 8) & 0x80u;
+    const uint32_t e = (h >> 7) & 0xFFu;
+    const uint32_t mt = h & 0x7Fu;
+    if (e >= 121) return sign | ((e - 120) << 3) | (mt >> 4);
+    if (e < 118) return sign;
+    return sign | ((0x80u | mt) >> (125 - e));
 }
 
 // Order-preserving map of a score to uint32 (larger score -> larger key);

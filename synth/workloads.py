@@ -69,7 +69,9 @@ class Workload:
     seqs: List[SeqLayout]
     # store rows written before the measured step: (pos0=0, n_q=pos0) per seq
     prebuilt: bool = False
-    store_q8: bool = True
+    # proxy-key store: 2 E4M3 codes (uint8), 1 the same values held in
+    # bf16, 0 bf16 values
+    store_q8: int = 2
     seed: int = 0
     notes: str = ""
     # loops of calls (decode loops, chained prefills): seqs holds
@@ -149,7 +151,7 @@ def _multi(name, parts, B, K, row_gap=0, order=None) -> Workload:
     return Workload(name, B, K, seqs, prebuilt=True)
 
 
-def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
+def make(name: str, seed: int = 0, store_q8: int = 2) -> Workload:
     if name == "tiny_prefill_256":
         w = _prefill(name, 256, 8, 16)
     elif name == "prefill_8k":
@@ -196,7 +198,7 @@ def make(name: str, seed: int = 0, store_q8: bool = True) -> Workload:
     else:
         raise KeyError(name)
     w.seed = seed
-    w.store_q8 = store_q8
+    w.store_q8 = int(store_q8)
     return w
 
 
@@ -234,7 +236,7 @@ def device_inputs(wl: Workload, device="cuda") -> DeviceInputs:
     t["w"] = dv.fill_f32(torch.empty((Nq, G, HI), dtype=f32, device=device), wl.seed, TID_W, scale=C_W)
     t["proxy_k"] = dv.fill_bf16(torch.empty((R, DI), dtype=bf, device=device), wl.seed, TID_PROXY)
     t["logits"] = dv.fill_f32(torch.empty((R, DI), dtype=f32, device=device), wl.seed, TID_LOGITS)
-    t["store"] = torch.zeros((S, DI), dtype=bf, device=device)
+    t["store"] = torch.zeros((S, DI), dtype=torch.uint8 if wl.store_q8 == 2 else bf, device=device)
     t["sel"] = torch.zeros((Nq, G, wl.topk), dtype=torch.int32, device=device)
     t["sel_scores"] = torch.zeros((Nq, G, wl.topk), dtype=f32, device=device)
     t["q_hat"] = torch.zeros((Nq, G, HI, DI), dtype=bf, device=device)

@@ -19,7 +19,7 @@ from .gpu_setup import lib_config, lib_seq, lib_seqs, log, prepare, setup_seqs  
 
 
 def oracle_config(wl: W.Workload) -> O.Config:
-    return O.Config(block_size=wl.block_size, topk_blocks=wl.topk, store_q8=wl.store_q8,
+    return O.Config(block_size=wl.block_size, topk_blocks=wl.topk, store_q8=bool(wl.store_q8),
                     softmax_scale=float(np.float32(1.0 / np.sqrt(192.0))))
 
 
@@ -69,7 +69,10 @@ class Checker:
     def __init__(self, wl: W.Workload, di, cfg):
         self.wl, self.di, self.cfg = wl, di, cfg
         self.ocfg = oracle_config(wl)
-        self.store = di["store"].cpu().view(torch.int16).numpy().view(np.uint16)
+        st = di["store"].cpu()
+        if st.dtype == torch.uint8:            # E4M3 codes: widened exactly to bf16
+            st = st.view(torch.float8_e4m3fn).to(torch.bfloat16)
+        self.store = st.view(torch.int16).numpy().view(np.uint16)
         self.sel = di["sel"].cpu().numpy()
         self.sel_scores = di["sel_scores"].cpu().numpy()
         self.q_hat = di["q_hat"].cpu().view(torch.int16).numpy().view(np.uint16)

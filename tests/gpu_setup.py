@@ -45,6 +45,19 @@ def lib_seq(s: W.SeqLayout) -> sg.Seq:
                   store_offset=s.store_offset, store_capacity=s.store_capacity)
 
 
+def poison_store(rows):
+    """Mark store rows as unwritten: NaN, or the E4M3FN NaN code (0x7F) in a
+    code store, which widens to NaN."""
+    rows.fill_(0x7F if rows.dtype == torch.uint8 else float("nan"))
+
+
+def store_values(store):
+    """The store's values as float32 (codes widened)."""
+    if store.dtype == torch.uint8:
+        store = store.view(torch.float8_e4m3fn)
+    return store.float()
+
+
 def prepare(wl: W.Workload):
     di = W.device_inputs(wl)
     cfg = lib_config(wl)

@@ -70,7 +70,7 @@ def _good_seq(n_q=8, pos0=0):
 
 @pytest.mark.parametrize("field,value,code", [
     ("num_q_heads", 0, E_CONFIG), ("num_q_heads", 65, E_CONFIG), ("rope_dim", 31, E_CONFIG),
-    ("rope_dim", 256, E_CONFIG), ("store_q8", 2, E_CONFIG), ("softmax_scale", math.nan, E_CONFIG),
+    ("rope_dim", 256, E_CONFIG), ("store_q8", 3, E_CONFIG), ("store_q8", -1, E_CONFIG), ("softmax_scale", math.nan, E_CONFIG),
     ("softmax_scale", -1.0, E_CONFIG), ("eps_rms", -1.0, E_CONFIG), ("rope_base", 0.0, E_CONFIG),
     ("topk_blocks", 0, E_CONFIG), ("block_size", 0, E_CONFIG),
     ("head_dim", 128, E_UNSUP), ("idx_dim", 64, E_UNSUP), ("num_kv_groups", 8, E_UNSUP),
@@ -286,3 +286,19 @@ def test_binding_rejects_wrong_tensors():
     with pytest.raises((TypeError, ValueError)):
         sg.sparse_attn(cfg, [_good_seq()], torch.zeros(4), torch.zeros(4), torch.zeros(4),
                        torch.zeros(4, dtype=torch.int32), torch.zeros(4))
+
+
+def test_binding_store_format():
+    # store_q8 = 2 (the default) takes E4M3 codes in a uint8 store; the dtype is checked
+    # before any call (CPU tensors and a bf16 store are both refused)
+    import torch
+    with pytest.raises(ValueError):
+        sg.config(store_q8=3)
+    cfg = sg.config()
+    assert cfg.store_q8 == 2
+    with pytest.raises(TypeError):
+        sg._store_ptr(cfg, torch.zeros(4, 128, dtype=torch.bfloat16))
+    with pytest.raises(ValueError):
+        sg._store_ptr(cfg, torch.zeros(4, 128, dtype=torch.uint8))      # not a device tensor
+    with pytest.raises(TypeError):
+        sg._store_ptr(sg.config(store_q8=1), torch.zeros(4, 128, dtype=torch.uint8))

@@ -18,6 +18,7 @@ import sparse_long_context_block_amd as sg
 from synth import workloads as W
 
 from .gpu_checks import Checker, lib_config, lib_seq, log, stratified_rows
+from .gpu_setup import poison_store, store_values
 
 pytestmark = pytest.mark.gpu
 
@@ -30,7 +31,7 @@ def test_chained_prefill_builds_its_own_store(name):
     log("case", name, n_calls, "calls of", wl.seqs[0].n_q, "B", B, "K", K)
     di = W.device_inputs(wl)
     cfg = lib_config(wl)
-    di["store"].fill_(float("nan"))
+    poison_store(di["store"])
     torch.cuda.synchronize()
     for c in range(n_calls):
         sg.forward(cfg, [lib_seq(s) for s in wl.step_seqs(c)], di["proxy_k"], di["logits"],
@@ -38,7 +39,7 @@ def test_chained_prefill_builds_its_own_store(name):
                    di["out"], lse=di["lse"], sel_scores=di["sel_scores"])
     torch.cuda.synchronize()
     assert torch.isfinite(di["out"].float()).all() and torch.isfinite(di["lse"]).all()
-    assert torch.isfinite(di["store"].float()).all()
+    assert torch.isfinite(store_values(di["store"])).all()
 
     # the indexer once more per call, only to expose q_hat (the store is
     # complete now, but a call only ever reads blocks before its queries)

@@ -19,6 +19,7 @@ import sparse_long_context_block_amd as sg
 from synth import workloads as W
 
 from .gpu_checks import Checker, lib_config, log
+from .gpu_setup import poison_store
 
 pytestmark = pytest.mark.gpu
 
@@ -53,7 +54,7 @@ def test_decode_loop_appends_and_compresses():
         tail = slice(s.kv_offset + s.pos0, s.kv_offset + s.kv_capacity)
         for name in _CACHE_TENSORS:
             di[name][tail] = float("nan")
-        di["store"][s.store_offset + s.pos0 // B:s.store_offset + s.store_capacity] = float("nan")
+        poison_store(di["store"][s.store_offset + s.pos0 // B:s.store_offset + s.store_capacity])
     torch.cuda.synchronize()
 
     completed = 0

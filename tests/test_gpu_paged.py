@@ -18,6 +18,7 @@ import sparse_long_context_block_amd as sg
 from synth import workloads as W
 
 from .gpu_checks import Checker, lib_seq, lib_seqs, log, prepare, stratified_rows
+from .gpu_setup import poison_store
 
 pytestmark = pytest.mark.gpu
 
@@ -39,7 +40,7 @@ def test_paged_forward_matches_contiguous(name):
     pre = [sg.Seq(q_offset=0, n_q=s.pos0, pos0=0, cache_len=s.pos0, kv_offset=p.kv_offset,
                   kv_capacity=s.kv_capacity, store_offset=s.store_offset, store_capacity=s.store_capacity)
            for s, p in zip(wl.seqs, pseqs) if s.pos0 > 0]
-    di["store"].fill_(float("nan"))
+    poison_store(di["store"])
     if pre:
         sg.compress_paged(cfg, pre, pools["proxy_k"], pools["logits"], table, di["store"])
     for k in ("sel", "sel_scores", "out", "lse"):

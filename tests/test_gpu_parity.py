@@ -11,7 +11,7 @@ from .gpu_checks import Checker, log, prepare, run_steps
 pytestmark = pytest.mark.gpu
 
 
-def _run_and_check(name, n_rows=64, store_q8=True, check_all_store=True, seed_rows=0):
+def _run_and_check(name, n_rows=64, store_q8=2, check_all_store=True, seed_rows=0):
     wl = W.make(name, store_q8=store_q8)
     log("case", wl.name, "q8" if store_q8 else "bf16")
     di, cfg = prepare(wl)

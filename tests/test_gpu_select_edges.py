@@ -21,7 +21,8 @@ id), so no oracle run is needed:
   full and selected from their keys.
 
 Inputs are seeded random tensors (or constructed exactly), written straight
-into the indexer's inputs; only the index step runs.
+into the indexer's inputs as a bf16-held store (store_q8 = 1, so the tied-mass
+case can use values E4M3 does not hold); only the index step runs.
 """
 import numpy as np
 import pytest
@@ -60,7 +61,7 @@ def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
     q_idx = torch.randn(n_q, 4, 4, 128, generator=gen, device="cuda").to(torch.bfloat16)
     w = torch.zeros(n_q, 4, 4, dtype=torch.float32, device="cuda")
     store = torch.randn(cache // B, 128, generator=gen, device="cuda").to(torch.bfloat16)
-    cfg = sg.config(block_size=B, topk_blocks=K)
+    cfg = sg.config(block_size=B, topk_blocks=K, store_q8=1)
     sel, ssc = _run_index(cfg, [sg.seq(n_q, pos0=pos0, block_size=B)], n_q, q_idx, w, store)
     n = (pos0 + np.arange(n_q)) // B                       # candidates per row
     m = np.minimum(n, K)
@@ -95,7 +96,7 @@ def test_sample_overestimate_falls_back_exactly(K, hot_groups):
     q_idx[0, :, 0] = u               # head 0 of every group
     w = torch.zeros(1, 4, 4, dtype=torch.float32)
     w[0, :, 0] = 1.0
-    cfg = sg.config(block_size=B, topk_blocks=K)
+    cfg = sg.config(block_size=B, topk_blocks=K, store_q8=1)
     sel, ssc = _run_index(cfg, [sg.seq(1, pos0=t, block_size=B)], 1,
                           q_idx.to(torch.bfloat16).cuda(), w.cuda(),
                           store.to(torch.bfloat16).cuda())
@@ -138,7 +139,7 @@ def test_listed_threshold_above_kth_falls_back_exactly():
     q_idx[:, :, 0] = u
     w = torch.zeros(n_q, 4, 4, dtype=torch.float32)
     w[:, :, 0] = 1.0
-    cfg = sg.config(block_size=B, topk_blocks=K)
+    cfg = sg.config(block_size=B, topk_blocks=K, store_q8=1)
     sel, ssc = _run_index(cfg, [sg.seq(n_q, pos0=pos0, block_size=B)], n_q,
                           q_idx.to(torch.bfloat16).cuda(), w.cuda(), store.to(torch.bfloat16).cuda())
     hot_set = set(hot)
@@ -190,7 +191,7 @@ def test_listed_rows_with_tied_mass_above_the_pool(w0):
         q[:, :, i, 40 + i] = 1.0
     q_idx = torch.from_numpy(q).to(torch.bfloat16).cuda()
     w = torch.tensor([w0, -1.0, -1.0, -1.0], dtype=torch.float32).repeat(n_q, 4, 1).cuda()
-    cfg = sg.config(block_size=B, topk_blocks=K)
+    cfg = sg.config(block_size=B, topk_blocks=K, store_q8=1)
     seqs = [sg.seq(n_q, pos0=pos0, kv_capacity=cache, store_capacity=n_blocks)]
     sel, ssc = _run_index(cfg, seqs, n_q, q_idx, w, store_d)
     c = float(torch.tensor(1.0 / np.sqrt(1.0 / 128 + 1e-6)).to(torch.bfloat16))

@@ -1,0 +1,98 @@
+"""The proxy-key store held as E4M3 codes (store_q8 = 2; page "Step-5-Preview:
+Sparse Reads Are Not a Compressed KV Cache", section "Eight tokens become one
+search key, coordinate by coordinate": the summaries are stored in E4M3 and
+widened to BF16 for the score matmul).
+
+Every store value is an E4M3 value either way, so a run over a uint8 code
+store must give the same bits as the run over the bf16-held store
+(store_q8 = 1): the codes widen to the very bf16 values, and every score
+kernel sees identical MFMA operands.  Checked on workloads that take each
+index path (fused streaming top-k, split scoring, tiled keyed and listed
+tiles, the list select's rescue) and through the oracle on one of them.
+"""
+import numpy as np
+import pytest
+import torch
+
+import sparse_long_context_block_amd as sg
+from synth import workloads as W
+
+from .gpu_checks import Checker, log, prepare, run_steps, stratified_rows
+from .gpu_setup import lib_seqs
+
+pytestmark = pytest.mark.gpu
+
+
+def _forward(wl):
+    di, cfg = prepare(wl)
+    sg.forward(cfg, lib_seqs(wl), di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"], di["sel"],
+               di["q"], di["k"], di["v"], di["out"], lse=di["lse"], sel_scores=di["sel_scores"])
+    torch.cuda.synchronize()
+    return di
+
+
+@pytest.mark.parametrize("name", [
+    "prefill_300_b8_k64",            # every row has <= k candidates: fused kernel
+    "tiny_prefill_256",              # split scoring, short rows
+    "decode_small",                  # split scoring, long rows, split attention
+    "prefill_2000_b1_k64",           # tiled keyed scoring, wave and staged selects
+    "chunk_40000_1024_b1_k64",       # listed tiles: sample, threshold, candidate lists
+    "chunk_1003_1997_b8_k64",        # a chunk over an existing cache
+])
+def test_code_store_gives_identical_bits(name):
+    log("case store codes", name)
+    ref = _forward(W.make(name, store_q8=1))
+    got = _forward(W.make(name, store_q8=2))
+    assert got["store"].dtype == torch.uint8
+    widened = got["store"].view(torch.float8_e4m3fn).to(torch.bfloat16)
+    assert torch.equal(widened.view(torch.int16), ref["store"].view(torch.int16))
+    for k in ("sel", "sel_scores", "lse"):
+        assert torch.equal(got[k], ref[k]), k
+    assert torch.equal(got["out"].view(torch.int16), ref["out"].view(torch.int16))
+
+
+def test_code_store_against_the_oracle():
+    wl = W.make("decode_small", store_q8=2)
+    log("case store codes, oracle", wl.name)
+    di, cfg = prepare(wl)
+    run_steps(wl, di, cfg)
+    ck = Checker(wl, di, cfg)
+    rng = np.random.default_rng(3)
+    for si, s in enumerate(wl.seqs[:4]):
+        stored, exact = ck.oracle_store(s, s.cache_len // wl.block_size)
+        ck.check_store(s, stored, exact)
+        ck.check_seq(si, stratified_rows(s, wl.block_size, wl.topk, 8, rng), store_exact=(stored, exact))
+    log(" ", ck.finish())
+
+
+def test_code_store_rescue_path():
+    # a listed tile whose sampled threshold admits fewer than k candidates
+    # (hot blocks only on sampled positions): the rows are scored again from
+    # the code store by the rescore kernel and selected from their keys
+    B, K, n_q, pos0 = 1, 512, 1024, 40960
+    n0 = pos0 // B
+    hot = sorted({(g * (n0 - 16)) // 127 + i for g in range(4) for i in range(16)})
+    log("case store codes, rescue", len(hot))
+    u = torch.zeros(128, dtype=torch.float32)
+    u[32:] = 1.0
+    store = torch.zeros((pos0 + n_q) // B, 128, dtype=torch.float32)
+    store[hot] = u
+    q_idx = torch.zeros(n_q, 4, 4, 128, dtype=torch.float32)
+    q_idx[:, :, 0] = u
+    w = torch.zeros(n_q, 4, 4, dtype=torch.float32)
+    w[:, :, 0] = 1.0
+    seqs = [sg.seq(n_q, pos0=pos0, block_size=B)]
+    q_idx, w = q_idx.to(torch.bfloat16).cuda(), w.cuda()
+    outs = []
+    for q8, st in ((1, store.to(torch.bfloat16).cuda()),
+                   (2, store.to(torch.float8_e4m3fn).view(torch.uint8).cuda())):
+        cfg = sg.config(block_size=B, topk_blocks=K, store_q8=q8)
+        sel = torch.full((n_q, 4, K), -7, dtype=torch.int32, device="cuda")
+        ssc = torch.full((n_q, 4, K), 7.0, dtype=torch.float32, device="cuda")
+        sg.index_topk(cfg, seqs, q_idx, w, st, sel, sel_scores=ssc)
+        torch.cuda.synchronize()
+        outs.append((sel.cpu(), ssc.cpu()))
+    assert torch.equal(outs[0][0], outs[1][0]) and torch.equal(outs[0][1], outs[1][1])
+    hot_set = set(hot)
+    exp = np.array(sorted(hot + [r for r in range(K) if r not in hot_set][:K - len(hot)]), dtype=np.int32)
+    assert (outs[1][0].numpy() == exp[None, None, :]).all()
