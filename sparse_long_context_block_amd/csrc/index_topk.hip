@@ -393,9 +393,41 @@ __global__ __launch_bounds__(64) void index_topk_kernel(SeqTable seqs, IndexArgs
 // block ids; one workgroup per (query, group) then selects.  Keys cost 4 B
 // per (query, group, candidate): 33 MB for 64 sequences of 256K tokens.
 // ---------------------------------------------------------------------------
+// Store tiles in the decode scorer's lane-contiguous order: lane (qq, m)
+// holds coordinates 32 qq .. 32 qq + 31 of row m (64 B of bf16 or 32 B of
+// E4M3 codes, read with whole 16 B loads that together cover whole cache
+// lines), and MFMA step kk takes coordinates 32 qq + 8 kk .. + 7 of it; the
+// query fragments are permuted to the same order.
+template <bool FP8>
+struct LaneRows {
+    static constexpr int kLoads = FP8 ? 2 : 4;
+    static constexpr int kRowBytes = FP8 ? kIdxDim : 2 * kIdxDim;
+    struct Tile {
+        uint4 v[kLoads];
+    };
+    __device__ static const uint8_t* rows(const void* store, int64_t store_offset, int qq) {
+        return (const uint8_t*)store + store_offset * kRowBytes + qq * (kRowBytes / 4);
+    }
+    __device__ static Tile load(const uint8_t* p) {
+        Tile t;
+#pragma unroll
+        for (int i = 0; i < kLoads; ++i) t.v[i] = *(const uint4*)(p + 16 * i);
+        return t;
+    }
+    __device__ static bf16x8 operand(const Tile& t, int kk) {
+        if constexpr (FP8) {
+            const uint4 u = t.v[kk >> 1];
+            return (kk & 1) ? StoreFmt<true>::widen(uint2{u.z, u.w}) : StoreFmt<true>::widen(uint2{u.x, u.y});
+        } else {
+            return as_bf16x8(t.v[kk]);
+        }
+    }
+};
+
 template <bool FP8>
 __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArgs a) {
-    using F = StoreFmt<FP8>;
+    using F = LaneRows<FP8>;
+    __shared__ uint4 xp[4][4][16];
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = blockIdx.x / a.n_split;
     const int split = blockIdx.x % a.n_split;
@@ -412,21 +444,24 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
     bf16x8 afrag[4];
     index_query_fragments(a, row, t, qq, m, split == 0, afrag);
     if (r_lo >= r_hi) return;
+    // lane (qq, m) takes for step kk the fragment of chunk qq that lane
+    // (kk, m) formed: q_hat coordinates 32 qq + 8 kk .. + 7 of row m
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) xp[kk][qq][m] = __builtin_bit_cast(uint4, afrag[kk]);
+    wave_lds_sync();
+#pragma unroll
+    for (int kk = 0; kk < 4; ++kk) afrag[kk] = as_bf16x8(xp[qq][kk][m]);
     const float4 wv = *(const float4*)(a.w + (row * kGroups + qq) * kIdxHeads);
     const uint8_t* store = F::rows(a.store, sq.store_offset, qq);
     uint32_t* keys = a.part_key + ((sq.ws_row + qi) * kGroups + qq) * a.key_stride;
     // 16-block store tiles, kDepth of them in flight (a ring refilled kDepth
     // tiles ahead as each is used)
     constexpr int kDepth = 4;
-    typename F::Raw b[kDepth][4];
+    typename F::Tile b[kDepth];
     auto row_of = [&](int64_t r0) { return (r0 + m < r_hi ? r0 + m : r_lo) * F::kRowBytes; };
 #pragma unroll
     for (int d = 0; d < kDepth; ++d)
-        if (r_lo + 16 * d < r_hi) {
-            const int64_t o = row_of(r_lo + 16 * d);
-#pragma unroll
-            for (int kk = 0; kk < 4; ++kk) b[d][kk] = F::load(store + o, kk);
-        }
+        if (r_lo + 16 * d < r_hi) b[d] = F::load(store + row_of(r_lo + 16 * d));
     for (int64_t r00 = r_lo; r00 < r_hi; r00 += 16 * kDepth) {
 #pragma unroll
         for (int d = 0; d < kDepth; ++d) {
@@ -434,12 +469,8 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
             if (r0 >= r_hi) break;                     // wavefront-uniform
             f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-            for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], F::widen(b[d][kk]), acc);
-            if (r0 + 16 * kDepth < r_hi) {
-                const int64_t o = row_of(r0 + 16 * kDepth);
-#pragma unroll
-                for (int kk = 0; kk < 4; ++kk) b[d][kk] = F::load(store + o, kk);
-            }
+            for (int kk = 0; kk < 4; ++kk) acc = mfma_16x16x32(afrag[kk], F::operand(b[d], kk), acc);
+            if (r0 + 16 * kDepth < r_hi) b[d] = F::load(store + row_of(r0 + 16 * kDepth));
             float s = wv.x * fmaxf(acc[0], 0.f);
             s += wv.y * fmaxf(acc[1], 0.f);
             s += wv.z * fmaxf(acc[2], 0.f);
