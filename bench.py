@@ -43,6 +43,7 @@ H, G, D, HI, DI = 64, 4, 192, 4, 128
 def work_model(wl, seqs=None) -> dict:
     """Work of one step over `seqs` (default: the workload's sequences)."""
     B, K = wl.block_size, wl.topk
+    row_bytes = DI * (1 if wl.store_q8 == 2 else 2)     # E4M3 codes or bf16 values
     attn_pairs = 0          # sum over (t, g) of |U_t,g|
     idx_pairs = 0           # sum over t of b(t) (per group)
     comp_blocks = 0
@@ -54,14 +55,14 @@ def work_model(wl, seqs=None) -> dict:
         u = np.minimum(b, K) * B + (t - b * B) + 1
         attn_pairs += int(u.sum()) * G
         idx_pairs += int(b.sum())
-        store_bytes += int(b.sum()) * DI * 2
+        store_bytes += int(b.sum()) * row_bytes
         comp_blocks += s.cache_len // B - s.pos0 // B
     return {
         "attn_flops": attn_pairs * (H // G) * 4 * D,        # QK^T + PV, 2 flop per MAC
         "attn_gather_bytes": attn_pairs * 2 * D * 2,          # K and V rows, bf16
         "index_flops": idx_pairs * G * HI * 2 * DI,
         "index_store_bytes": store_bytes,                     # store read once per query
-        "compress_bytes": comp_blocks * (B * (DI * 2 + DI * 4) + DI * 2),
+        "compress_bytes": comp_blocks * (B * (DI * 2 + DI * 4) + row_bytes),
         "queries": sum(s.n_q for s in seqs),
     }
 
@@ -461,6 +462,13 @@ def main() -> int:
         if peaks:
             roof["measured_peak"] = max(peaks["hbm_copy_GBps"], peaks["hbm_read_GBps"])
             roof["frac_of_measured"] = achieved / roof["measured_peak"]
+        # the indexer and the attention together: the store streamed once per
+        # query plus the gathered K/V rows, over both calls' event times
+        path_bytes = wm["index_store_bytes"] + wm["attn_gather_bytes"]
+        path_ms = k_ms["index_topk"] + k_ms["sparse_attn"]
+        roof["index_plus_attention"] = {
+            "bytes": path_bytes, "ms": path_ms, "GBps": path_bytes / (path_ms * 1e-3) / 1e9,
+            "frac": path_bytes / (path_ms * 1e-3) / PEAK_HBM_BPS}
         queries = wm_loop_queries / args.steps if wm_loop_queries else wm["queries"]
         value, unit = queries / (ms_step * 1e-3), "queries/s"
     else:

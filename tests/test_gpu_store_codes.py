@@ -8,7 +8,8 @@ store must give the same bits as the run over the bf16-held store
 (store_q8 = 1): the codes widen to the very bf16 values, and every score
 kernel sees identical MFMA operands.  Checked on workloads that take each
 index path (fused streaming top-k, split scoring, tiled keyed and listed
-tiles, the list select's rescue) and through the oracle on one of them.
+tiles, the list select's rescue) and through the oracle on one of them; every
+finite code is scored once through the fused and the decode scorer.
 """
 import numpy as np
 import pytest
@@ -96,3 +97,43 @@ def test_code_store_rescue_path():
     hot_set = set(hot)
     exp = np.array(sorted(hot + [r for r in range(K) if r not in hot_set][:K - len(hot)]), dtype=np.int32)
     assert (outs[1][0].numpy() == exp[None, None, :]).all()
+
+
+@pytest.mark.parametrize("K", [256, 64])
+def test_every_code_widens_exactly(K):
+    # block r of the store holds code r on coordinate 40 (past the rotary
+    # span; the two NaN codes replaced by zero) and zeros elsewhere; indexer
+    # head 0 of every group is +e_40 for the first query and -e_40 for the
+    # second, weight 1, so block r scores c * max(+-value(r), 0) exactly
+    # (c = bf16 of the RMSNorm of a one-hot row; a bf16 x E4M3 product is
+    # exact in fp32).  K = 256 keeps every block (fused kernel); K = 64 keeps
+    # the 64 largest of each sign (decode-sized scoring kernel).
+    log("case every code", K)
+    codes = np.arange(256, dtype=np.uint8)
+    codes[[0x7F, 0xFF]] = 0
+    vals = torch.from_numpy(codes.copy()).view(torch.float8_e4m3fn).float().numpy()
+    rows = 257
+    store = np.zeros((2 * rows, 128), dtype=np.uint8)
+    store[:256, 40] = codes
+    store[rows:rows + 256, 40] = codes
+    q = np.zeros((2, 4, 4, 128), dtype=np.float32)
+    q[0, :, 0, 40] = 1.0
+    q[1, :, 0, 40] = -1.0
+    w = np.zeros((2, 4, 4), dtype=np.float32)
+    w[:, :, 0] = 1.0
+    seqs = [sg.Seq(q_offset=i, n_q=1, pos0=256, cache_len=257, kv_offset=0, kv_capacity=257,
+                   store_offset=i * rows, store_capacity=rows) for i in range(2)]
+    cfg = sg.config(block_size=1, topk_blocks=K)
+    sel = torch.full((2, 4, K), -7, dtype=torch.int32, device="cuda")
+    ssc = torch.full((2, 4, K), 7.0, dtype=torch.float32, device="cuda")
+    sg.index_topk(cfg, seqs, torch.from_numpy(q).to(torch.bfloat16).cuda(), torch.from_numpy(w).cuda(),
+                  torch.from_numpy(store).cuda(), sel, sel_scores=ssc)
+    torch.cuda.synchronize()
+    sel, ssc = sel.cpu().numpy(), ssc.cpu().numpy()
+    c = np.float32(float(torch.tensor(1.0 / np.sqrt(1.0 / 128 + 1e-6)).to(torch.bfloat16)))
+    for i, sign in enumerate((1.0, -1.0)):
+        s = (c * np.maximum(np.float32(sign) * vals, 0)).astype(np.float32)
+        want = np.sort(np.argsort(-s, kind="stable")[:K]).astype(np.int32)
+        for g in range(4):
+            assert np.array_equal(sel[i, g], want), (sign, g)
+            assert np.array_equal(ssc[i, g], s[want]), (sign, g)
