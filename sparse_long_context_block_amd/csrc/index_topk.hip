@@ -732,6 +732,7 @@ __host__ __device__ constexpr int select_capacity(int k, int nw) { return k + 10
 template <int NW>
 struct SelectShared {
     uint32_t hist[NW][256];
+    uint32_t total[256];        // NW > 4: the wavefronts' histograms summed
     uint32_t red[NW];
     int cnt[2][NW];
     int digit, above, count;
@@ -782,15 +783,31 @@ __device__ void radix_kth(const uint32_t* keys, int n, int k, SelectShared<NW>& 
             if ((kk & pmask) == prefix) atomicAdd(&sh.hist[w][(kk >> lo) & dmask], 1u);
         }
         __syncthreads();
+        if constexpr (NW > 4) {
+            // many wavefronts: 256 threads sum the histograms, so the scan
+            // below reads one total per bin instead of NW partial counts
+            if (tid < nbins) {
+                uint32_t hs = 0;
+#pragma unroll
+                for (int ww = 0; ww < NW; ++ww) hs += sh.hist[ww][tid];
+                sh.total[tid] = hs;
+            }
+            __syncthreads();
+        }
         if (w == 0) {
             uint32_t h[4], tot = 0;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const int d = nbins - 1 - 4 * lane - j;
                 uint32_t hs = 0;
-                if (d >= 0)
+                if (d >= 0) {
+                    if constexpr (NW > 4) {
+                        hs = sh.total[d];
+                    } else {
 #pragma unroll
-                    for (int ww = 0; ww < NW; ++ww) hs += sh.hist[ww][d];
+                        for (int ww = 0; ww < NW; ++ww) hs += sh.hist[ww][d];
+                    }
+                }
                 h[j] = hs;
                 tot += h[j];
             }

@@ -183,6 +183,8 @@ def make(name: str, seed: int = 0, store_q8: int = 2) -> Workload:
         w = _chained(name, 4, 1024, 1, 256)
     elif name == "decode_small":                 # 8 sequences, split paths (tests)
         w = _decode(name, n_seqs=8, lo=8192, hi=40000, cap=40960, seed=seed)
+    elif name == "decode_64_small":              # 64 sequences: one attention workgroup per CU (tests)
+        w = _decode(name, n_seqs=64, lo=4100, hi=12000, cap=12288, seed=seed)
     elif name.startswith("chunk_"):              # chunk_<pos0>_<n>[_b<B>_k<K>] (tests)
         parts = name.split("_")
         pos0, n = int(parts[1]), int(parts[2])

@@ -22,7 +22,7 @@ from .gpu_setup import poison_store
 
 pytestmark = pytest.mark.gpu
 
-@pytest.mark.parametrize("name", ["chunk_1003_997_b8_k64", "decode_small", "prefill_2000_b1_k64",
+@pytest.mark.parametrize("name", ["chunk_1003_997_b8_k64", "decode_small", "decode_64_small", "prefill_2000_b1_k64",
                                   "prefill_1003_b16_k8"])
 def test_paged_forward_matches_contiguous(name):
     wl = W.make(name)

@@ -80,6 +80,13 @@ def test_listed_long_rows(name):
     _run_and_check(name, n_rows=24, check_all_store=False)
 
 
+def test_decode_one_workgroup_per_cu():
+    # 64 sequences x 4 groups = 256 unsplit attention workgroups: the
+    # eight-wavefront gather
+    st = _run_and_check("decode_64_small", n_rows=1, check_all_store=False)
+    assert st["rows"] >= 64
+
+
 def test_decode_split_paths():
     st = _run_and_check("decode_small", n_rows=1, check_all_store=True)
     assert st["rows"] == 8
