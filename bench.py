@@ -451,7 +451,7 @@ def main() -> int:
         achieved = wm["attn_gather_bytes"] / (k_ms["sparse_attn"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
                 "frac": achieved / (PEAK_HBM_BPS / 1e9), "traffic": None,
-                "kernel": "sparse_attn_kernel + attn_merge_kernel (one sgqa_sparse_attn call)",
+                "kernel": "sparse_attn_kernel (one sgqa_sparse_attn call; calls split across workgroups add attn_merge_kernel)",
                 "algorithmic_bytes_per_launch": wm["attn_gather_bytes"],
                 "launch_ms": k_ms["sparse_attn"]}
         ctr = (recorded_counters(wl.name, ["sparse_attn_kernel<false>"])
