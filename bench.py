@@ -446,7 +446,8 @@ def main() -> int:
     dense = sum(min(s.n_q, max(0, 4 * wl.topk * wl.block_size - s.pos0)) if s.n_q >= 64 else 0
                 for s in op_seqs)
     if decode:
-        # dominant op: the attention call (split gather + merge), HBM-bound:
+        # dominant op: the attention call (the gather; a split call adds the
+        # merge), HBM-bound:
         # every gathered K/V row is read once per query and group
         achieved = wm["attn_gather_bytes"] / (k_ms["sparse_attn"] * 1e-3) / 1e9
         roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
