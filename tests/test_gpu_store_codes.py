@@ -9,7 +9,8 @@ store must give the same bits as the run over the bf16-held store
 kernel sees identical MFMA operands.  Checked on workloads that take each
 index path (fused streaming top-k, split scoring, tiled keyed and listed
 tiles, the list select's rescue) and through the oracle on one of them; every
-finite code is scored once through the fused and the decode scorer.
+finite code is scored once through the fused and the decode scorer, and written
+once by the merge step (B = 1, gamma 0, beta set to the codes' values).
 """
 import numpy as np
 import pytest
@@ -137,3 +138,35 @@ def test_every_code_widens_exactly(K):
         for g in range(4):
             assert np.array_equal(sel[i, g], want), (sign, g)
             assert np.array_equal(ssc[i, g], s[want]), (sign, g)
+
+
+def test_compress_writes_every_code():
+    # B = 1 and ln_gamma = 0: a block's summary is ln_beta exactly (softmax
+    # over one token is 1; LayerNorm times 0 plus beta), so with beta set to
+    # E4M3 values on the coordinates past the rotary span (32..127) the store
+    # codes must be those values' codes.  Three calls cover the 253 nonzero
+    # finite codes (0x80, negative zero, is left out: beta = -0 stores +0).
+    codes = np.array([c for c in range(256) if c not in (0x00, 0x7F, 0x80, 0xFF)], dtype=np.uint8)
+    log("case compress codes", len(codes))
+    n = 3
+    cfg = sg.config(block_size=1, topk_blocks=8)
+    seqs = [sg.Seq(q_offset=0, n_q=n, pos0=0, cache_len=n, kv_offset=0, kv_capacity=n, store_offset=0,
+                   store_capacity=n)]
+    rng = np.random.default_rng(11)
+    proxy = torch.from_numpy(rng.standard_normal((n, 128)).astype(np.float32)).to(torch.bfloat16).cuda()
+    logits = torch.from_numpy(rng.standard_normal((n, 128)).astype(np.float32)).cuda()
+    gamma = torch.zeros(128, dtype=torch.bfloat16, device="cuda")
+    for part in range(0, len(codes), 96):
+        chunk = codes[part:part + 96]
+        c96 = np.zeros(96, dtype=np.uint8)
+        c96[:len(chunk)] = chunk
+        beta = np.zeros(128, dtype=np.float32)
+        beta[32:] = torch.from_numpy(c96).view(torch.float8_e4m3fn).float().numpy()
+        store = torch.full((n, 128), 0x7F, dtype=torch.uint8, device="cuda")
+        sg.compress(cfg, seqs, proxy, logits, store, ln_gamma=gamma,
+                    ln_beta=torch.from_numpy(beta).to(torch.bfloat16).cuda())
+        torch.cuda.synchronize()
+        st = store.cpu().numpy()
+        for r in range(n):
+            assert np.array_equal(st[r, 32:], c96), (part, r)
+            assert np.isin(st[r, :32], (0x00, 0x80)).all(), (part, r)     # zeros on the rotary span
