@@ -3,19 +3,26 @@
 
 One step = one ``sgqa_forward`` (block merging -> indexer scores + causal
 top-k -> sparse GQA attention) of one attention layer over one batch of
-seeded synthetic input already resident in HBM.  Default workload: the
-single-layer prefill of 8,192 tokens (64 heads / 4 KV groups / head_dim 192,
-indexer 4 x 128 per group, B=8, k = 512 blocks = 4,096 tokens).
+seeded synthetic input already resident in HBM.
 
-Prints one JSON line with whole-step throughput, the distribution of single
-step times (warm, and cold: a 512 MiB write between steps evicts the caches),
-the roofline of the dominant kernel (its per-launch time measured with HIP
-events on the stream it runs on, against AMD's published peak and against
-what this GPU reaches on a plain copy and a bf16 GEMM), and the CPU oracle
-timed on a bounded sample of the same workload.
+Default run: the 8,192-query chunk at positions 1,040,384..1,048,575 over a
+1,048,576-token cache (64 heads / 4 KV groups / head_dim 192, indexer 4 x 128
+per group, B=8, k = 512 blocks = 4,096 tokens) is the headline record; the
+65,536-token prefill and the 64-sequence decode step over up to 262,144
+cached tokens ride along as sub-records of the same JSON line, each with its
+own roofline.
 
-    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
-                    [--paged] [--neighbours] [--store-bf16 | --store-e4m3-bf16] [--no-cold] [--no-peaks]
+Per workload: whole-step throughput over the timed steps, the distribution
+of single step times (warm, and cold: a 512 MiB write between steps evicts
+the caches), the step's stages timed inside the step with HIP events on the
+launch stream (warm and cold), the roofline of the dominant kernel (its
+in-step duration against AMD's published peak and against what this GPU
+reaches on a plain copy and a bf16 GEMM), and -- for the headline record --
+the CPU oracle timed on a bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--sub NAMES|none]
+                    [--no-cpu-baseline] [--paged] [--neighbours]
+                    [--store-bf16 | --store-e4m3-bf16] [--no-cold] [--no-peaks]
 """
 from __future__ import annotations
 
@@ -262,55 +269,79 @@ def event_time_ms(fn, stream, reps: int) -> float:
     return start.elapsed_time(end) / reps
 
 
-def main() -> int:
-    ap = argparse.ArgumentParser()
-    ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=50)
-    ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="prefill_8k")
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--kernel-reps", type=int, default=20)
-    ap.add_argument("--calibrate-copy", action="store_true",
-                    help="also run one 512 MiB device-to-device copy (HBM byte-counter scale)")
-    ap.add_argument("--paged", action="store_true",
-                    help="per-token caches as pools of 16-token pages behind a random page table")
-    ap.add_argument("--neighbours", action="store_true",
-                    help="each step also runs the main Q/K producer (RMSNorm, partial rotary span, "
-                         "cache writes) before the path and the sigmoid output gate in the attention")
-    ap.add_argument("--store-bf16", action="store_true",
-                    help="keep the store in bf16 (no E4M3 rounding: the ablation)")
-    ap.add_argument("--store-e4m3-bf16", action="store_true",
-                    help="hold the E4M3 store values in bf16 (store_q8 = 1) instead of one-byte codes")
-    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache step times")
-    ap.add_argument("--no-peaks", action="store_true",
-                    help="skip measuring this GPU's copy bandwidth and bf16 GEMM rate")
-    args = ap.parse_args()
-    if args.gpus != 1:
-        print(f"bench.py measures one GPU only (the path has no multi-GPU part); "
-              f"--gpus {args.gpus} is not supported", file=sys.stderr)
-        return 2
+
+
+# ---------------------------------------------------------------------------
+# one workload
+# ---------------------------------------------------------------------------
+
+DEFAULT_WORKLOAD = "chunk_1m"
+DEFAULT_SUBS = ("prefill_64k", "decode_64x256k")
+
+
+def dense_split(wl, seqs):
+    """The host's attention routing, restated: a sequence's leading queries
+    whose selection covers at least a quarter of their candidates
+    (floor(t/B) < 4K, i.e. t < 4*K*B) take the tiled kernel when the sequence
+    brings at least 64 queries; the rest take the gather kernel.  Returns the
+    per-sequence query counts (tiled, gathered)."""
+    out = []
+    for s in seqs:
+        nd = 0 if s.n_q < 64 else max(0, min(s.n_q, 4 * wl.topk * wl.block_size - s.pos0))
+        out.append((nd, s.n_q - nd))
+    return out
+
+
+def stage_times(stages, stream, n: int, flush=None) -> dict:
+    """`stages` (name -> callable) run in order as one step, n times, with a
+    HIP event between consecutive stages on the launch stream; per stage the
+    median, 10th and 90th percentile of its in-step duration.  With `flush` a
+    512 MiB write precedes every step outside the timed intervals (cold)."""
+    import torch
+    names = list(stages)
+    ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n)]
+    with torch.cuda.stream(stream):
+        for i in range(n):
+            if flush is not None:
+                flush.fill_(i & 0x7F)
+            ev[i][0].record(stream)
+            for j, nm in enumerate(names):
+                stages[nm]()
+                ev[i][j + 1].record(stream)
+    torch.cuda.synchronize()
+    out = {}
+    for j, nm in enumerate(names):
+        ms = np.array([ev[i][j].elapsed_time(ev[i][j + 1]) for i in range(n)])
+        out[nm] = {"median_ms": float(np.median(ms)), "p10_ms": float(np.percentile(ms, 10)),
+                   "p90_ms": float(np.percentile(ms, 90))}
+    tot = np.array([ev[i][0].elapsed_time(ev[i][-1]) for i in range(n)])
+    out["step"] = {"median_ms": float(np.median(tot)), "p10_ms": float(np.percentile(tot, 10)),
+                   "p90_ms": float(np.percentile(tot, 90)), "n": n}
+    return out
+
+
+def bench_workload(name: str, args, primary: bool, peaks=None) -> dict:
+    """Prepare `name`, time it and return its record (the JSON line's fields
+    for the headline workload, a sub-record otherwise)."""
+    import dataclasses
 
     import torch
 
     import sparse_long_context_block_amd as sg
     from synth import workloads as W
-    from tests.gpu_setup import lib_seq, lib_seqs, prepare
+    from synth.library import lib_seq, lib_seqs, prepare
 
-    if args.store_bf16 and args.store_e4m3_bf16:
-        print("--store-bf16 and --store-e4m3-bf16 exclude each other", file=sys.stderr)
-        return 2
-    wl = W.make(args.workload, store_q8=0 if args.store_bf16 else 1 if args.store_e4m3_bf16 else 2)
+    wl = W.make(name, store_q8=0 if args.store_bf16 else 1 if args.store_e4m3_bf16 else 2)
     if args.paged and wl.loop_steps:
-        print("bench.py --paged takes workloads of one call", file=sys.stderr)
-        return 2
+        raise SystemExit("bench.py --paged takes workloads of one call")
     print(f"[bench] workload {wl.name}: preparing inputs", file=sys.stderr, flush=True)
     di, cfg = prepare(wl)
     pools = table = None
     if args.paged:
         # the same logical contents in page pools; the contiguous copies go
         pools, table, layouts = W.paginate(wl, di, np.random.default_rng(0))
-        for name in ("k", "v", "proxy_k", "logits"):
-            di.t[name] = None
+        for nm in ("k", "v", "proxy_k", "logits"):
+            di.t[nm] = None
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
     nb = None
@@ -330,17 +361,19 @@ def main() -> int:
     if wl.loop_steps:
         loop = [[lib_seq(s) for s in wl.step_seqs(k)] for k in range(wl.loop_steps)]
         ws_n = max(sg.workspace_size(cfg, sq, sg.OP_FORWARD) for sq in loop)
+        op_layouts = wl.step_seqs(wl.loop_steps - 1)
     elif args.paged:
         loop = [[lib_seq(s) for s in layouts]]
         ws_n = sg.workspace_size(cfg, loop[0], sg.OP_FORWARD)
+        op_layouts = layouts
     else:
         loop = [lib_seqs(wl)]
         ws_n = sg.workspace_size(cfg, loop[0], sg.OP_FORWARD)
+        op_layouts = wl.seqs
     stream = torch.cuda.current_stream()
     ws = torch.empty(max(ws_n, 1) + 256, dtype=torch.uint8, device="cuda")
     ws_view = ws[(-ws.data_ptr()) % 256:][:max(ws_n, 1)]
     step_no = [0]
-
     k_cache = pools["k"] if pools is not None else di["k"]
     v_cache = pools["v"] if pools is not None else di["v"]
     gate = nb["gate"] if nb else None
@@ -367,34 +400,38 @@ def main() -> int:
                        di["sel"], di["q"], di["k"], di["v"], di["out"], lse=di["lse"],
                        ws=ws_view, stream=stream)
 
-    def op_compress():
+    # the stages of one call (the loop's last call: its longest context),
+    # the same kernels sgqa_forward launches, one call each
+    seqs = loop[-1]
+
+    def op_compress(sq=seqs):
         if pools is not None:
-            sg.compress_paged(cfg, seqs, pools["proxy_k"], pools["logits"], table, di["store"],
+            sg.compress_paged(cfg, sq, pools["proxy_k"], pools["logits"], table, di["store"],
                               stream=stream)
-            return
-        sg.compress(cfg, seqs, di["proxy_k"], di["logits"], di["store"], stream=stream)
+        else:
+            sg.compress(cfg, sq, di["proxy_k"], di["logits"], di["store"], stream=stream)
 
-    def op_index():
-        sg.index_topk(cfg, seqs, di["q_idx"], di["w"], di["store"], di["sel"],
-                      ws=ws_view, stream=stream)
+    def op_index(sq=seqs):
+        sg.index_topk(cfg, sq, di["q_idx"], di["w"], di["store"], di["sel"], ws=ws_view, stream=stream)
 
-    def op_attn():
+    def op_attn(sq=seqs):
         if pools is not None:
-            sg.sparse_attn_paged(cfg, seqs, di["q"], pools["k"], pools["v"], table, di["sel"],
+            sg.sparse_attn_paged(cfg, sq, di["q"], pools["k"], pools["v"], table, di["sel"],
                                  di["out"], lse=di["lse"], gate=gate, ws=ws_view, stream=stream)
         elif nb:
-            sg.sparse_attn_gated(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"], gate,
+            sg.sparse_attn_gated(cfg, sq, di["q"], di["k"], di["v"], di["sel"], di["out"], gate,
                                  lse=di["lse"], ws=ws_view, stream=stream)
         else:
-            sg.sparse_attn(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"],
+            sg.sparse_attn(cfg, sq, di["q"], di["k"], di["v"], di["sel"], di["out"],
                            lse=di["lse"], ws=ws_view, stream=stream)
 
     for _ in range(args.warmup):
         step()
     torch.cuda.synchronize()
-    print(f"[bench] warmup done ({args.warmup} steps); timing {args.steps}", file=sys.stderr,
-          flush=True)
+    print(f"[bench] {wl.name}: warmup done ({args.warmup} steps); timing {args.steps}",
+          file=sys.stderr, flush=True)
     first_timed = step_no[0]
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for _ in range(args.steps):
         step()
@@ -402,29 +439,217 @@ def main() -> int:
     wall = time.perf_counter() - t0
     ms_step = wall * 1e3 / args.steps
     timed = [loop[k % len(loop)] for k in range(first_timed, step_no[0])]
-    # the distribution of single steps (after the timed region): warm, and
-    # for workloads of one call also cold; a loop's steps are different calls
-    n_dist = min(args.steps, 20)
-    dist = {"warm": step_times(step, stream, n_dist)} if n_dist > 0 else {}
-    if not args.no_cold and not wl.loop_steps and n_dist > 0:
+
+    # single steps after the timed region: warm, and for workloads of one
+    # call also cold; a loop's steps are different calls
+    n_dist = min(max(args.steps, 1), 20)
+    dist = {"warm": step_times(step, stream, n_dist)}
+    flush = None
+    if not args.no_cold and not wl.loop_steps:
         flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
         dist["cold"] = step_times(step, stream, n_dist, flush)
-        del flush
-    print(f"[bench] step times {dist}", file=sys.stderr, flush=True)
-    # per-op timings and the roofline use the loop's last call (its longest
-    # context), or the step itself
-    seqs = loop[-1]
+    print(f"[bench] {wl.name}: step times {dist}", file=sys.stderr, flush=True)
 
-    reps = args.kernel_reps
-    k_ms = {
-        "compress": event_time_ms(op_compress, stream, reps),
-        "index_topk": event_time_ms(op_index, stream, reps),
-        "sparse_attn": event_time_ms(op_attn, stream, reps),
-    }
+    # the stages inside one step (one call of each, in order), warm and cold
+    stages = {"compress": op_compress, "index_topk": op_index, "sparse_attn": op_attn}
     if nb:
-        k_ms["qk_prep"] = event_time_ms(lambda: op_qk_prep(seqs), stream, reps)
-    print(f"[bench] per-op ms {k_ms}", file=sys.stderr, flush=True)
+        stages = {"qk_prep": lambda: op_qk_prep(seqs), **stages}
+    in_step = {"warm": stage_times(stages, stream, n_dist)}
+    if flush is not None:
+        in_step["cold"] = stage_times(stages, stream, n_dist, flush)
+    if flush is not None:
+        del flush
+        torch.cuda.empty_cache()
+    print(f"[bench] {wl.name}: in-step stages {in_step}", file=sys.stderr, flush=True)
 
+    # each attention kernel alone: the queries the host routes to the tiled
+    # kernel and those it routes to the gather kernel as two calls (each a
+    # valid call: the first covers positions up to its own last query)
+    wm = work_model(wl, op_layouts)
+    kernel_ms = {}
+    split = dense_split(wl, op_layouts)
+    n_dense = sum(a for a, _ in split)
+    n_gath = sum(b for _, b in split)
+    lb = wl.block_size.bit_length() - 1
+    reps = args.kernel_reps
+    union_name, gather_name = f"attn_union_kernel<{lb}>", "sparse_attn_kernel"
+    if n_dense and n_gath and pools is None and not nb:
+        dl, gl = [], []
+        for s, (a, b) in zip(op_layouts, split):
+            if a:
+                dl.append(dataclasses.replace(s, n_q=a))
+            if b:
+                gl.append(dataclasses.replace(s, q_offset=s.q_offset + a, n_q=b, pos0=s.pos0 + a))
+        d_seqs, g_seqs = [lib_seq(s) for s in dl], [lib_seq(s) for s in gl]
+        kernel_ms[union_name] = event_time_ms(lambda: op_attn(d_seqs), stream, reps)
+        kernel_ms[gather_name] = event_time_ms(lambda: op_attn(g_seqs), stream, reps)
+        wm_d, wm_g = work_model(wl, dl), work_model(wl, gl)
+    else:
+        wm_d = wm if n_dense else None
+        wm_g = wm if n_gath else None
+    per_op = {"compress": event_time_ms(op_compress, stream, reps),
+              "index_topk": event_time_ms(op_index, stream, reps),
+              "sparse_attn": event_time_ms(op_attn, stream, reps)}
+    print(f"[bench] {wl.name}: repeated-call ms {per_op} kernels {kernel_ms}", file=sys.stderr,
+          flush=True)
+
+    decode = wl.name.startswith("decode")
+    attn_ms = in_step["warm"]["sparse_attn"]["median_ms"]
+    plain = pools is None and not nb and wl.store_q8 and not wl.loop_steps
+    if decode:
+        # dominant kernel: the gather (HBM-bound): every selected K/V row is
+        # read once per query and group
+        achieved = wm["attn_gather_bytes"] / (attn_ms * 1e-3) / 1e9
+        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
+                "frac": achieved / (PEAK_HBM_BPS / 1e9), "traffic": None,
+                "kernel": "sparse_attn_kernel (one sgqa_sparse_attn call; a call split across "
+                          "workgroups adds attn_merge_kernel)",
+                "algorithmic_bytes_per_launch": wm["attn_gather_bytes"], "launch_ms": attn_ms,
+                "launch_ms_from": "median in-step duration, warm"}
+        ctr = recorded_counters(wl.name, ["sparse_attn_kernel<false>"]) if plain else None
+        if ctr:
+            roof["traffic"] = ctr["fetch"] + ctr["write"]
+            roof["reuse"] = wm["attn_gather_bytes"] / ctr["fetch"]
+        if peaks:
+            roof["measured_peak"] = max(peaks["hbm_copy_GBps"], peaks["hbm_read_GBps"])
+            roof["frac_of_measured"] = achieved / roof["measured_peak"]
+        # the indexer and the attention of one step: the store streamed once
+        # per query plus the gathered K/V rows, over the two stages' in-step
+        # durations (cold: nothing of the step's inputs in any cache)
+        path_bytes = wm["index_store_bytes"] + wm["attn_gather_bytes"]
+        ipa = {"bytes": path_bytes}
+        for mode, st in in_step.items():
+            ms = st["index_topk"]["median_ms"] + st["sparse_attn"]["median_ms"]
+            ipa[mode] = {"ms": ms, "GBps": path_bytes / (ms * 1e-3) / 1e9,
+                         "frac": path_bytes / (ms * 1e-3) / PEAK_HBM_BPS}
+        roof["index_plus_attention"] = ipa
+        queries = (sum(sum(s.n_q for s in sq) for sq in timed) / args.steps if wl.loop_steps
+                   else wm["queries"])
+        value, unit = queries / (ms_step * 1e-3), "queries/s"
+    else:
+        achieved = wm["attn_flops"] / (attn_ms * 1e-3) / 1e12
+        kern = (union_name if not n_gath else gather_name if not n_dense
+                else f"{union_name} + {gather_name} ({n_dense} of {wm['queries']} queries tiled)")
+        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12,
+                "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16_FLOPS / 1e12), "traffic": None,
+                "kernel": kern, "algorithmic_flops_per_launch": wm["attn_flops"],
+                "launch_ms": attn_ms, "launch_ms_from": "median in-step duration, warm"}
+        union_k = f"attn_union_kernel<{lb}, false>"
+        ctr_k = ([union_k] if n_dense else []) + (["sparse_attn_kernel<false>"] if n_gath else [])
+        ctr = recorded_counters(wl.name, ctr_k) if plain else None
+        if ctr:
+            roof["traffic"] = ctr["fetch"] + ctr["write"]
+            # K/V bytes a gather per (query, group) would move over the bytes
+            # fetched from HBM
+            roof["reuse"] = wm["attn_gather_bytes"] / ctr["fetch"]
+        if peaks:
+            roof["measured_peak"] = peaks["bf16_gemm_TFLOPs"]
+            roof["frac_of_measured"] = achieved / peaks["bf16_gemm_TFLOPs"]
+        # each kernel on its own: MFMA fraction of its useful FLOPs and, for
+        # the gather, the rate it moves the selected K/V rows at and the HBM
+        # fraction of the bytes it fetched (FETCH_SIZE records, when current)
+        per_k = {}
+        for kname, w_k, ctr_name in ((union_name, wm_d, union_k),
+                                     (gather_name, wm_g, "sparse_attn_kernel<false>")):
+            if w_k is None:
+                continue
+            ms = kernel_ms.get(kname, attn_ms)
+            e = {"ms": ms, "ms_from": ("repeated calls of its queries alone" if kname in kernel_ms
+                                       else "median in-step duration, warm"),
+                 "flops": w_k["attn_flops"],
+                 "TFLOPs": w_k["attn_flops"] / (ms * 1e-3) / 1e12,
+                 "mfma_frac": w_k["attn_flops"] / (ms * 1e-3) / PEAK_BF16_FLOPS,
+                 "gathered_bytes": w_k["attn_gather_bytes"],
+                 "gathered_GBps": w_k["attn_gather_bytes"] / (ms * 1e-3) / 1e9}
+            c1 = recorded_counters(wl.name, [ctr_name]) if plain else None
+            if c1:
+                e["fetched_bytes"] = c1["fetch"]
+                e["hbm_GBps"] = c1["fetch"] / (ms * 1e-3) / 1e9
+                e["hbm_frac"] = c1["fetch"] / (ms * 1e-3) / PEAK_HBM_BPS
+                e["reuse"] = w_k["attn_gather_bytes"] / c1["fetch"]
+            per_k[kname] = e
+        roof["kernels"] = per_k
+        queries = (sum(sum(s.n_q for s in sq) for sq in timed) / args.steps if wl.loop_steps
+                   else wm["queries"])
+        value, unit = queries / (ms_step * 1e-3), "tokens/s"
+
+    rec = {
+        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
+        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": wl.name + ("+paged" if args.paged else "")
+                   + ("+neighbours" if nb else ""), "queries": wm["queries"],
+                   "block_size": wl.block_size, "topk_blocks": wl.topk, "store_q8": wl.store_q8,
+                   "heads": H, "kv_groups": G, "head_dim": D},
+        "per_op_ms": per_op,
+        "step_times": dist,
+        "in_step_ms": in_step,
+        "roofline": roof,
+    }
+    if wl.loop_steps:
+        rec["config"]["loop_calls"] = wl.loop_steps
+        rec["config"]["per_op_call"] = wl.loop_steps - 1
+        if args.steps % wl.loop_steps == 0:
+            # wall time of one pass over every call of the loop (a chained
+            # prefill: the whole prefill of one layer)
+            rec["loop_pass_s"] = wall / (args.steps // wl.loop_steps)
+    if primary and not args.no_cpu_baseline:
+        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
+        one = (dataclasses.replace(wl, seqs=wl.step_seqs(wl.loop_steps - 1), loop_steps=0,
+                                   loop_seqs=0) if wl.loop_steps else wl)
+        rec["cpu_baseline"] = cpu_baseline(one)
+    del di, ws, ws_view, pools, table, nb
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    return rec
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default=None,
+                    help=f"headline workload (default {DEFAULT_WORKLOAD}, with "
+                         f"{', '.join(DEFAULT_SUBS)} as sub-records)")
+    ap.add_argument("--sub", default=None,
+                    help="comma-separated sub-record workloads, or 'none' (default: "
+                         f"{','.join(DEFAULT_SUBS)} with the default workload, none otherwise)")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--kernel-reps", type=int, default=10)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one 512 MiB device-to-device copy (HBM byte-counter scale)")
+    ap.add_argument("--paged", action="store_true",
+                    help="per-token caches as pools of 16-token pages behind a random page table")
+    ap.add_argument("--neighbours", action="store_true",
+                    help="each step also runs the main Q/K producer (RMSNorm, partial rotary span, "
+                         "cache writes) before the path and the sigmoid output gate in the attention")
+    ap.add_argument("--store-bf16", action="store_true",
+                    help="keep the store in bf16 (no E4M3 rounding: the ablation)")
+    ap.add_argument("--store-e4m3-bf16", action="store_true",
+                    help="hold the E4M3 store values in bf16 (store_q8 = 1) instead of one-byte codes")
+    ap.add_argument("--no-cold", action="store_true", help="skip the cold-cache step times")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip measuring this GPU's copy bandwidth and bf16 GEMM rate")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (the path has no multi-GPU part); "
+              f"--gpus {args.gpus} is not supported", file=sys.stderr)
+        return 2
+    if args.store_bf16 and args.store_e4m3_bf16:
+        print("--store-bf16 and --store-e4m3-bf16 exclude each other", file=sys.stderr)
+        return 2
+    name = args.workload or DEFAULT_WORKLOAD
+    if args.sub is None:
+        subs = list(DEFAULT_SUBS) if args.workload is None else []
+    else:
+        subs = [] if args.sub == "none" else [x for x in args.sub.split(",") if x]
+
+    import torch
+
+    import sparse_long_context_block_amd as sg
+    sg.lib()                      # fails loudly when the library is not built
+    stream = torch.cuda.current_stream()
     peaks = None if args.no_peaks else measured_peaks(stream)
     if args.calibrate_copy:
         src = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
@@ -432,112 +657,14 @@ def main() -> int:
         dst.copy_(src)
         torch.cuda.synchronize()
         del src, dst
-
-    if wl.loop_steps:
-        op_seqs = wl.step_seqs(wl.loop_steps - 1)
-        wm = work_model(wl, op_seqs)
-        # throughput over the timed calls
-        wm_loop_queries = sum(sum(s.n_q for s in sq) for sq in timed)
-    else:
-        op_seqs = wl.seqs
-        wm = work_model(wl)
-        wm_loop_queries = None
-    decode = wl.name.startswith("decode")
-    dense = sum(min(s.n_q, max(0, 4 * wl.topk * wl.block_size - s.pos0)) if s.n_q >= 64 else 0
-                for s in op_seqs)
-    if decode:
-        # dominant op: the attention call (the gather; a split call adds the
-        # merge), HBM-bound:
-        # every gathered K/V row is read once per query and group
-        achieved = wm["attn_gather_bytes"] / (k_ms["sparse_attn"] * 1e-3) / 1e9
-        roof = {"bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_BPS / 1e9, "unit": "GB/s",
-                "frac": achieved / (PEAK_HBM_BPS / 1e9), "traffic": None,
-                "kernel": "sparse_attn_kernel (one sgqa_sparse_attn call; calls split across workgroups add attn_merge_kernel)",
-                "algorithmic_bytes_per_launch": wm["attn_gather_bytes"],
-                "launch_ms": k_ms["sparse_attn"]}
-        ctr = (recorded_counters(wl.name, ["sparse_attn_kernel<false>"])
-               if not args.paged and not nb and wl.store_q8 and not wl.loop_steps else None)
-        if ctr:
-            roof["traffic"] = ctr["fetch"] + ctr["write"]
-            roof["reuse"] = wm["attn_gather_bytes"] / ctr["fetch"]
-        if peaks:
-            roof["measured_peak"] = max(peaks["hbm_copy_GBps"], peaks["hbm_read_GBps"])
-            roof["frac_of_measured"] = achieved / roof["measured_peak"]
-        # the indexer and the attention together: the store streamed once per
-        # query plus the gathered K/V rows, over both calls' event times
-        path_bytes = wm["index_store_bytes"] + wm["attn_gather_bytes"]
-        path_ms = k_ms["index_topk"] + k_ms["sparse_attn"]
-        roof["index_plus_attention"] = {
-            "bytes": path_bytes, "ms": path_ms, "GBps": path_bytes / (path_ms * 1e-3) / 1e9,
-            "frac": path_bytes / (path_ms * 1e-3) / PEAK_HBM_BPS}
-        queries = wm_loop_queries / args.steps if wm_loop_queries else wm["queries"]
-        value, unit = queries / (ms_step * 1e-3), "queries/s"
-    else:
-        achieved = wm["attn_flops"] / (k_ms["sparse_attn"] * 1e-3) / 1e12
-        lb = wl.block_size.bit_length() - 1
-        kern = (f"attn_union_kernel<{lb}>" if dense == wm["queries"]
-                else "sparse_attn_kernel" if dense == 0
-                else f"attn_union_kernel<{lb}> + sparse_attn_kernel ({dense} of {wm['queries']} "
-                     f"queries tiled)")
-        # counters were taken on the plain (contiguous, ungated) call that
-        # runs one attention kernel
-        union_k = "attn_union_kernel<%d, false>" % (wl.block_size.bit_length() - 1)
-        ctr_kernels = ([union_k] if dense == wm["queries"] else ["sparse_attn_kernel<false>"] if dense == 0
-                       else [union_k, "sparse_attn_kernel<false>"])
-        ctr = (recorded_counters(wl.name, ctr_kernels)
-               if not args.paged and not nb and wl.store_q8 and not wl.loop_steps else None)
-        roof = {"bound": "mfma", "achieved": achieved, "peak": PEAK_BF16_FLOPS / 1e12,
-                "unit": "TFLOP/s", "frac": achieved / (PEAK_BF16_FLOPS / 1e12),
-                "traffic": ctr["fetch"] + ctr["write"] if ctr else None,
-                "kernel": kern,
-                "algorithmic_flops_per_launch": wm["attn_flops"],
-                "launch_ms": k_ms["sparse_attn"]}
-        if peaks:
-            roof["measured_peak"] = peaks["bf16_gemm_TFLOPs"]
-            roof["frac_of_measured"] = achieved / peaks["bf16_gemm_TFLOPs"]
-        if ctr:
-            # K/V bytes a gather per (query, group) would move over the bytes
-            # the kernel fetched from HBM
-            roof["reuse"] = wm["attn_gather_bytes"] / ctr["fetch"]
-        if dense < wm["queries"]:
-            # gathered K/V rows (768 B per query, group and attended token):
-            # the rate the gather kernel moves them at, against HBM peak
-            roof["gathered_GBps"] = wm["attn_gather_bytes"] / (k_ms["sparse_attn"] * 1e-3) / 1e9
-        queries = wm_loop_queries / args.steps if wm_loop_queries else wm["queries"]
-        value, unit = queries / (ms_step * 1e-3), "tokens/s"
-
-    res = {
-        "metric": METRIC, "value": value, "unit": unit, "n_gpus": 1, "steps": args.steps,
-        "warmup": args.warmup, "ms_per_step": ms_step, "higher_is_better": True,
-        "scaling": "weak", "vs_baseline": None, "dtype": "bf16", "data": "synthetic",
-        "config": {"workload": wl.name + ("+paged" if args.paged else "")
-                   + ("+neighbours" if nb else ""), "queries": wm["queries"],
-                   "block_size": wl.block_size,
-                   "topk_blocks": wl.topk, "store_q8": wl.store_q8,
-                   "heads": H, "kv_groups": G, "head_dim": D},
-        "per_op_ms": k_ms,
-        "step_times": dist,
-        "roofline": roof,
-    }
+    rec = bench_workload(name, args, primary=True, peaks=peaks)
     if peaks:
-        res["measured_peaks"] = peaks
-    if wl.loop_steps:
-        res["config"]["loop_calls"] = wl.loop_steps
-        res["config"]["per_op_call"] = wl.loop_steps - 1
-        if args.steps % wl.loop_steps == 0:
-            # wall time of one pass over every call of the loop (a chained
-            # prefill: the whole prefill of one layer)
-            res["loop_pass_s"] = wall / (args.steps // wl.loop_steps)
-    if not args.no_cpu_baseline:
-        print("[bench] timing the CPU oracle on a bounded sample", file=sys.stderr, flush=True)
-        if wl.loop_steps:
-            import dataclasses
-            one = dataclasses.replace(wl, seqs=wl.step_seqs(wl.loop_steps - 1),
-                                      loop_steps=0, loop_seqs=0)
-            res["cpu_baseline"] = cpu_baseline(one)
-        else:
-            res["cpu_baseline"] = cpu_baseline(wl)
-    print(json.dumps(res), flush=True)
+        rec["measured_peaks"] = peaks
+    if subs:
+        rec["sub_records"] = {}
+        for s in subs:
+            rec["sub_records"][s] = bench_workload(s, args, primary=False, peaks=peaks)
+    print(json.dumps(rec), flush=True)
     return 0
 
 

@@ -143,6 +143,25 @@ size_t sgqa_workspace_size(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
                            int32_t op);
 
 /*
+ * Diagnostics of the index step (for checking and monitoring).  Calls whose
+ * index step works in the tiled mode (1024 or more queries) keep, in their
+ * workspace at the byte offset returned here, a block of 64 uint32 words:
+ *   [0]  the number of (query, group) rows whose candidate lists could not
+ *        give the exact top k and were scored again over every candidate;
+ *   [1]  reserved (0);
+ *   [2 + 2j], [3 + 2j]  for j < min([0], 31): query row (q_offset + index in
+ *        the sequence, low 32 bits) and group of the j-th such row (in the
+ *        order the device found them).
+ * The block is cleared at the start of the call's index step and written by
+ * its kernels; the attention of the same sgqa_forward call leaves it alone
+ * (calls of that size never split their attention).  Returns -1, with no
+ * block kept, when the index step of these arguments does not use the tiled
+ * mode or the arguments are invalid (sgqa_last_error() says which).  The
+ * offset is the same for SGQA_OP_INDEX_TOPK and SGQA_OP_FORWARD workspaces.
+ */
+int64_t sgqa_index_diag_offset(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs);
+
+/*
  * Step 1 -- block-wise token merging (page section "Eight tokens become one
  * search key, coordinate by coordinate"; norms and rotary span from section
  * "Two paths leave the same hidden state").

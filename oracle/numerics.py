@@ -1,11 +1,10 @@
 """Storage roundings of the path, float64 in and float64 out.
 
-The compression kernel the first page audits accumulates in FP32 and rounds
-the result through BF16 into E4M3 for storage; the E4M3 values are widened
-losslessly back to BF16 for the score matmul ("Step-5-Preview: Sparse Reads
-Are Not a Compressed KV Cache", sections "Eight tokens become one search key,
-coordinate by coordinate" and "Selection is a weighted ReLU score, not
-attention softmax").
+A merged proxy key is an fp32 sum, stored after two roundings: first to
+bf16, then to E4M3; for scoring, the stored E4M3 value is converted exactly to
+bf16 ("Step-5-Preview: Sparse Reads Are Not a Compressed KV Cache", sections
+"Eight tokens become one search key, coordinate by coordinate" and
+"Selection is a weighted ReLU score, not attention softmax").
 
 * ``to_f32``     float64 -> nearest fp32 (ties to even), as a GPU fp32 result.
 * ``round_bf16`` float64 -> fp32 -> bf16, both steps round-to-nearest-even.

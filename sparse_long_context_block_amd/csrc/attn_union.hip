@@ -493,8 +493,7 @@ template <int LOG2B, bool PAGED>
 static hipError_t launch_union_t(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                                  int words, hipStream_t stream) {
     const size_t lds = (size_t)16 * words * sizeof(uint32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)attn_union_kernel<LOG2B, PAGED>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_dynamic_lds((const void*)attn_union_kernel<LOG2B, PAGED>, lds);
     if (e != hipSuccess) return e;
     const int64_t n_qt = (max_nq + 15) / 16;
     dim3 grid((unsigned)(n_qt * kGroups), (unsigned)seqs.n);

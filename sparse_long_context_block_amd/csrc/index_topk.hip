@@ -489,6 +489,10 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
 // wavefront per query; q_hat is written here when asked.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(256) void index_qfrag_kernel(SeqTable seqs, IndexArgs a) {
+    // the call's first launch clears its diagnostics block (the list select
+    // of this and later launches appends to it)
+    if (a.diag && a.diag_clear && blockIdx.x == 0 && blockIdx.y == 0 && threadIdx.x < kDiagWords)
+        a.diag[threadIdx.x] = 0u;
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
     if (qi >= sq.n_q) return;
@@ -1390,6 +1394,13 @@ __global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, I
         if (tid == 0) {
             const uint32_t slot = atomicAdd(&a.ctl[0], 1u);
             a.ctl[1 + slot] = ((uint32_t)qi << 8) | ((uint32_t)blockIdx.y << 2) | (uint32_t)g;
+            if (a.diag) {
+                const uint32_t d = atomicAdd(&a.diag[0], 1u);
+                if (d < (uint32_t)kDiagRows) {
+                    a.diag[2 + 2 * d] = (uint32_t)(sq.q_offset + qi);
+                    a.diag[3 + 2 * d] = (uint32_t)g;
+                }
+            }
         }
     };
     if (bad || total < K) {
@@ -1518,8 +1529,7 @@ static size_t select_long_lds(const IndexArgs& a) {
 template <int NW>
 static hipError_t launch_select_long(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a, hipStream_t stream) {
     const size_t lds = select_long_lds<NW>(a);
-    hipError_t e = hipFuncSetAttribute((const void*)index_select_kernel<true, NW>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_dynamic_lds((const void*)index_select_kernel<true, NW>, lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
     hipLaunchKernelGGL((index_select_kernel<true, NW>), grid, dim3(64 * NW), lds, stream, seqs, a);
@@ -1551,8 +1561,7 @@ static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const Inde
     }
     if (min_b <= kSelectStageKeys && max_rows_b > kWaveSelectKeys) {
         const size_t lds_s = (size_t)(max_b < kSelectStageKeys ? max_b : kSelectStageKeys) * sizeof(uint32_t);
-        e = hipFuncSetAttribute((const void*)index_select_kernel<false, 4>,
-                                hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_s);
+        e = set_dynamic_lds((const void*)index_select_kernel<false, 4>, lds_s);
         if (e != hipSuccess) return e;
         hipLaunchKernelGGL((index_select_kernel<false, 4>), grid, dim3(256), lds_s, stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1573,7 +1582,7 @@ hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexAr
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
     const size_t lds = index_lds_bytes(a.cap);
     const void* fn = a.store_fp8 ? (const void*)index_topk_kernel<true> : (const void*)index_topk_kernel<false>;
-    hipError_t e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_dynamic_lds(fn, lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(max_nq * a.n_split), (unsigned)seqs.n);
     if (a.store_fp8)
@@ -1651,8 +1660,7 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
     IndexArgs al = a;
     al.list_cap = list_capacity(n0_listed, a.topk);
     const size_t lds_l = (size_t)al.list_cap * 8;
-    if ((e = hipFuncSetAttribute((const void*)index_list_select_kernel,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_l)) != hipSuccess)
+    if ((e = set_dynamic_lds((const void*)index_list_select_kernel, lds_l)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(index_list_select_kernel, rows_grid, dim3(256), lds_l, stream, seqs, al);
     if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -1664,8 +1672,7 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
         hipLaunchKernelGGL(index_rescore_kernel<false>, dim3(1024), dim3(256), 0, stream, seqs, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     const size_t lds_r = select_long_lds<4>(a);
-    if ((e = hipFuncSetAttribute((const void*)index_select_rescue_kernel,
-                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds_r)) != hipSuccess)
+    if ((e = set_dynamic_lds((const void*)index_select_rescue_kernel, lds_r)) != hipSuccess)
         return e;
     hipLaunchKernelGGL(index_select_rescue_kernel, dim3(512), dim3(256), lds_r, stream, seqs, a);
     return hipGetLastError();

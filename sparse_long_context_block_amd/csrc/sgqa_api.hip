@@ -10,11 +10,31 @@
 
 #include <algorithm>
 #include <initializer_list>
+#include <map>
+#include <mutex>
 #include <utility>
 #include <string>
 
 #include "sgqa.h"
 #include "sgqa_internal.hpp"
+
+namespace sgqa {
+
+hipError_t set_dynamic_lds(const void* kernel, size_t bytes) {
+    static std::mutex mu;
+    static std::map<std::pair<int, const void*>, size_t> set;
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    std::lock_guard<std::mutex> lock(mu);
+    size_t& have = set[{dev, kernel}];
+    if (bytes <= have) return hipSuccess;
+    e = hipFuncSetAttribute(kernel, hipFuncAttributeMaxDynamicSharedMemorySize, (int)bytes);
+    if (e == hipSuccess) have = bytes;
+    return e;
+}
+
+}  // namespace sgqa
 
 namespace {
 
@@ -133,6 +153,7 @@ struct IndexPlan {
     int64_t chunk_rows = 0;     // tiled mode: queries per launch (one key pass)
     size_t frag_off = 0;        // tiled mode: byte offset of the query fragments
     size_t ctl_off = 0;         // tiled mode: byte offset of the failed-row list
+    size_t diag_off = 0;        // tiled mode: byte offset of the diagnostics block
     bool listed = false;        // tiled mode: long rows may use candidate lists
     int32_t list_off = 0, samp_off = 0, tau_off = 0;
     size_t ws = 0;
@@ -215,7 +236,8 @@ IndexPlan plan_index(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
         p.n_split = (int)std::max<int64_t>(1, (max_b + kTiledSplitBlocks - 1) / kTiledSplitBlocks);
         p.frag_off = align_up((size_t)chunk * row_bytes);
         p.ctl_off = p.frag_off + align_up((size_t)chunk * kQueryFragBytes);
-        p.ws = p.ctl_off + align_up((size_t)(1 + chunk * sgqa::kGroups) * 4);
+        p.diag_off = p.ctl_off + align_up((size_t)(1 + chunk * sgqa::kGroups) * 4);
+        p.ws = p.diag_off + align_up((size_t)sgqa::kDiagWords * 4);
         // candidate lists share a key row with one count per segment, the
         // sample and the threshold; rows short enough to hold them all are
         // long enough to be listed
@@ -389,6 +411,8 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     a.part_key = nullptr;
     a.q_frag = nullptr;
     a.ctl = nullptr;
+    a.diag = nullptr;
+    a.diag_clear = 0;
     a.key_stride = p.key_stride;
     a.listed = p.listed ? 1 : 0;
     a.list_off = p.list_off;
@@ -397,6 +421,10 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
     if (p.key_stride > 0) a.part_key = (uint32_t*)ws;
     if (p.frag_off > 0) a.q_frag = (uint4*)((char*)ws + p.frag_off);
     if (p.ctl_off > 0) a.ctl = (uint32_t*)((char*)ws + p.ctl_off);
+    if (p.diag_off > 0) {
+        a.diag = (uint32_t*)((char*)ws + p.diag_off);
+        a.diag_clear = 1;
+    }
     if (p.mode == IndexMode::Tiled) {
         // launches of at most chunk_rows queries (one pass over the key
         // workspace each) and kMaxSeqsPerLaunch entries, filled in call
@@ -422,6 +450,7 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
                 if (used == p.chunk_rows || tab.n == sgqa::kMaxSeqsPerLaunch) {
                     hipError_t e = sgqa::launch_index_tiled(tab, mx, a, st);
                     if (e != hipSuccess) return hip_fail(e, "index_topk launch");
+                    a.diag_clear = 0;
                     tab.n = 0;
                     used = 0;
                     mx = 0;
@@ -573,6 +602,12 @@ const char* sgqa_status_string(int status) {
         case SGQA_ERR_HIP: return "SGQA_ERR_HIP";
         default: return "SGQA_UNKNOWN_STATUS";
     }
+}
+
+int64_t sgqa_index_diag_offset(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs) {
+    if (check_config(cfg) != SGQA_OK || check_seqs(cfg, seqs, n_seqs) != SGQA_OK) return -1;
+    const IndexPlan p = plan_index(cfg, seqs, n_seqs);
+    return p.diag_off > 0 ? (int64_t)p.diag_off : -1;
 }
 
 size_t sgqa_workspace_size(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,

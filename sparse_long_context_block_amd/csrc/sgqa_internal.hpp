@@ -20,6 +20,16 @@ constexpr int kIdxDim = 128;      // indexer dim
 constexpr int kRopeDim = 32;      // indexer rotary span
 constexpr int kMaxTopK = 3072;
 constexpr int kMaxSeqsPerLaunch = 64;
+// diagnostics block of a tiled index call (uint32 words): [0] rows whose
+// candidate lists failed and were scored again in full, [1] reserved, then
+// (query row, group) of the first kDiagRows of them
+constexpr int kDiagWords = 64;
+constexpr int kDiagRows = (kDiagWords - 2) / 2;
+
+// Raise a kernel's dynamic-LDS limit to at least `bytes` on the current
+// device; the limit already set per (device, kernel) is remembered, so the
+// runtime is called only when a launch needs more than before.
+hipError_t set_dynamic_lds(const void* kernel, size_t bytes);
 constexpr int kMaxAttnSplits = 64;
 
 // Per-sequence descriptor as the kernels see it (passed by value in the
@@ -77,6 +87,9 @@ struct IndexArgs {
                                 // row = DevSeq::ws_row + query index
     uint4* q_frag;              // tiled calls: indexer A fragments [launch rows, 4, 64]
     uint32_t* ctl;              // tiled calls: [0] rows whose list failed, [1..] those rows
+    uint32_t* diag;             // tiled calls: the call's diagnostics block (kDiagWords),
+                                // or null
+    int32_t diag_clear;         // this launch is the call's first: clear diag first
     int64_t key_stride;
     int32_t listed;             // tiled calls: long rows may select from candidate lists
     int32_t list_off;           // listed rows: u32 offsets inside a key row of the

@@ -344,8 +344,7 @@ template <bool PAGED>
 static hipError_t launch_sparse_attn_t(const SeqTable& seqs, int64_t max_nq, const AttnArgs& a,
                                        hipStream_t stream) {
     const size_t lds = (size_t)a.topk * sizeof(int32_t);
-    hipError_t e = hipFuncSetAttribute((const void*)sparse_attn_kernel<PAGED>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = set_dynamic_lds((const void*)sparse_attn_kernel<PAGED>, lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(max_nq * kGroups * a.n_split), (unsigned)seqs.n);
     hipLaunchKernelGGL((sparse_attn_kernel<PAGED>), grid, dim3(256), lds, stream, seqs, a);

@@ -263,6 +263,19 @@ def host_k(wl: Workload, kv_rows) -> np.ndarray:
     return rms_rows_bf16_bits(wl.seed, TID_K, rows, D).reshape(-1, G, D)
 
 
+def host_k_group(wl: Workload, kv_rows, g: int) -> np.ndarray:
+    """K cache rows of one group: [n, D] bits (the same values as host_k[:, g])."""
+    kv_rows = np.asarray(kv_rows, dtype=np.int64).reshape(-1)
+    return rms_rows_bf16_bits(wl.seed, TID_K, kv_rows * G + g, D)
+
+
+def host_v_group(wl: Workload, kv_rows, g: int) -> np.ndarray:
+    """V cache rows of one group: [n, D] bits (the same values as host_v[:, g])."""
+    kv_rows = np.asarray(kv_rows, dtype=np.int64).reshape(-1)
+    idx = (kv_rows[:, None] * (G * D) + g * D + np.arange(D)[None, :]).astype(np.uint64)
+    return normal_bf16_bits(wl.seed, TID_V, idx)
+
+
 def _flat(rows, width):
     rows = np.asarray(rows, dtype=np.int64).reshape(-1)
     return (rows[:, None] * width + np.arange(width)[None, :]).astype(np.uint64)

@@ -23,16 +23,16 @@ def oracle_config(wl: W.Workload) -> O.Config:
                     softmax_scale=float(np.float32(1.0 / np.sqrt(192.0))))
 
 
-def run_steps(wl: W.Workload, di, cfg, use_forward: bool = False):
+def run_steps(wl: W.Workload, di, cfg, use_forward: bool = False, ws=None):
     seqs = lib_seqs(wl)
     if use_forward:
         sg.forward(cfg, seqs, di["proxy_k"], di["logits"], di["store"], di["q_idx"], di["w"],
                    di["sel"], di["q"], di["k"], di["v"], di["out"], lse=di["lse"],
-                   sel_scores=di["sel_scores"])
+                   sel_scores=di["sel_scores"], ws=ws)
     else:
         sg.compress(cfg, seqs, di["proxy_k"], di["logits"], di["store"])
         sg.index_topk(cfg, seqs, di["q_idx"], di["w"], di["store"], di["sel"],
-                      sel_scores=di["sel_scores"], q_hat_out=di["q_hat"])
+                      sel_scores=di["sel_scores"], q_hat_out=di["q_hat"], ws=ws)
         sg.sparse_attn(cfg, seqs, di["q"], di["k"], di["v"], di["sel"], di["out"], lse=di["lse"])
     torch.cuda.synchronize()
 
@@ -119,6 +119,7 @@ class Checker:
         else:
             stored, exact = store_exact
         s_lo_all, s_hi_all = P.rounding_interval(exact[:b_max], wl.store_q8, P.REL_STORE)
+        sb = P.StoreBounds(s_lo_all, s_hi_all)
         qrows = s.q_offset + qs
         qi_bits = W.host_q_idx(wl, qrows)
         w = W.host_w(wl, qrows).astype(np.float64)
@@ -141,8 +142,8 @@ class Checker:
             for g in range(4):
                 where = f"{wl.name} seq {si} t={t} g={g}"
                 s_ref = O.block_scores(qh[n_i, g], w[n_i, g], stored[:b])
-                lo, hi = P.score_bounds(q_lo[n_i, g], q_hi[n_i, g], s_lo_all[:b], s_hi_all[:b],
-                                        w[n_i, g])
+                lo, hi = P.score_bounds(q_lo[n_i, g], q_hi[n_i, g], None, None, w[n_i, g],
+                                        sb=sb, b=b)
                 sel_gpu = self.sel[row, g]
                 P.check_selection(sel_gpu, b, K, s_ref, lo, hi, where)
                 r = P.check_scores(self.sel_scores[row, g], sel_gpu, s_ref, lo, hi, where)
@@ -156,15 +157,13 @@ class Checker:
             if not check_attn:
                 continue
             # attention of row t for the 4 groups over the (validated) selections
-            sets = [O.token_set(sr, t, B) for sr in sel_ref_all]
-            toks = np.unique(np.concatenate(sets))
-            kk = nu.bf16_bits_to_f64(W.host_k(wl, s.kv_offset + toks))
-            vv = nu.bf16_bits_to_f64(W.host_v(wl, s.kv_offset + toks))
             q = nu.bf16_bits_to_f64(q_main[n_i])
             for g in range(4):
-                u = np.searchsorted(toks, sets[g])
+                u = O.token_set(sel_ref_all[g], t, B)
+                kk = nu.bf16_bits_to_f64(W.host_k_group(wl, s.kv_offset + u, g))
+                vv = nu.bf16_bits_to_f64(W.host_v_group(wl, s.kv_offset + u, g))
                 heads = slice(16 * g, 16 * g + 16)
-                o, l = O.attend(q[heads], kk[u, g], vv[u, g], ocfg.softmax_scale)
+                o, l = O.attend(q[heads], kk, vv, ocfg.softmax_scale)
                 if gate_bits is not None:
                     o = O.gate(o, gate_bits[row, heads])
                 self._o_ref.append(o)

@@ -23,8 +23,12 @@ valid:
    output; where it differs but is valid, against the oracle's attention over
    the GPU's (validated) set.
 
-Attention outputs: max |diff| <= 2e-2 and ||diff||_F / ||ref||_F <= 1e-2 over
-the compared tensor; log-sum-exp within 1e-3 absolute.
+Attention outputs, per (query row, head) vector of 192 values: the relative
+error ||diff|| / ||ref|| <= 1e-2 and every element within 2e-2 * max |ref| of
+that vector, besides max |diff| <= 2e-2 over everything compared; the
+log-sum-exp within 1e-3 absolute.  A single ratio over all rows stacked would
+be dominated by the early rows (fewer than B tokens attended, outputs near 1)
+and would let a large error on the long rows (outputs near 0.02) through.
 """
 from __future__ import annotations
 
@@ -71,15 +75,30 @@ def check_rounded(gpu_vals: np.ndarray, exact: np.ndarray, q8: bool, rel: float,
             "max_abs": float(np.abs(diff).max()) if diff.size else 0.0}
 
 
-def score_bounds(q_lo, q_hi, s_lo, s_hi, w):
+class StoreBounds:
+    """Midpoints and radii of the admissible store values [s_lo, s_hi]
+    ([b, Di]), computed once per sequence so that bounding one (query, group)
+    row costs only small matrix products."""
+
+    def __init__(self, s_lo, s_hi):
+        self.sc = (s_lo + s_hi) / 2
+        self.sr = (s_hi - s_lo) / 2
+        self.abs_sc = np.abs(self.sc)
+
+
+def score_bounds(q_lo, q_hi, s_lo, s_hi, w, sb: StoreBounds = None, b: int = None):
     """Interval bounds of sum_i w_i relu(q_i . S_r) over admissible q in
     [q_lo, q_hi] ([Hi, Di]) and S in [s_lo, s_hi] ([b, Di]); returns
-    (lo [b], hi [b])."""
+    (lo [b], hi [b]).  With `sb` (the store's precomputed midpoints and
+    radii) the first `b` store rows are used and s_lo / s_hi are ignored."""
     qc, qr = (q_lo + q_hi) / 2, (q_hi - q_lo) / 2
-    sc, sr = (s_lo + s_hi) / 2, (s_hi - s_lo) / 2
+    if sb is None:
+        sb = StoreBounds(s_lo, s_hi)
+        b = sb.sc.shape[0]
+    sc, sr, abs_sc = sb.sc[:b], sb.sr[:b], sb.abs_sc[:b]
     dot = sc @ qc.T
-    rad = np.abs(sc) @ qr.T + sr @ np.abs(qc).T + sr @ qr.T
-    rad = rad + ACC_REL * (np.abs(sc) @ np.abs(qc).T) + 1e-30
+    rad = abs_sc @ qr.T + sr @ np.abs(qc).T + sr @ qr.T
+    rad = rad + ACC_REL * (abs_sc @ np.abs(qc).T) + 1e-30
     dl, dh = np.maximum(dot - rad, 0.0), np.maximum(dot + rad, 0.0)
     w = np.asarray(w, dtype=np.float64)[None, :]
     lo = np.where(w >= 0, w * dl, w * dh).sum(axis=1)
@@ -135,14 +154,33 @@ def check_scores(gpu_scores: np.ndarray, sel: np.ndarray, s_ref, s_lo, s_hi, whe
 
 def check_attention(o_gpu: np.ndarray, o_ref: np.ndarray, lse_gpu=None, lse_ref=None,
                     what: str = "attention") -> dict:
-    d = o_gpu - o_ref
+    """o_* [..., D]: every vector along the last axis is one (row, head)
+    output; lse_* the matching [...] log-sum-exps."""
+    o_gpu = np.asarray(o_gpu, dtype=np.float64)
+    o_ref = np.asarray(o_ref, dtype=np.float64)
+    assert o_gpu.shape == o_ref.shape, f"{what}: shapes {o_gpu.shape} vs {o_ref.shape}"
+    d = (o_gpu - o_ref).reshape(-1, o_ref.shape[-1])
+    r = o_ref.reshape(-1, o_ref.shape[-1])
+    assert np.all(np.isfinite(o_gpu)), f"{what}: non-finite outputs"
     max_abs = float(np.abs(d).max())
-    rel = float(np.linalg.norm(d) / max(np.linalg.norm(o_ref), 1e-30))
     assert max_abs <= O_MAX_ABS, f"{what}: max |diff| {max_abs} > {O_MAX_ABS}"
-    assert rel <= O_REL_FRO, f"{what}: relative Frobenius {rel} > {O_REL_FRO}"
-    out = {"max_abs": max_abs, "rel_fro": rel}
+    vec_rel = np.linalg.norm(d, axis=1) / np.maximum(np.linalg.norm(r, axis=1), 1e-30)
+    worst = int(np.argmax(vec_rel))
+    assert vec_rel[worst] <= O_REL_FRO, (
+        f"{what}: vector {worst} of {r.shape[0]}: ||diff|| / ||ref|| {vec_rel[worst]} > {O_REL_FRO}")
+    scale = np.abs(r).max(axis=1)
+    elem = np.abs(d).max(axis=1) / np.maximum(scale, 1e-30)
+    worst_e = int(np.argmax(elem))
+    assert elem[worst_e] <= O_MAX_ABS, (
+        f"{what}: vector {worst_e}: max |diff| {np.abs(d[worst_e]).max()} above "
+        f"{O_MAX_ABS} x max |ref| {scale[worst_e]}")
+    rel = float(np.linalg.norm(d) / max(np.linalg.norm(r), 1e-30))
+    out = {"max_abs": max_abs, "rel_fro": rel, "vectors": int(r.shape[0]),
+           "max_vec_rel": float(vec_rel[worst]), "max_elem_rel": float(elem[worst_e])}
     if lse_gpu is not None:
-        dl = float(np.abs(lse_gpu - lse_ref).max())
+        lg = np.asarray(lse_gpu, dtype=np.float64)
+        assert np.all(np.isfinite(lg)), f"{what}: non-finite log-sum-exp"
+        dl = float(np.abs(lg - np.asarray(lse_ref, dtype=np.float64)).max())
         assert dl <= LSE_ABS, f"{what}: lse diff {dl} > {LSE_ABS}"
         out["lse_max_abs"] = dl
     return out

@@ -165,14 +165,20 @@ def test_workspace_size_invalid_args_is_zero(L):
 
 def test_prefill_key_workspace(L):
     # prefills of 1024+ queries keep 4-byte score keys per (row, group,
-    # candidate), each query's 16 x 128 bf16 indexer rows and a list of rows
+    # candidate), each query's 16 x 128 bf16 indexer rows, a list of rows
     # to score again (a count and one word per row and group, rounded up to
-    # 256 B) in the workspace; compression and attention need none
+    # 256 B) and the 256-byte diagnostics block in the workspace; compression
+    # and attention need none
     cfg = sg.config()
     # key rows: 1023 candidates padded to 1088 (64 x an odd count)
-    need = 8192 * 4 * 1088 * 4 + 8192 * 16 * 128 * 2 + (1 + 8192 * 4) * 4 // 256 * 256 + 256
+    diag = 8192 * 4 * 1088 * 4 + 8192 * 16 * 128 * 2 + (1 + 8192 * 4) * 4 // 256 * 256 + 256
+    need = diag + 256
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_INDEX_TOPK) == need
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_FORWARD) == need
+    assert sg.index_diag_offset(cfg, [sg.seq(8192)]) == diag
+    # decode-sized calls keep no diagnostics block
+    assert sg.index_diag_offset(cfg, [sg.seq(1, pos0=200_000)]) is None
+    assert sg.index_diag_offset(sg.config(block_size=3), [sg.seq(8192)]) is None
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_COMPRESS) == 0
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_SPARSE_ATTN) == 0
     # long prefills run in passes over query rows: the keys stay within 4 GiB
@@ -298,7 +304,119 @@ def test_binding_store_format():
     assert cfg.store_q8 == 2
     with pytest.raises(TypeError):
         sg._store_ptr(cfg, torch.zeros(4, 128, dtype=torch.bfloat16))
-    with pytest.raises(ValueError):
-        sg._store_ptr(cfg, torch.zeros(4, 128, dtype=torch.uint8))      # not a device tensor
+    with pytest.raises(ValueError):                                   # not a device tensor
+        sg._addrs([sg._store_ptr(cfg, torch.zeros(4, 128, dtype=torch.uint8))])
     with pytest.raises(TypeError):
         sg._store_ptr(sg.config(store_q8=1), torch.zeros(4, 128, dtype=torch.uint8))
+
+
+# ---------------------------------------------------------------------------
+# the binding checks every tensor's extents against the config and the
+# sequences before it calls the library (the C ABI sees bare pointers); the
+# checks run before the device check, so CPU tensors exercise them here
+# ---------------------------------------------------------------------------
+
+def _bf(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.bfloat16)
+
+
+def _f32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.float32)
+
+
+def _i32(*shape):
+    import torch
+    return torch.zeros(shape, dtype=torch.int32)
+
+
+def _attn_args(nq=40, rows=64, K=512):
+    return dict(q=_bf(nq, 64, 192), k_cache=_bf(rows, 4, 192), v_cache=_bf(rows, 4, 192),
+                sel=_i32(nq, 4, K), out=_bf(nq, 64, 192), lse=_f32(nq, 64))
+
+
+def _seqs_for_shapes():
+    # two sequences: query rows up to 40, cache rows up to 64, store rows up to 8
+    return [sg.Seq(q_offset=0, n_q=8, pos0=24, cache_len=32, kv_offset=0, kv_capacity=32,
+                   store_offset=0, store_capacity=4),
+            sg.Seq(q_offset=32, n_q=8, pos0=0, cache_len=8, kv_offset=32, kv_capacity=32,
+                   store_offset=4, store_capacity=4)]
+
+
+def test_binding_accepts_exact_shapes_up_to_the_device_check():
+    cfg = sg.config()
+    with pytest.raises(ValueError, match="device"):
+        sg.sparse_attn(cfg, _seqs_for_shapes(), **_attn_args())
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("q", _bf(39, 64, 192)),              # fewer rows than the last query row
+    ("q", _bf(40, 64, 128)),              # head_dim
+    ("q", _bf(40, 60, 192)),              # heads
+    ("k_cache", _bf(63, 4, 192)),         # fewer rows than kv_offset + kv_capacity
+    ("v_cache", _bf(64, 8, 192)),         # groups
+    ("sel", _i32(40, 4, 256)),            # last dim is not topk_blocks
+    ("sel", _i32(39, 4, 512)),
+    ("out", _bf(40, 64 * 192)),           # rank
+    ("lse", _f32(40, 32)),
+])
+def test_binding_rejects_wrong_attention_extents(name, bad):
+    args = _attn_args()
+    args[name] = bad
+    with pytest.raises(ValueError, match=name):
+        sg.sparse_attn(sg.config(), _seqs_for_shapes(), **args)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("q_idx", _bf(40, 4, 4, 64)), ("q_idx", _bf(39, 4, 4, 128)), ("w", _f32(40, 4, 2)),
+    ("store", __import__("torch").zeros((7, 128), dtype=__import__("torch").uint8)),
+    ("sel_scores", _f32(40, 4, 100)), ("q_hat_out", _bf(40, 4, 4, 127)),
+    ("rms_gamma", _bf(64)),
+])
+def test_binding_rejects_wrong_index_extents(name, bad):
+    import torch
+    args = dict(q_idx=_bf(40, 4, 4, 128), w=_f32(40, 4, 4),
+                store=torch.zeros((8, 128), dtype=torch.uint8), sel=_i32(40, 4, 512))
+    args[name] = bad
+    with pytest.raises(ValueError, match=name):
+        sg.index_topk(sg.config(), _seqs_for_shapes(), **args)
+
+
+@pytest.mark.parametrize("name,bad", [
+    ("proxy_k", _bf(63, 128)), ("comp_logits", _f32(64, 64)), ("ln_gamma", _bf(127)),
+    ("store", __import__("torch").zeros((8, 64), dtype=__import__("torch").uint8)),
+])
+def test_binding_rejects_wrong_compress_extents(name, bad):
+    import torch
+    args = dict(proxy_k=_bf(64, 128), comp_logits=_f32(64, 128),
+                store=torch.zeros((8, 128), dtype=torch.uint8))
+    args[name] = bad
+    with pytest.raises(ValueError, match=name):
+        sg.compress(sg.config(), _seqs_for_shapes(), **args)
+
+
+def test_binding_checks_store_dtype_against_the_config():
+    import torch
+    args = dict(proxy_k=_bf(64, 128), comp_logits=_f32(64, 128),
+                store=torch.zeros((8, 128), dtype=torch.uint8))
+    with pytest.raises(TypeError, match="store"):
+        sg.compress(sg.config(store_q8=1), _seqs_for_shapes(), **args)
+
+
+def test_binding_rejects_wrong_page_pools():
+    import torch
+    seqs = [sg.Seq(q_offset=0, n_q=8, pos0=0, cache_len=8, kv_offset=0, kv_capacity=32,
+                   store_offset=0, store_capacity=4)]
+    table = _i32(2)
+    base = dict(q=_bf(8, 64, 192), k_pages=_bf(5, 16, 4, 192), v_pages=_bf(5, 16, 4, 192),
+                page_table=table, sel=_i32(8, 4, 512), out=_bf(8, 64, 192))
+    bad = dict(base, k_pages=_bf(5, 8, 4, 192))          # pages of 8 tokens
+    with pytest.raises(ValueError, match="k_pages"):
+        sg.sparse_attn_paged(sg.config(), seqs, **bad)
+    bad = dict(base, v_pages=_bf(4, 16, 4, 192))         # pools of different sizes
+    with pytest.raises(ValueError, match="v_pages"):
+        sg.sparse_attn_paged(sg.config(), seqs, **bad)
+    with pytest.raises(ValueError, match="device"):
+        sg.sparse_attn_paged(sg.config(), seqs, **base)
+    del torch

@@ -1,28 +1,49 @@
 """Full-size workloads through sgqa_forward (the launch configuration the
 benchmark times), checked against the oracle on sampled rows: the 8K prefill,
 the 64K prefill at B=8 and its B=1 ablation, 64-sequence decode at up to 256K
-tokens, and the 8K-query chunk over a 1M-token cache."""
+tokens, and the 8K-query chunk over a 1M-token cache.
+
+The sampled rows are stratified (rows with fewer than B tokens, first and
+last tokens of blocks, the k*B threshold, the last query, uniform draws).
+Where the index step keeps its diagnostics block, the rows whose candidate
+lists failed and were scored again in full are read back from the device and
+checked too, and the 1M-token chunk must have taken that path at least once.
+"""
 import time
 
 import numpy as np
 import pytest
 import torch
 
+import sparse_long_context_block_amd as sg
 from synth import workloads as W
 
-from .gpu_checks import Checker, log, prepare, run_steps, stratified_rows
+from .gpu_checks import Checker, lib_seqs, log, prepare, run_steps, stratified_rows
 
 pytestmark = pytest.mark.gpu
 
 
+def _aligned_ws(n):
+    buf = torch.empty(max(n, 1) + 256, dtype=torch.uint8, device="cuda")
+    return buf[(-buf.data_ptr()) % 256:][:max(n, 1)]
+
+
 def _forward_then_index(wl, di, cfg):
-    # the timed path: one sgqa_forward; then the split index call once more
-    # only to expose q_hat for the check (same store, same selections)
-    run_steps(wl, di, cfg, use_forward=True)
+    """The timed path: one sgqa_forward on a workspace of our own, whose
+    diagnostics block (if any) is read back; then the split index call once
+    more only to expose q_hat for the check (same store, same selections)."""
+    seqs = lib_seqs(wl)
+    ws = _aligned_ws(sg.workspace_size(cfg, seqs, sg.OP_FORWARD))
+    off = sg.index_diag_offset(cfg, seqs)
+    if off is not None:
+        ws[off:off + 256].fill_(0xFF)          # the call must clear it
+    run_steps(wl, di, cfg, use_forward=True, ws=ws)
+    diag = sg.index_diagnostics(ws, off) if off is not None else None
     out = di["out"].clone()
     sel = di["sel"].clone()
     run_steps(wl, di, cfg, use_forward=False)
     assert torch.equal(out, di["out"]) and torch.equal(sel, di["sel"])
+    return diag
 
 
 def _check(name, rows_per_seq, seqs=None, store_blocks=None, seed=3):
@@ -30,14 +51,19 @@ def _check(name, rows_per_seq, seqs=None, store_blocks=None, seed=3):
     wl = W.make(name)
     log("case", name, "preparing")
     di, cfg = prepare(wl)
-    _forward_then_index(wl, di, cfg)
-    log("  gpu done", round(time.time() - t0, 1), "s")
+    diag = _forward_then_index(wl, di, cfg)
+    log("  gpu done", round(time.time() - t0, 1), "s; index diagnostics", diag)
     ck = Checker(wl, di, cfg)
     rng = np.random.default_rng(seed)
     seq_ids = range(len(wl.seqs)) if seqs is None else seqs
+    rescored = 0
     for si in seq_ids:
         s = wl.seqs[si]
         qs = stratified_rows(s, wl.block_size, wl.topk, rows_per_seq, rng)
+        if diag:
+            extra = [r - s.q_offset for r, _ in diag["rows"] if s.q_offset <= r < s.q_offset + s.n_q]
+            rescored += len(set(extra))
+            qs = np.unique(np.concatenate([qs, np.asarray(extra, dtype=np.int64)]))
         t_max = s.pos0 + int(qs.max())
         stored, exact = ck.oracle_store(s, max(t_max // wl.block_size, s.cache_len // wl.block_size))
         n_st = stored.shape[0]
@@ -46,25 +72,29 @@ def _check(name, rows_per_seq, seqs=None, store_blocks=None, seed=3):
                                       np.arange(max(0, n_st - 64), n_st)]))
         ck.check_store(s, stored, exact, blocks)
         ck.check_seq(si, qs, store_exact=(stored, exact))
+        log("  seq", si, "rows", qs.size, round(time.time() - t0, 1), "s")
     st = ck.finish()
+    st["rescored_rows"] = diag["rescored_rows"] if diag else None
+    st["rescored_checked"] = rescored
     log(" ", name, st, round(time.time() - t0, 1), "s")
     return st
 
 
 @pytest.mark.timeout(900)
 def test_prefill_8k_bench_configuration():
-    _check("prefill_8k", 48)
+    _check("prefill_8k", 256)
 
 
 @pytest.mark.timeout(900)
 def test_prefill_64k():
-    st = _check("prefill_64k", 40, store_blocks=2048)
-    assert st["sel_rows"] == 160
+    st = _check("prefill_64k", 512, store_blocks=2048)
+    assert st["rows"] >= 512 and st["sel_rows"] == 4 * st["rows"]
 
 
 @pytest.mark.timeout(900)
 def test_prefill_64k_block_size_one():
-    _check("prefill_64k_b1", 24, store_blocks=4096)
+    st = _check("prefill_64k_b1", 256, store_blocks=4096)
+    assert st["rows"] >= 256
 
 
 @pytest.mark.timeout(900)
@@ -75,4 +105,9 @@ def test_decode_64_sequences():
 
 @pytest.mark.timeout(900)
 def test_chunk_over_1m_cache():
-    _check("chunk_1m", 24, store_blocks=4096)
+    st = _check("chunk_1m", 256, store_blocks=4096)
+    assert st["rows"] >= 256
+    # the chunk's long rows go through candidate lists; some lists cannot give
+    # the exact top k and those rows are scored again over every candidate:
+    # the device counted them and the checked rows include them
+    assert st["rescored_rows"] >= 1 and st["rescored_checked"] >= 1

@@ -81,8 +81,8 @@ def test_listed_long_rows(name):
 
 
 def test_decode_one_workgroup_per_cu():
-    # 64 sequences x 4 groups = 256 unsplit attention workgroups: the
-    # eight-wavefront gather
+    # 64 sequences x 4 groups = 256 (sequence, group) units, enough to fill
+    # the CUs, so the gather runs unsplit (no partials, no merge kernel)
     st = _run_and_check("decode_64_small", n_rows=1, check_all_store=False)
     assert st["rows"] >= 64
 

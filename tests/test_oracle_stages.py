@@ -370,6 +370,65 @@ def test_gather_equals_dense_mask_formulation():
         assert np.allclose(out["o"][:, g * hg:(g + 1) * hg], o, rtol=1e-12, atol=1e-12)
 
 
+def test_attend_lse_closed_forms():
+    # equal logits (q = 0): the normaliser over n tokens is ln(n) exactly;
+    # one token: the logit itself; two tokens at z and z - ln 3 with z = 1000
+    # (exp(z) overflows): z + ln(4/3), which needs the maximum term
+    rng = np.random.default_rng(11)
+    for n in (1, 7, 4104):
+        k = rng.standard_normal((n, 16))
+        v = rng.standard_normal((n, 16))
+        o, lse = O.attend(np.zeros((3, 16)), k, v, 0.25)
+        assert np.allclose(lse, math.log(n), rtol=0, atol=1e-12)
+        assert np.allclose(o, v.mean(axis=0)[None, :], rtol=1e-12, atol=1e-12)
+    q = rng.standard_normal((2, 8))
+    k = rng.standard_normal((1, 8))
+    _, lse = O.attend(q, k, rng.standard_normal((1, 8)), 0.5)
+    assert np.allclose(lse, 0.5 * (q @ k[0]), rtol=1e-14, atol=1e-14)
+    q = np.zeros((1, 2))
+    q[0, 0] = 1.0
+    k = np.array([[1000.0, 0.0], [1000.0 - math.log(3.0), 0.0]])
+    o, lse = O.attend(q, k, np.eye(2), 1.0)
+    assert np.isfinite(lse).all()
+    assert abs(lse[0] - (1000.0 + math.log(4.0 / 3.0))) < 1e-9
+    assert np.allclose(o[0], [0.75, 0.25], rtol=0, atol=1e-12)
+
+
+def _masked_logsumexp(q, k, mask, scale):
+    """torch.logsumexp over the scaled float64 logits of the allowed keys:
+    q [T, h, D] against k [T, D] with mask [T, T] (query, key)."""
+    z = torch.einsum("thd,ud->thu", torch.from_numpy(q), torch.from_numpy(k)) * scale
+    z = z.masked_fill(~torch.from_numpy(mask)[:, None, :], float("-inf"))
+    return torch.logsumexp(z, dim=-1).numpy()
+
+
+def test_attend_lse_matches_library_logsumexp():
+    # every block selected (dense causal, the t < B rows included) and a
+    # sparse selection: the oracle's lse is the natural-log normaliser of
+    # exactly the attended keys
+    for topk, seed in ((1000, 4), (3, 5)):
+        cfg = O.Config(num_q_heads=8, num_kv_groups=2, head_dim=16, block_size=4, topk_blocks=topk)
+        T = 48
+        q, k, v, qi, w, kp, lg = _small_inputs(T, cfg, seed=seed)
+        out = O.forward(cfg, q, k, v, qi, w, kp, lg)
+        qf, kf = nu.bf16_bits_to_f64(q), nu.bf16_bits_to_f64(k)
+        hg = cfg.heads_per_group
+        for g in range(cfg.num_kv_groups):
+            mask = np.zeros((T, T), dtype=bool)
+            for t in range(T):
+                for r in out["sel"][t, g]:
+                    if r >= 0:
+                        mask[t, 4 * r:4 * r + 4] = True
+                mask[t, 4 * (t // 4):t + 1] = True
+            if topk == 1000:
+                assert np.array_equal(mask, np.tril(np.ones((T, T), dtype=bool)))
+            ref = _masked_logsumexp(qf[:, g * hg:(g + 1) * hg], kf[:, g], mask, cfg.softmax_scale)
+            assert np.allclose(out["lse"][:, g * hg:(g + 1) * hg], ref, rtol=1e-13, atol=1e-13)
+        # row 0 attends to itself only
+        z0 = (qf[0, 0] @ kf[0, 0]) * cfg.softmax_scale
+        assert abs(out["lse"][0, 0] - z0) < 1e-13
+
+
 def test_future_tokens_do_not_change_a_query():
     cfg = O.Config(num_q_heads=8, num_kv_groups=2, head_dim=16, block_size=4, topk_blocks=2)
     T = 40

@@ -56,3 +56,13 @@ def test_seq_lengths_range():
     L = synth.seq_lengths(0, 64, 131072, 262144)
     assert L.min() >= 131072 and L.max() <= 262144
     assert len(set(L.tolist())) == 64
+
+
+def test_group_slices_equal_full_rows():
+    from synth import workloads as W
+    wl = W.make("prefill_8k")
+    rows = np.array([0, 5, 77, 8191, 3000])
+    k, v = W.host_k(wl, rows), W.host_v(wl, rows)
+    for g in range(4):
+        assert np.array_equal(k[:, g], W.host_k_group(wl, rows, g))
+        assert np.array_equal(v[:, g], W.host_v_group(wl, rows, g))
