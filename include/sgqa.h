@@ -229,7 +229,9 @@ int sgqa_index_topk(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs
  * entries after the first -1 are ignored.
  *
  *   q        bf16 [Nq, H, D]
- *   k_cache  bf16 [rows, G, D], v_cache bf16 [rows, G, D]  (row kv_offset + position)
+ *   k_cache  bf16 [rows, G, D], v_cache bf16 [rows, G, D]  (row kv_offset + position);
+ *            a sequence's kv_capacity must be at most 2,796,202 rows
+ *            (SGQA_ERR_UNSUPPORTED otherwise; the paged calls have no such limit)
  *   sel      int32 [Nq, G, K]
  *   out      bf16 [Nq, H, D]    (written)
  *   lse      fp32 [Nq, H] or NULL (natural log)

@@ -315,6 +315,20 @@ AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     return p;
 }
 
+// The gather kernel addresses a contiguous cache's rows with 32-bit byte
+// offsets from the sequence's first row (1536 bytes per row of one tensor).
+constexpr int64_t kMaxGatherRows = (((int64_t)1 << 32) - 1024) / (sgqa::kGroups * sgqa::kHeadDim * 2);
+
+int check_gather_rows(const sgqa_seq* s, int32_t n) {
+    for (int32_t i = 0; i < n; ++i)
+        if (s[i].kv_capacity > kMaxGatherRows)
+            return fail(SGQA_ERR_UNSUPPORTED,
+                        "seqs[%d]: kv_capacity %lld above %lld rows (contiguous K/V caches are "
+                        "addressed with 32-bit offsets per sequence; use the paged calls)",
+                        i, (long long)s[i].kv_capacity, (long long)kMaxGatherRows);
+    return SGQA_OK;
+}
+
 // Tensor rows are read and written with vector accesses of up to 16 bytes.
 int check_aligned(std::initializer_list<std::pair<const void*, const char*>> ptrs) {
     for (const auto& p : ptrs)
@@ -683,6 +697,7 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
     int rc = check_config(cfg);
     if (rc) return rc;
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if ((rc = check_gather_rows(seqs, n_seqs))) return rc;
     if (!q || !k_cache || !v_cache || !sel || !out)
         return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel and out are required");
     if ((rc = check_aligned({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {sel, "sel"}, {out, "out"}, {lse, "lse"}}))) return rc;
@@ -699,6 +714,7 @@ int sgqa_sparse_attn_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
     int rc = check_config(cfg);
     if (rc) return rc;
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if ((rc = check_gather_rows(seqs, n_seqs))) return rc;
     if (!q || !k_cache || !v_cache || !sel || !out || !gate)
         return fail(SGQA_ERR_NULL, "q, k_cache, v_cache, sel, out and gate are required");
     if ((rc = check_aligned({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {sel, "sel"}, {out, "out"}, {lse, "lse"}, {gate, "gate"}}))) return rc;
@@ -738,6 +754,7 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
     int rc = check_config(cfg);
     if (rc) return rc;
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if ((rc = check_gather_rows(seqs, n_seqs))) return rc;
     if (!proxy_k || !comp_logits || !store || !q_idx || !w || !sel || !q || !k_cache ||
         !v_cache || !out)
         return fail(SGQA_ERR_NULL,
@@ -758,6 +775,7 @@ int sgqa_forward_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_s
     int rc = check_config(cfg);
     if (rc) return rc;
     if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if ((rc = check_gather_rows(seqs, n_seqs))) return rc;
     if (!proxy_k || !comp_logits || !store || !q_idx || !w || !sel || !q || !k_cache ||
         !v_cache || !out || !gate)
         return fail(SGQA_ERR_NULL,

@@ -12,20 +12,27 @@
 // Gather mapping (one workgroup of 4 wavefronts per (query, group, split)):
 // the query's token list (selected blocks in ascending order, then the
 // current block up to t) is cut into 16-token chunks; wavefront w takes
-// chunks w, w+4, ..., with the rows of its next chunk in flight while the
-// current one is processed (two register sets alternate).  Per chunk it
-//   * loads the 16 K rows straight into the A operand of S^T = K Q^T
-//     (v_mfma_f32_16x16x32_bf16; the group's 16 heads are the N dimension,
-//     so every gathered K/V byte serves all 16 heads);
+// chunks w, w+4, ...  A chunk's 16 K rows and 16 V rows (384 bytes each for
+// the group) are fetched with coalesced loads -- each group of four lanes
+// reads 64 contiguous bytes of one row, so a 1 KB load instruction touches
+// about eight cache lines instead of sixteen half lines, one per lane
+// (reading the rows straight into MFMA operand order made every lane a
+// separate cache access and the address unit the bottleneck) -- and written
+// to the wavefront's padded LDS tiles.  Per chunk the wavefront
+//   * reads K back as the A operand of S^T = K Q^T (v_mfma_f32_16x16x32_bf16;
+//     the group's 16 heads are the N dimension, so every gathered K/V byte
+//     serves all 16 heads);
 //   * runs the online softmax on the result layout, where each lane holds 4
 //     tokens of one head, with a lazily raised reference max: the
 //     exponentiated tile is directly the B operand (P^T) of O^T = V^T P^T
 //     (v_mfma_f32_16x16x16bf16_1k), no LDS round trip;
-//   * writes the 16 V rows to a per-wave LDS tile and reads the A operand
-//     V^T back with transposed reads.
-// The four wavefronts' (max, sum, O) are merged in LDS; a split call (decode:
-// few queries) writes partials that attn_merge_kernel combines.  Workgroups
-// run group-major.
+//   * reads V^T from the V tile with transposed reads.
+// Two register sets hold the rows of the next two chunks in flight while a
+// chunk is processed from LDS.  The four wavefronts' (max, sum, O) are merged
+// in LDS; a split call (decode: few queries) writes partials that
+// attn_merge_kernel combines.  Workgroups run group-major.
+#include <type_traits>
+
 #include "attn_common.hpp"
 
 namespace sgqa {
@@ -34,46 +41,90 @@ namespace {
 using namespace dev;
 using namespace attn;
 
-constexpr int kGVStride = kHeadDim + 8;             // bf16 per row of a wave's V tile (100 dwords)
+constexpr int kTileRow = kHeadDim + 8;              // bf16 per padded tile row (100 dwords)
+constexpr int kTileBytes = 16 * kTileRow * 2;          // one 16-row tile: 6,400 B
+constexpr int kWaveLds = 2 * kTileBytes;               // a wavefront's K and V tiles
 constexpr int kWaveBufFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;
-static_assert(16 * kGVStride * 2 <= kWaveBufFloats * 4, "a wave's V tile fits its merge buffer");
+static_assert(kWaveBufFloats * 4 <= kWaveLds, "a wavefront's merge buffer fits its tiles");
+constexpr uint32_t kRowBytes = kGroups * kHeadDim * 2;  // bytes between a tensor's token rows
 
-// Cache row of entry i of the query's token list.  Contiguous caches:
-// sel[j] holds selected block ids, rows are positions (cur0 = first position
-// of the current block).  Paged caches: sel[j] already holds the pool row of
-// block j's first position, cur0 the pool row of the current block's (a
-// block never straddles a 16-token page).
-__device__ __forceinline__ int64_t token_at(int64_t i, int n_sel, int shift_b, int B, bool paged,
-                                            const int32_t* sel, int64_t cur0) {
-    const int64_t j = i >> shift_b;
-    if (j < n_sel) return (paged ? (int64_t)sel[j] : (int64_t)sel[j] * B) + (i & (B - 1));
-    return cur0 + (i - ((int64_t)n_sel << shift_b));
-}
-
-// K/V rows of chunk c for this lane (token 16c + m; K dims 32kk + 8qq, V
-// dims 8(qq + 4j)); chunks past the token list read the current token (row
-// t_row), whose values stay finite and are masked.  Rows are clamped to
-// [0, row_max], so malformed ids never read outside the cache or pool.
-struct GatherRegs {
-    uint4 k[6], v[6];
+// Token list of a (query, group): entry i < n_sel*B is token i%B of block
+// sel[i/B] (contiguous caches: sel holds block ids; paged: the pool row of
+// the block's first position), later entries are the current block's tokens
+// up to t.  Entries past the list, or chunks at or past c_hi, read row t_row
+// (finite values, masked).  Rows are clamped to [0, row_max], so malformed
+// ids never read outside the cache or the pool.
+struct ChunkMap {
+    const int32_t* sel_lds;
+    int n_sel, shift_b, n_tok, c_hi;
+    int64_t cur0, t_row, row_max;
 };
 
-__device__ __forceinline__ GatherRegs gather_chunk(int64_t c, int m, int qq, int64_t n_tok, int n_sel, int shift_b,
-                                                   int B, bool paged, const int32_t* sel_lds, int64_t cur0,
-                                                   int64_t t_row, int64_t row_max, const uint16_t* kbase,
-                                                   const uint16_t* vbase) {
-    constexpr int64_t kRowStride = (int64_t)kGroups * kHeadDim;
-    const int64_t ti = 16 * c + m;
-    int64_t tok = ti < n_tok ? token_at(ti, n_sel, shift_b, B, paged, sel_lds, cur0) : t_row;
-    tok = tok < 0 ? 0 : (tok > row_max ? row_max : tok);
-    const uint16_t* krow = kbase + tok * kRowStride + 8 * qq;
-    const uint16_t* vrow = vbase + tok * kRowStride;
-    GatherRegs r;
+// Cache row (contiguous: relative to the sequence's first row; paged: pool
+// row) of token 16c + tau of the list.  Branch-free: the selection entry is
+// read for every lane (index 0 when the token is not a historical one).
+__device__ __forceinline__ uint32_t token_row(int c, int tau, bool paged, const ChunkMap& cm) {
+    const int ti = 16 * c + tau;
+    const bool listed = (c < cm.c_hi) & (ti < cm.n_tok);
+    const int j = ti >> cm.shift_b;
+    const bool hist = j < cm.n_sel;
+    const int64_t e = cm.sel_lds[hist ? j : 0];
+    const int64_t within = ti & ((1 << cm.shift_b) - 1);
+    const int64_t tok_h = (paged ? e : e << cm.shift_b) + within;
+    const int64_t tok_c = cm.cur0 + (ti - (cm.n_sel << cm.shift_b));
+    int64_t tok = listed ? (hist ? tok_h : tok_c) : cm.t_row;
+    tok = tok < 0 ? 0 : (tok > cm.row_max ? cm.row_max : tok);
+    return (uint32_t)tok;
+}
+
+// Coalesced piece map.  A tensor's chunk is 16 rows x 24 pieces of 16 bytes;
+// load instruction i (< 6) of lane L fetches piece x = 64 i + L: row
+// tau = x / 24, piece p = x % 24, so consecutive lanes read consecutive
+// 16-byte pieces of a row.  Packed per i: the piece's LDS byte offset in a
+// tile (tau * 400 + 16 p, bits 0..12), its byte offset in the row (16 p,
+// bits 13..21) and tau (bits 22..25).
+__device__ __forceinline__ uint32_t piece_code(int i, int lane) {
+    const int x = 64 * i + lane;
+    const int tau = x / 24, p = x - 24 * (x / 24);
+    return (uint32_t)(tau * kTileRow * 2 + 16 * p) | ((uint32_t)(16 * p) << 13) | ((uint32_t)tau << 22);
+}
+
+// Byte offset from the K (or V) base of this lane's piece i of chunk c:
+// 32-bit for contiguous caches (the host keeps a sequence's capacity below
+// 2^32 / 1536 rows), 64-bit into a page pool.
+template <bool PAGED>
+using RowOff = typename std::conditional<PAGED, uint64_t, uint32_t>::type;
+
+// The rows of chunk c into registers (k[i], v[i]: piece i of the K and V
+// rows): lanes 0..15 find the chunk's 16 rows, every lane takes the rows of
+// its six pieces from them (ds_bpermute).
+// Native vectors (not the HIP uint4 struct, whose copies become memcpys that
+// keep the staging arrays in scratch memory).
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+template <bool PAGED>
+__device__ __forceinline__ void load_chunk(int c, int lane, const uint32_t (&pc)[6], const ChunkMap& cm,
+                                           const char* kbase, const char* vbase, u32x4 (&k)[6], u32x4 (&v)[6]) {
+    const uint32_t row = token_row(c, lane & 15, PAGED, cm);
 #pragma unroll
-    for (int kk = 0; kk < 6; ++kk) r.k[kk] = *(const uint4*)(krow + 32 * kk);
+    for (int i = 0; i < 6; ++i) {
+        const uint32_t tau = pc[i] >> 22;
+        const uint32_t rw = (uint32_t)__builtin_amdgcn_ds_bpermute((int)(tau << 2), (int)row);
+        const RowOff<PAGED> off = (RowOff<PAGED>)rw * kRowBytes + ((pc[i] >> 13) & 0x1FFu);
+        k[i] = *(const u32x4*)(kbase + off);
+        v[i] = *(const u32x4*)(vbase + off);
+    }
+}
+
+// The staged rows into the wavefront's tiles (row tau at tau * 400 bytes).
+__device__ __forceinline__ void store_chunk(const u32x4 (&k)[6], const u32x4 (&v)[6], const uint32_t (&pc)[6],
+                                            char* ktile, char* vtile) {
 #pragma unroll
-    for (int j = 0; j < 6; ++j) r.v[j] = *(const uint4*)(vrow + 8 * (qq + 4 * j));
-    return r;
+    for (int i = 0; i < 6; ++i) {
+        const uint32_t o = pc[i] & 0x1FFFu;
+        *(u32x4*)(ktile + o) = k[i];
+        *(u32x4*)(vtile + o) = v[i];
+    }
 }
 
 struct GatherState {
@@ -83,27 +134,28 @@ struct GatherState {
 };
 
 struct GatherLane {
-    uint16_t* vtile;   // this wavefront's V tile in LDS
-    int tr_off;        // this lane's transposed-read offset in it
-    int m, qq;
-    int64_t n_tok;
+    const char* ktile;   // this wavefront's K tile in LDS
+    const char* vtile;   // and its V tile
+    int k_off;           // this lane's A-operand offset in the K tile (bytes)
+    int tr_off;          // its transposed-read offset in the V tile (bytes)
+    int qq;
+    int n_tok;
     float sl2;
 };
 
-// One 16-token chunk.  The V rows go into the wavefront's tile (100-dword
-// rows: the b128 row writes are conflict-free); the O^T A operand comes out
-// of it with ds_read_b64_tr_b16: lane 16G + 4i + c supplies row 4G + i, dims
-// 4c..4c+3 of a 16-dim block, and lane 16G + j receives dim j of tokens
-// 4G..4G+3 -- row j, k = 4G + i of v_mfma_f32_16x16x16bf16_1k.  The softmax
-// runs on the S^T result layout (lane: tokens 16c + 4qq + i of head m) with
-// a lazily raised reference max; the exponentiated tile is the B operand.
-__device__ __forceinline__ void gather_step(GatherState& st, const GatherRegs& r, const bf16x8 (&qf)[6], int64_t c,
-                                            const GatherLane& gl) {
+// One 16-token chunk from the tiles.  S^T A operand: lane (m, qq) reads row
+// m, dims 32kk + 8qq .. +7 (100-dword rows: the b128 reads of eight lanes
+// fall in distinct banks).  O^T A operand with ds_read_b64_tr_b16: lane
+// 16G + 4i + c supplies row 4G + i, dims 4c..4c+3 of a 16-dim block, and lane
+// 16G + j receives dim j of tokens 4G..4G+3 -- row j, k = 4G + i of
+// v_mfma_f32_16x16x16bf16_1k.  The softmax runs on the S^T result layout
+// (lane: tokens 16c + 4qq + i of head m) with a lazily raised reference max;
+// the exponentiated tile is the B operand.
+__device__ __forceinline__ void gather_step(GatherState& st, const bf16x8 (&qf)[6], int c, const GatherLane& gl) {
     f32x4 s = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-    for (int kk = 0; kk < 6; ++kk) s = mfma_16x16x32(as_bf16x8(r.k[kk]), qf[kk], s);
-#pragma unroll
-    for (int j = 0; j < 6; ++j) *(uint4*)(gl.vtile + gl.m * kGVStride + 8 * (gl.qq + 4 * j)) = r.v[j];
+    for (int kk = 0; kk < 6; ++kk)
+        s = mfma_16x16x32(*(const bf16x8*)(gl.ktile + gl.k_off + 64 * kk), qf[kk], s);
     float xv[4];
     float tmax = -INFINITY;
 #pragma unroll
@@ -135,20 +187,18 @@ __device__ __forceinline__ void gather_step(GatherState& st, const GatherRegs& r
     pb.x = pack_bf16(p[0], p[1]);
     pb.y = pack_bf16(p[2], p[3]);
     const i16x4 pbv = as_i16x4(pb);
-    wave_lds_sync();
 #pragma unroll
     for (int nt = 0; nt < 12; ++nt) {
         const i16x4 av = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(gl.vtile + gl.tr_off + 16 * nt));
+            (__attribute__((address_space(3))) i16x4*)(gl.vtile + gl.tr_off + 32 * nt));
         st.o[nt] = mfma_16x16x16(av, pbv, st.o[nt]);
     }
-    wave_lds_sync();
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArgs a) {
+__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, AttnArgs a) {
     extern __shared__ int32_t sel_lds[];                        // [K]
-    __shared__ float wave_buf[4][kWaveBufFloats];
+    __shared__ __align__(16) char tiles[4][kWaveLds];
     __shared__ int s_nsel;
 
     // group-major order: the workgroups in flight read one group's K/V
@@ -196,10 +246,10 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
         row_max = a.n_pages * kPageTokens - 1;
         __syncthreads();
     }
-    const int64_t n_tok = ((int64_t)n_sel << shift_b) + (t - cur_first + 1);
-    const int64_t n_chunks = (n_tok + 15) >> 4;
-    const int64_t c_lo = (int64_t)split * a.chunks_per_split;
-    const int64_t c_hi = n_chunks < c_lo + a.chunks_per_split ? n_chunks : c_lo + a.chunks_per_split;
+    const int n_tok = (n_sel << shift_b) + (int)(t - cur_first + 1);
+    const int n_chunks = (n_tok + 15) >> 4;
+    const int c_lo = split * a.chunks_per_split;
+    const int c_hi = n_chunks < c_lo + a.chunks_per_split ? n_chunks : c_lo + a.chunks_per_split;
 
     const int w = threadIdx.x >> 6;
     const int lane = lane_id();
@@ -217,30 +267,61 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
     for (int nt = 0; nt < 12; ++nt) st.o[nt] = f32x4{0.f, 0.f, 0.f, 0.f};
     st.m_use = -INFINITY;
     st.lsum = 0.f;
+    char* ktile = tiles[w];
+    char* vtile = tiles[w] + kTileBytes;
     GatherLane gl;
-    gl.vtile = (uint16_t*)wave_buf[w];
-    gl.tr_off = (4 * qq + ((lane >> 2) & 3)) * kGVStride + 4 * (lane & 3);
-    gl.m = m;
+    gl.ktile = ktile;
+    gl.vtile = vtile;
+    gl.k_off = m * kTileRow * 2 + 16 * qq;
+    gl.tr_off = ((4 * qq + ((lane >> 2) & 3)) * kTileRow + 4 * (lane & 3)) * 2;
     gl.qq = qq;
-    gl.n_tok = n_tok;
+    // tokens past this split's chunks are masked (a pair's second chunk may
+    // lie past c_hi; its rows are row t_row's)
+    gl.n_tok = n_tok < 16 * c_hi ? n_tok : 16 * c_hi;
     gl.sl2 = a.scale_log2;
+    // contiguous caches: rows relative to the sequence's first row
     const int64_t row0 = PAGED ? 0 : sq.kv_offset;
-    const uint16_t* kbase = a.k + (row0 * kGroups + g) * kHeadDim;
-    const uint16_t* vbase = a.v + (row0 * kGroups + g) * kHeadDim;
+    const char* kbase = (const char*)(a.k + (row0 * kGroups + g) * kHeadDim);
+    const char* vbase = (const char*)(a.v + (row0 * kGroups + g) * kHeadDim);
+    ChunkMap cm;
+    cm.sel_lds = sel_lds;
+    cm.n_sel = n_sel;
+    cm.shift_b = shift_b;
+    cm.n_tok = n_tok;
+    cm.c_hi = c_hi;
+    cm.cur0 = cur0;
+    cm.t_row = t_row;
+    cm.row_max = row_max;
+    uint32_t pc[6];
+#pragma unroll
+    for (int i = 0; i < 6; ++i) pc[i] = piece_code(i, lane);
 
-    // two register sets alternate: one chunk's rows are in flight while the
-    // other chunk is processed
-    if (c_lo + w < c_hi) {
-        GatherRegs ra = gather_chunk(c_lo + w, m, qq, n_tok, n_sel, shift_b, B, PAGED, sel_lds, cur0, t_row, row_max, kbase,
-                                     vbase);
-        for (int64_t c = c_lo + w; c < c_hi; c += 8) {
-            const GatherRegs rb =
-                gather_chunk(c + 4, m, qq, n_tok, n_sel, shift_b, B, PAGED, sel_lds, cur0, t_row, row_max, kbase, vbase);
-            gather_step(st, ra, qf, c, gl);
-            if (c + 4 >= c_hi) break;
-            ra = gather_chunk(c + 8, m, qq, n_tok, n_sel, shift_b, B, PAGED, sel_lds, cur0, t_row, row_max, kbase, vbase);
-            gather_step(st, rb, qf, c + 4, gl);
-        }
+    // Chunks w, w + 4, ... in pairs.  Two register sets: a set's rows go to
+    // the tiles just before their chunk is processed, and the set is
+    // refilled at once with the chunk eight ahead, so the next two chunks'
+    // rows are in flight while a chunk is processed.  A pair's second chunk
+    // may lie past c_hi (fully masked: it adds nothing); loads of chunks past
+    // the wavefront's last read row t_row (the same lines for every lane).
+    // The loop has a single exit at its end, which keeps the compiler's wait
+    // counts exact: each store waits only for its own set's rows.
+    int c = c_lo + w;
+    if (c < c_hi) {
+        u32x4 ak[6], av[6], bk[6], bv[6];
+        load_chunk<PAGED>(c, lane, pc, cm, kbase, vbase, ak, av);
+        load_chunk<PAGED>(c + 4, lane, pc, cm, kbase, vbase, bk, bv);
+        do {
+            store_chunk(ak, av, pc, ktile, vtile);
+            wave_lds_sync();
+            load_chunk<PAGED>(c + 8, lane, pc, cm, kbase, vbase, ak, av);
+            gather_step(st, qf, c, gl);
+            wave_lds_sync();
+            store_chunk(bk, bv, pc, ktile, vtile);
+            wave_lds_sync();
+            load_chunk<PAGED>(c + 12, lane, pc, cm, kbase, vbase, bk, bv);
+            gather_step(st, qf, c + 4, gl);
+            wave_lds_sync();
+            c += 8;
+        } while (c < c_hi);
     }
     float lsum = st.lsum;
     f32x4 (&o)[12] = st.o;
@@ -253,7 +334,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
 
     // ---- merge the four wavefronts ----
     __syncthreads();
-    float* buf = wave_buf[w];
+    float* buf = (float*)tiles[w];
 #pragma unroll
     for (int nt = 0; nt < 12; ++nt)
 #pragma unroll
@@ -270,7 +351,7 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
         float mw[4], M = -INFINITY;
 #pragma unroll
         for (int ww = 0; ww < 4; ++ww) {
-            mw[ww] = wave_buf[ww][kHeadsPerGroup * kHeadDim + head];
+            mw[ww] = ((const float*)tiles[ww])[kHeadsPerGroup * kHeadDim + head];
             M = fmaxf(M, mw[ww]);
         }
         float L = 0.f, O = 0.f;
@@ -278,8 +359,8 @@ __global__ __launch_bounds__(256) void sparse_attn_kernel(SeqTable seqs, AttnArg
 #pragma unroll
             for (int ww = 0; ww < 4; ++ww) {
                 const float sc = exp2f(mw[ww] - M);
-                L += wave_buf[ww][kHeadsPerGroup * kHeadDim + kHeadsPerGroup + head] * sc;
-                O += wave_buf[ww][e] * sc;
+                L += ((const float*)tiles[ww])[kHeadsPerGroup * kHeadDim + kHeadsPerGroup + head] * sc;
+                O += ((const float*)tiles[ww])[e] * sc;
             }
         }
         const int d = e - head * kHeadDim;

@@ -420,3 +420,19 @@ def test_binding_rejects_wrong_page_pools():
     with pytest.raises(ValueError, match="device"):
         sg.sparse_attn_paged(sg.config(), seqs, **base)
     del torch
+
+
+def test_contiguous_gather_row_limit(L):
+    # contiguous caches are addressed with 32-bit offsets per sequence
+    cfg = sg.config()
+    big = sg.Seq(q_offset=0, n_q=1, pos0=100, cache_len=101, kv_offset=0, kv_capacity=2_796_203,
+                 store_offset=0, store_capacity=12)
+    arr, n = _seqs(big)
+    P = ctypes.c_void_p(FAKE)
+    assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, P, P, P, P, P, None, None, 0, None) == E_UNSUP
+    assert "2796202" in L.sgqa_last_error().decode()
+    ok = sg.Seq(q_offset=0, n_q=1, pos0=100, cache_len=101, kv_offset=0, kv_capacity=2_796_202,
+                store_offset=0, store_capacity=12)
+    arr, n = _seqs(ok)
+    # passes the limit; fails later only for the missing workspace-free NULL out
+    assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, P, P, P, P, None, None, None, 0, None) == E_NULL
