@@ -176,9 +176,23 @@ constexpr int kTiledSplitBlocks = 512;
 struct AttnPlan {
     int n_split = 1;
     int chunks_per_split = 0;
-    int64_t rows = 0;
+    int64_t rows = 0;           // workspace rows: gather queries of one launch
+    bool range_split = false;   // splits are ranges of the token list, one per XCD (pair)
     size_t ws = 0;
 };
+
+// Range splits across XCDs.  Workgroups go to the eight XCDs round-robin in
+// launch order, and the gather grid is (group, query, split)-major, so with
+// 4 or 8 splits every split of every unit runs on the same XCD(s): each
+// XCD's L2 then holds only its split's range of the group's selected rows.
+// Measured on the 64K-token prefill's late rows: 21 TB/s of gathered rows
+// with each XCD's reads confined to an eighth or a quarter of the block
+// range, 9 TB/s unconfined.  Worth it while a sequence's K+V rows of one
+// group (768 B per token) split in four or eight stay near 12 MB, i.e. up to
+// 128K tokens; the partials of at most kRangeSplitPassBytes go per launch.
+constexpr int64_t kRangeSplitMaxTokens = 131072;
+constexpr int64_t kRangeSplitMinUnits = 2048;
+constexpr size_t kRangeSplitPassBytes = (size_t)1 << 30;
 
 // Workspace rows are numbered per launch table (DevSeq::ws_row), so a
 // workspace holds the queries of the largest table, whatever the queries'
@@ -290,9 +304,23 @@ AttnPlan plan_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
     const int64_t max_chunks =
         ((int64_t)c->topk_blocks * c->block_size + c->block_size + 15) / 16;
     const int64_t units = total_q * sgqa::kGroups;
-    // split only calls too small to give each CU a workgroup (measured on the
-    // 64-sequence decode: 256 unsplit workgroups beat 1024 split ones and the
-    // merge they need)
+    int64_t max_cache = 0;
+    for (int32_t i = 0; i < n; ++i)
+        if (s[i].n_q - dense_queries(c, s[i]) > 0) max_cache = std::max(max_cache, s[i].cache_len);
+    if (units >= kRangeSplitMinUnits && max_cache <= kRangeSplitMaxTokens && max_chunks >= 64) {
+        p.range_split = true;
+        p.n_split = max_cache > 65536 ? 8 : 4;
+        p.chunks_per_split = (int)((max_chunks + p.n_split - 1) / p.n_split);
+        const size_t row_bytes =
+            (size_t)sgqa::kGroups * p.n_split * sgqa::kHeadsPerGroup * (sgqa::kHeadDim + 2) * 4;
+        p.rows = std::max<int64_t>(1, std::min<int64_t>(p.rows, (int64_t)(kRangeSplitPassBytes / row_bytes)));
+        const size_t parts = (size_t)p.rows * sgqa::kGroups * p.n_split * sgqa::kHeadsPerGroup;
+        p.ws = align_up(parts * sgqa::kHeadDim * 4) + align_up(parts * 2 * 4);
+        return p;
+    }
+    // otherwise split only calls too small to give each CU a workgroup
+    // (measured on the 64-sequence decode: 256 unsplit workgroups beat 1024
+    // split ones and the merge they need)
     int64_t want = units > 0 ? (256 + units - 1) / units : 1;
     int64_t split = std::min<int64_t>({want, std::max<int64_t>(1, max_chunks / 8),
                                        (int64_t)sgqa::kMaxAttnSplits});
@@ -514,6 +542,33 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
         a.part_o = (float*)ws;
         a.part_ml = (float*)((char*)ws + align_up(parts * sgqa::kHeadDim * 4));
     }
+    // the gather queries in launches of at most p.rows queries (the
+    // workspace rows) and kMaxSeqsPerLaunch entries; a sequence that does not
+    // fit the room left is cut
+    sgqa::SeqTable gt;
+    gt.n = 0;
+    gt.pad_ = 0;
+    int64_t gmax = 0, grows = 0;
+    auto flush_gather = [&]() -> int {
+        if (gt.n == 0) return SGQA_OK;
+        hipError_t e = sgqa::launch_sparse_attn(gt, gmax, a, st);
+        if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
+        if (p.n_split > 1) {
+            sgqa::AttnMergeArgs ma;
+            ma.part_o = a.part_o;
+            ma.part_ml = a.part_ml;
+            ma.gate = a.gate;
+            ma.out = (uint16_t*)out;
+            ma.lse = lse;
+            ma.n_split = p.n_split;
+            e = sgqa::launch_attn_merge(gt, gmax, ma, st);
+            if (e != hipSuccess) return hip_fail(e, "attn_merge launch");
+        }
+        gt.n = 0;
+        gmax = 0;
+        grows = 0;
+        return SGQA_OK;
+    };
     for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
         const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
         // dense-ish leading queries -> tiled kernel
@@ -521,10 +576,6 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
         ut.n = 0;
         ut.pad_ = 0;
         int64_t umax = 0, ublk = 0;
-        sgqa::SeqTable gt;
-        gt.n = 0;
-        gt.pad_ = 0;
-        int64_t gmax = 0, grows = 0;
         for (int32_t i = first; i < first + cnt; ++i) {
             const sgqa_seq& q = s[i];
             const int64_t nd = dense_queries(c, q);
@@ -539,37 +590,37 @@ int run_attn(const sgqa_config* c, const sgqa_seq* s, int32_t n, const AttnPlan&
                 umax = std::max(umax, nd);
                 ublk = std::max(ublk, (q.pos0 + nd - 1) / c->block_size);
             }
-            if (q.n_q - nd > 0) {
-                sgqa::DevSeq& d = gt.s[gt.n++];
-                d.q_offset = q.q_offset + nd;
-                d.n_q = q.n_q - nd;
-                d.pos0 = q.pos0 + nd;
-                d.kv_offset = q.kv_offset;
-                d.store_offset = q.store_offset;
-                d.ws_row = grows;
-                grows += q.n_q - nd;
-                gmax = std::max(gmax, q.n_q - nd);
-            }
         }
         if (ut.n > 0) {
             const int words = (int)(ublk / 32 + 1);
             hipError_t e = sgqa::launch_attn_union(ut, umax, a, words, st);
             if (e != hipSuccess) return hip_fail(e, "sparse_attn (tiled) launch");
         }
-        if (gt.n == 0) continue;
-        hipError_t e = sgqa::launch_sparse_attn(gt, gmax, a, st);
-        if (e != hipSuccess) return hip_fail(e, "sparse_attn launch");
-        if (p.n_split > 1) {
-            sgqa::AttnMergeArgs ma;
-            ma.part_o = a.part_o;
-            ma.part_ml = a.part_ml;
-            ma.gate = a.gate;
-            ma.out = (uint16_t*)out;
-            ma.lse = lse;
-            ma.n_split = p.n_split;
-            e = sgqa::launch_attn_merge(gt, gmax, ma, st);
-            if (e != hipSuccess) return hip_fail(e, "attn_merge launch");
+        for (int32_t i = first; i < first + cnt; ++i) {
+            const sgqa_seq& q = s[i];
+            const int64_t nd = dense_queries(c, q);
+            for (int64_t done = nd; done < q.n_q;) {
+                const int64_t take = std::min(q.n_q - done, p.rows - grows);
+                sgqa::DevSeq& d = gt.s[gt.n++];
+                d.q_offset = q.q_offset + done;
+                d.n_q = take;
+                d.pos0 = q.pos0 + done;
+                d.kv_offset = q.kv_offset;
+                d.store_offset = q.store_offset;
+                d.ws_row = grows;
+                grows += take;
+                done += take;
+                gmax = std::max(gmax, take);
+                if (grows == p.rows || gt.n == sgqa::kMaxSeqsPerLaunch) {
+                    const int rc = flush_gather();
+                    if (rc) return rc;
+                }
+            }
         }
+    }
+    {
+        const int rc = flush_gather();
+        if (rc) return rc;
     }
     return SGQA_OK;
 }

@@ -41,9 +41,16 @@ namespace {
 using namespace dev;
 using namespace attn;
 
-constexpr int kTileRow = kHeadDim + 8;              // bf16 per padded tile row (100 dwords)
-constexpr int kTileBytes = 16 * kTileRow * 2;          // one 16-row tile: 6,400 B
-constexpr int kWaveLds = 2 * kTileBytes;               // a wavefront's K and V tiles
+// Padded tile rows.  K tile: 100 dwords per row, so the b128 operand reads
+// of eight (and of sixteen) consecutive lanes -- rows m, m+1, ... -- start
+// in distinct bank groups.  V tile: 104 dwords per row, so the 8-byte
+// transposed reads of the 16 lanes of a lane group (4 rows x 4 column
+// quads) cover 32 distinct banks.
+constexpr int kTileRow = kHeadDim + 8;                 // K: bf16 per row (100 dwords)
+constexpr int kTileRowV = kHeadDim + 16;               // V: bf16 per row (104 dwords)
+constexpr int kTileBytes = 16 * kTileRow * 2;          // K tile: 6,400 B
+constexpr int kTileBytesV = 16 * kTileRowV * 2;        // V tile: 6,656 B
+constexpr int kWaveLds = kTileBytes + kTileBytesV;     // a wavefront's K and V tiles
 constexpr int kWaveBufFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;
 static_assert(kWaveBufFloats * 4 <= kWaveLds, "a wavefront's merge buffer fits its tiles");
 constexpr uint32_t kRowBytes = kGroups * kHeadDim * 2;  // bytes between a tensor's token rows
@@ -80,9 +87,9 @@ __device__ __forceinline__ uint32_t token_row(int c, int tau, bool paged, const 
 // Coalesced piece map.  A tensor's chunk is 16 rows x 24 pieces of 16 bytes;
 // load instruction i (< 6) of lane L fetches piece x = 64 i + L: row
 // tau = x / 24, piece p = x % 24, so consecutive lanes read consecutive
-// 16-byte pieces of a row.  Packed per i: the piece's LDS byte offset in a
-// tile (tau * 400 + 16 p, bits 0..12), its byte offset in the row (16 p,
-// bits 13..21) and tau (bits 22..25).
+// 16-byte pieces of a row.  Packed per i: the piece's LDS byte offset in the
+// K tile (tau * 400 + 16 p, bits 0..12; the V tile adds 16 tau), its byte
+// offset in the row (16 p, bits 13..21) and tau (bits 22..25).
 __device__ __forceinline__ uint32_t piece_code(int i, int lane) {
     const int x = 64 * i + lane;
     const int tau = x / 24, p = x - 24 * (x / 24);
@@ -116,14 +123,15 @@ __device__ __forceinline__ void load_chunk(int c, int lane, const uint32_t (&pc)
     }
 }
 
-// The staged rows into the wavefront's tiles (row tau at tau * 400 bytes).
+// The staged rows into the wavefront's tiles (row tau at tau * 400 bytes of
+// the K tile, tau * 416 bytes of the V tile).
 __device__ __forceinline__ void store_chunk(const u32x4 (&k)[6], const u32x4 (&v)[6], const uint32_t (&pc)[6],
                                             char* ktile, char* vtile) {
 #pragma unroll
     for (int i = 0; i < 6; ++i) {
         const uint32_t o = pc[i] & 0x1FFFu;
         *(u32x4*)(ktile + o) = k[i];
-        *(u32x4*)(vtile + o) = v[i];
+        *(u32x4*)(vtile + o + ((pc[i] >> 22) << 4)) = v[i];
     }
 }
 
@@ -273,7 +281,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, Attn
     gl.ktile = ktile;
     gl.vtile = vtile;
     gl.k_off = m * kTileRow * 2 + 16 * qq;
-    gl.tr_off = ((4 * qq + ((lane >> 2) & 3)) * kTileRow + 4 * (lane & 3)) * 2;
+    gl.tr_off = ((4 * qq + ((lane >> 2) & 3)) * kTileRowV + 4 * (lane & 3)) * 2;
     gl.qq = qq;
     // tokens past this split's chunks are masked (a pair's second chunk may
     // lie past c_hi; its rows are row t_row's)
