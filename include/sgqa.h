@@ -254,6 +254,27 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                  size_t ws_bytes, void* hip_stream);
 
 /*
+ * sgqa_forward for callers that cannot allocate memory -- code under HIP
+ * graph capture, tight serving loops, harnesses that forbid allocation: the
+ * same three steps with the same arguments and results, but the workspace is
+ * a static 64 MiB device array inside the library (one per GPU, held until
+ * the process ends) instead of a caller buffer.  No memory is allocated or
+ * freed by the call.  Calls whose workspace (sgqa_workspace_size(...,
+ * SGQA_OP_FORWARD)) exceeds 64 MiB return SGQA_ERR_WORKSPACE before any HIP
+ * call; decode-sized calls (e.g. 64 sequences of up to 262,144 cached tokens)
+ * fit.  All calls on one GPU share its array, which keeps the last call's
+ * contents: calls that overlap in time on one GPU (other streams, other
+ * threads) race and must be ordered by the caller.  The first call on each
+ * device resolves that device's copy (hipGetSymbolAddress) with it current.
+ */
+int sgqa_forward_noalloc(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                         const void* proxy_k, const float* comp_logits, const void* ln_gamma,
+                         const void* ln_beta, void* store, const void* q_idx, const float* w,
+                         const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
+                         const void* k_cache, const void* v_cache, void* out, float* lse,
+                         void* hip_stream);
+
+/*
  * Paged caches (page section "Cache capacity: 4,104 reads do not mean 4,104
  * stored tokens": global capacity rounded up to 16-token pages, with page
  * tables).  The per-token tensors live in a pool of n_pages pages of 16

@@ -31,7 +31,7 @@ __all__ = [
     "index_topk", "sparse_attn", "forward", "compress_paged", "sparse_attn_paged", "forward_paged",
     "QkConfig", "qk_config", "qk_prep", "sparse_attn_gated", "forward_gated",
     "LIB_PATH", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_SPARSE_ATTN", "OP_FORWARD",
-    "index_diag_offset", "index_diagnostics",
+    "index_diag_offset", "index_diagnostics", "forward_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgqa.so")
@@ -175,6 +175,9 @@ def lib() -> ctypes.CDLL:
     L.sgqa_abi_version.restype = I32
     L.sgqa_index_diag_offset.argtypes = [cfgp, seqp, I32]
     L.sgqa_index_diag_offset.restype = I64
+    L.sgqa_forward_noalloc.argtypes = [cfgp, seqp, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
+                                       P, P]
+    L.sgqa_forward_noalloc.restype = ctypes.c_int
     _lib = L
     return L
 
@@ -431,6 +434,24 @@ def forward(cfg: Config, seqs: Sequence[Seq], proxy_k, comp_logits, store, q_idx
     ptrs = _addrs(ptrs)
     wsp, wsn, _own = _workspace(cfg, seqs, OP_FORWARD, q.device, ws, stream)
     _check(lib().sgqa_forward(ctypes.byref(cfg), arr, n, *ptrs, wsp, wsn, _stream_ptr(stream)))
+
+
+def forward_noalloc(cfg: Config, seqs: Sequence[Seq], proxy_k, comp_logits, store, q_idx, w, sel, q,
+                    k_cache, v_cache, out, lse=None, sel_scores=None, ln_gamma=None, ln_beta=None,
+                    rms_gamma=None, stream=None) -> None:
+    """sgqa_forward on the library's static 64 MiB scratch: no workspace
+    argument and nothing allocated (for callers that cannot allocate)."""
+    seqs = list(seqs)
+    ext = _Extents(cfg, seqs)
+    arr, n = _seq_array(seqs)
+    ptrs = _forward_ptrs(cfg, ext, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
+                         rms_gamma, sel, sel_scores, q, False) + (
+        _ptr(k_cache, torch.bfloat16, "k_cache", shape=ext.kv()),
+        _ptr(v_cache, torch.bfloat16, "v_cache", shape=ext.kv()),
+        _ptr(out, torch.bfloat16, "out", shape=ext.q()),
+        _ptr(lse, torch.float32, "lse", False, shape=ext.lse()))
+    ptrs = _addrs(ptrs)
+    _check(lib().sgqa_forward_noalloc(ctypes.byref(cfg), arr, n, *ptrs, _stream_ptr(stream)))
 
 
 # ---------------------------------------------------------------------------

@@ -646,6 +646,52 @@ int run_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs, co
 }  // namespace
 
 // ---------------------------------------------------------------------------
+// The workspace of sgqa_forward_noalloc: a file-scope device array, one copy
+// per GPU, held until the process ends.  Host code never passes the array's
+// name to a kernel or a copy (on the host it is only a stand-in for the
+// symbol): each device's address comes from hipGetSymbolAddress, called once
+// per device with that device current, and only that address is used.
+// ---------------------------------------------------------------------------
+constexpr size_t kNoAllocScratchBytes = (size_t)64 << 20;
+static __device__ __align__(256) unsigned char scratch[kNoAllocScratchBytes];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+
+// address of `scratch` on the current device (resolved on the first call
+// per device), or nullptr with the status in *rc
+void* scratch_address(int* rc) {
+    static std::mutex mu;
+    static void* addr[kMaxDevices] = {};
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) {
+        *rc = hip_fail(e, "hipGetDevice");
+        return nullptr;
+    }
+    if (dev < 0 || dev >= kMaxDevices) {
+        *rc = fail(SGQA_ERR_UNSUPPORTED, "device %d above the %d devices the static scratch covers", dev,
+                   kMaxDevices);
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    if (!addr[dev]) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess || !ptr) {
+            *rc = hip_fail(e != hipSuccess ? e : hipErrorInvalidSymbol, "hipGetSymbolAddress(scratch)");
+            return nullptr;
+        }
+        addr[dev] = ptr;
+    }
+    *rc = SGQA_OK;
+    return addr[dev];
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
 // extern "C" entry points
 // ---------------------------------------------------------------------------
 extern "C" {
@@ -815,6 +861,35 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
     return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
                        rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, nullptr, ws,
                        ws_bytes, (hipStream_t)hip_stream);
+}
+
+int sgqa_forward_noalloc(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
+                         const void* proxy_k, const float* comp_logits, const void* ln_gamma,
+                         const void* ln_beta, void* store, const void* q_idx, const float* w,
+                         const void* rms_gamma, int32_t* sel, float* sel_scores, const void* q,
+                         const void* k_cache, const void* v_cache, void* out, float* lse,
+                         void* hip_stream) {
+    int rc = check_config(cfg);
+    if (rc) return rc;
+    if ((rc = check_seqs(cfg, seqs, n_seqs))) return rc;
+    if ((rc = check_gather_rows(seqs, n_seqs))) return rc;
+    if (!proxy_k || !comp_logits || !store || !q_idx || !w || !sel || !q || !k_cache ||
+        !v_cache || !out)
+        return fail(SGQA_ERR_NULL,
+                    "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache and out "
+                    "are required");
+    if ((rc = check_aligned({{proxy_k, "proxy_k"}, {comp_logits, "comp_logits"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}, {q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {out, "out"}, {lse, "lse"}}))) return rc;
+    const size_t need = std::max(plan_index(cfg, seqs, n_seqs).ws, plan_attn(cfg, seqs, n_seqs).ws);
+    if (need > kNoAllocScratchBytes)
+        return fail(SGQA_ERR_WORKSPACE,
+                    "these sequences need %zu bytes of workspace; sgqa_forward_noalloc's static "
+                    "scratch holds %zu (use sgqa_forward with a caller workspace)",
+                    need, kNoAllocScratchBytes);
+    void* ws = scratch_address(&rc);
+    if (!ws) return rc;
+    return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
+                       rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, nullptr, ws,
+                       kNoAllocScratchBytes, (hipStream_t)hip_stream);
 }
 
 int sgqa_forward_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,

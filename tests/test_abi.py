@@ -436,3 +436,19 @@ def test_contiguous_gather_row_limit(L):
     arr, n = _seqs(ok)
     # passes the limit; fails later only for the missing workspace-free NULL out
     assert L.sgqa_sparse_attn(ctypes.byref(cfg), arr, n, P, P, P, P, None, None, None, 0, None) == E_NULL
+
+
+def test_noalloc_forward_rejects_oversized_calls_before_any_hip_call(L):
+    # an 8K-token prefill needs ~142 MB of index keys: beyond the 64 MiB static
+    # scratch, so the call fails during validation (no device is touched)
+    cfg = sg.config()
+    arr, n = _seqs(sg.seq(8192))
+    P = ctypes.c_void_p(FAKE)
+    assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_FORWARD) > 64 << 20
+    rc = L.sgqa_forward_noalloc(ctypes.byref(cfg), arr, n, P, P, None, None, P, P, P, None, P, None,
+                                P, P, P, P, None, None)
+    assert rc == E_WS
+    assert "static scratch" in L.sgqa_last_error().decode()
+    # invalid arguments are reported first, as for sgqa_forward
+    assert L.sgqa_forward_noalloc(ctypes.byref(cfg), arr, n, None, P, None, None, P, P, P, None, P,
+                                  None, P, P, P, P, None, None) == E_NULL
