@@ -564,7 +564,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
     // ---- the wavefront's four queries: A fragments, weights, candidates ----
     bf16x8 af[4][4];
     int lim[4];                   // candidates r_lo + [0, lim) of (query, group qq)
-    uint32_t tauv[4];             // listed: its threshold
+    float tauf[4];                // listed: its threshold as a score
     // byte offset of the key row of (query 4 * wave + j, group qq): kofs0 +
     // j * krow_bytes (keys: from block r_lo)
     const uint32_t krow_bytes = (uint32_t)(kGroups * a.key_stride * 4);
@@ -587,7 +587,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
         const int64_t nb = ok ? t / a.block_size : 0;
         const int64_t hi = nb < r_hi ? nb : r_hi;
         lim[j] = hi > r_lo ? (int)(hi - r_lo) : 0;
-        if (LISTED) tauv[j] = a.part_key[((sq.ws_row + qi) * kGroups + qq) * a.key_stride + a.tau_off];
+        // the threshold key as the score it stands for: scores are never
+        // -0, and on other finite values the key map is strictly increasing,
+        // so key >= tau exactly when score >= this value
+        if (LISTED) tauf[j] = key_score(a.part_key[((sq.ws_row + qi) * kGroups + qq) * a.key_stride + a.tau_off]);
     }
     if (r_lo >= r_hi) return;                       // workgroup-uniform
 
@@ -653,6 +656,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
 #pragma unroll
             for (int kk = 0; kk < 4; ++kk)
                 bf[kk] = as_bf16x8(*(const uint4*)(buf + (16 * sub + m) * kStoreStrideU + 32 * kk + 8 * qq));
+            // the four queries' weights, read ahead of the epilogue's branches
+            float4 wq[4];
+#pragma unroll
+            for (int j = 0; j < 4; ++j) wq[j] = wlds[4 * wave + j][qq];
             // the four queries' chains interleaved, one accumulator each
             f32x4 acc[4];
 #pragma unroll
@@ -664,26 +671,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
             const int rr = rt + 16 * sub + m;
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-                const uint32_t key = score_key_nz(head_score(acc[j], wlds[4 * wave + j][qq]));
+                const float sc = head_score(acc[j], wq[j]);
                 const uint32_t kofs = kofs0 + (uint32_t)j * krow_bytes;
                 if (!LISTED) {
                     const uint32_t off = rr < lim[j] ? kofs + 4u * (uint32_t)rr : kDropped;
-                    __builtin_amdgcn_raw_buffer_store_b32(key, krs, (int)off, 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(score_key_nz(sc), krs, (int)off, 0, 0);
                 } else {
                     // append (key, block id) to the segment's list: the 16
-                    // lanes of group qq count the passing lanes below them
-                    const bool pass = rr < lim[j] && key >= tauv[j];
-                    const uint32_t gm = (uint32_t)(__ballot(pass) >> (16 * qq)) & 0xFFFFu;
-                    const uint32_t cj = (cnts >> (8 * j)) & 0xFFu;
-                    const uint32_t pos = cj + (uint32_t)__builtin_popcount(gm & ((1u << m) - 1u));
-                    const uint32_t off = pass && pos < (uint32_t)kSegCap
-                        ? kofs + 4u * ((uint32_t)a.list_off + seg * (2 * kSegCap) + 2u * pos)
-                        : kDropped;
-                    const uint32_t blk = (uint32_t)(r_lo + rr);
-                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{key, blk}, krs, (int)off, 0, 0);
-                    const uint32_t cn = cj + (uint32_t)__builtin_popcount(gm);
-                    cnts = (cnts & ~(0xFFu << (8 * j))) | ((cn < 255u ? cn : 255u) << (8 * j));
+                    // lanes of group qq count the passing lanes below them.
+                    // Few candidates pass the threshold, so a wavefront whose
+                    // lanes all fail skips the bookkeeping.
+                    const bool pass = rr < lim[j] && sc >= tauf[j];
+                    const uint64_t bal = __ballot(pass);
+                    if (bal) {                              // wavefront-uniform
+                        const uint32_t gm = (uint32_t)(bal >> (16 * qq)) & 0xFFFFu;
+                        const uint32_t cj = (cnts >> (8 * j)) & 0xFFu;
+                        const uint32_t pos = cj + (uint32_t)__builtin_popcount(gm & ((1u << m) - 1u));
+                        const uint32_t off = pass && pos < (uint32_t)kSegCap
+                            ? kofs + 4u * ((uint32_t)a.list_off + seg * (2 * kSegCap) + 2u * pos)
+                            : kDropped;
+                        const uint32_t blk = (uint32_t)(r_lo + rr);
+                        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{score_key_nz(sc), blk}, krs, (int)off, 0, 0);
+                        const uint32_t cn = cj + (uint32_t)__builtin_popcount(gm);
+                        cnts = (cnts & ~(0xFFu << (8 * j))) | ((cn < 255u ? cn : 255u) << (8 * j));
+                    }
                 }
             }
         }
