@@ -13,8 +13,8 @@ cached tokens ride along as sub-records of the same JSON line, each with its
 own roofline.
 
 Per workload: whole-step throughput over the timed steps, the distribution
-of single step times (warm, and cold: a 512 MiB write between steps evicts
-the caches), the step's stages timed inside the step with HIP events on the
+of single step times (warm, and cold: a 512 MiB write and a 512 MiB read
+between steps leave the caches holding clean unrelated lines), the step's stages timed inside the step with HIP events on the
 launch stream (warm and cold), the roofline of the dominant kernel (its
 in-step duration against AMD's published peak and against what this GPU
 reaches on a plain copy and a bf16 GEMM), and -- for the headline record --
@@ -235,18 +235,38 @@ def measured_peaks(stream) -> dict:
     return out
 
 
+class ColdCaches:
+    """Brings the L2s and the Infinity Cache to a cold state between steps:
+    a 512 MiB buffer is written, then another 512 MiB buffer is read, so the
+    caches end up holding clean lines of unrelated data.  (A write alone
+    leaves up to the Infinity Cache's 256 MiB of dirty lines behind; their
+    write-back then lands on the first kernel of the step and is charged to
+    it: the decode step's index stage measured about 113 us after a write
+    flush against about 79 us after this one.)"""
+
+    def __init__(self):
+        import torch
+        self.w = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        self.r = torch.ones(128 << 20, dtype=torch.float32, device="cuda")
+
+    def __call__(self, i: int):
+        self.w.fill_(i & 0x7F)
+        self.r.sum()
+
+
 def step_times(step, stream, n: int, flush=None) -> dict:
     """Per-step HIP-event times over n steps on the launch stream: median,
-    10th and 90th percentile.  With `flush` (cold mode) a 512 MiB buffer is
-    written before every step, outside the timed interval, so the step starts
-    with the L2s and the Infinity Cache holding none of its inputs."""
+    10th and 90th percentile.  With `flush` (cold mode, a ColdCaches) the
+    caches are brought to a cold state before every step, outside the timed
+    interval, so the step starts with the L2s and the Infinity Cache holding
+    none of its inputs."""
     import torch
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
           for _ in range(n)]
     with torch.cuda.stream(stream):
         for i in range(n):
             if flush is not None:
-                flush.fill_(i & 0x7F)
+                flush(i)
             ev[i][0].record(stream)
             step()
             ev[i][1].record(stream)
@@ -295,15 +315,15 @@ def dense_split(wl, seqs):
 def stage_times(stages, stream, n: int, flush=None) -> dict:
     """`stages` (name -> callable) run in order as one step, n times, with a
     HIP event between consecutive stages on the launch stream; per stage the
-    median, 10th and 90th percentile of its in-step duration.  With `flush` a
-    512 MiB write precedes every step outside the timed intervals (cold)."""
+    median, 10th and 90th percentile of its in-step duration.  With `flush` (a
+    ColdCaches) every step starts cold, as in step_times."""
     import torch
     names = list(stages)
     ev = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)] for _ in range(n)]
     with torch.cuda.stream(stream):
         for i in range(n):
             if flush is not None:
-                flush.fill_(i & 0x7F)
+                flush(i)
             ev[i][0].record(stream)
             for j, nm in enumerate(names):
                 stages[nm]()
@@ -446,7 +466,7 @@ def bench_workload(name: str, args, primary: bool, peaks=None) -> dict:
     dist = {"warm": step_times(step, stream, n_dist)}
     flush = None
     if not args.no_cold and not wl.loop_steps:
-        flush = torch.empty(512 << 20, dtype=torch.uint8, device="cuda")
+        flush = ColdCaches()
         dist["cold"] = step_times(step, stream, n_dist, flush)
     print(f"[bench] {wl.name}: step times {dist}", file=sys.stderr, flush=True)
 
