@@ -53,6 +53,10 @@ constexpr int kTileBytesV = 16 * kTileRowV * 2;        // V tile: 6,656 B
 constexpr int kWaveLds = kTileBytes + kTileBytesV;     // a wavefront's K and V tiles
 constexpr int kWaveBufFloats = kHeadsPerGroup * kHeadDim + 2 * kHeadsPerGroup;
 static_assert(kWaveBufFloats * 4 <= kWaveLds, "a wavefront's merge buffer fits its tiles");
+// wavefronts per gather workgroup: every per-wavefront array, the chunk
+// stride and the merge below are sized by this one constant
+constexpr int kGatherWaves = 4;
+constexpr int kGatherThreads = 64 * kGatherWaves;
 constexpr uint32_t kRowBytes = kGroups * kHeadDim * 2;  // bytes between a tensor's token rows
 
 // Token list of a (query, group): entry i < n_sel*B is token i%B of block
@@ -204,9 +208,9 @@ __device__ __forceinline__ void gather_step(GatherState& st, const bf16x8 (&qf)[
 }
 
 template <bool PAGED>
-__global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, AttnArgs a) {
+__global__ __launch_bounds__(kGatherThreads, 2) void sparse_attn_kernel(SeqTable seqs, AttnArgs a) {
     extern __shared__ int32_t sel_lds[];                        // [K]
-    __shared__ __align__(16) char tiles[4][kWaveLds];
+    __shared__ __align__(16) char tiles[kGatherWaves][kWaveLds];
     __shared__ int s_nsel;
 
     // group-major order: the workgroups in flight read one group's K/V
@@ -230,7 +234,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, Attn
     if (threadIdx.x == 0) s_nsel = a.topk;
     __syncthreads();
     const int32_t* selrow = a.sel + (row * kGroups + g) * a.topk;
-    for (int j = threadIdx.x; j < a.topk; j += 256) {
+    for (int j = threadIdx.x; j < a.topk; j += kGatherThreads) {
         const int32_t v = selrow[j];
         sel_lds[j] = v;
         if (v < 0) atomicMin(&s_nsel, j);
@@ -245,7 +249,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, Attn
     if (PAGED) {
         const int32_t* pt = a.page_table + sq.kv_offset;
         const int64_t b_max = t / B;
-        for (int j = threadIdx.x; j < n_sel; j += 256) {
+        for (int j = threadIdx.x; j < n_sel; j += kGatherThreads) {
             const int64_t r = sel_lds[j] > b_max ? b_max : sel_lds[j];
             sel_lds[j] = (int32_t)paged_row(pt, a.n_pages, r * B);
         }
@@ -304,10 +308,10 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, Attn
 #pragma unroll
     for (int i = 0; i < 6; ++i) pc[i] = piece_code(i, lane);
 
-    // Chunks w, w + 4, ... in pairs.  Two register sets: a set's rows go to
-    // the tiles just before their chunk is processed, and the set is
-    // refilled at once with the chunk eight ahead, so the next two chunks'
-    // rows are in flight while a chunk is processed.  A pair's second chunk
+    // Chunks w, w + W, ... (W = kGatherWaves) in pairs.  Two register sets:
+    // a set's rows go to the tiles just before their chunk is processed, and
+    // the set is refilled at once with the chunk 2W ahead, so the next two
+    // chunks' rows are in flight while a chunk is processed.  A pair's second chunk
     // may lie past c_hi (fully masked: it adds nothing); loads of chunks past
     // the wavefront's last read row t_row (the same lines for every lane).
     // The loop has a single exit at its end, which keeps the compiler's wait
@@ -316,19 +320,19 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, Attn
     if (c < c_hi) {
         u32x4 ak[6], av[6], bk[6], bv[6];
         load_chunk<PAGED>(c, lane, pc, cm, kbase, vbase, ak, av);
-        load_chunk<PAGED>(c + 4, lane, pc, cm, kbase, vbase, bk, bv);
+        load_chunk<PAGED>(c + kGatherWaves, lane, pc, cm, kbase, vbase, bk, bv);
         do {
             store_chunk(ak, av, pc, ktile, vtile);
             wave_lds_sync();
-            load_chunk<PAGED>(c + 8, lane, pc, cm, kbase, vbase, ak, av);
+            load_chunk<PAGED>(c + 2 * kGatherWaves, lane, pc, cm, kbase, vbase, ak, av);
             gather_step(st, qf, c, gl);
             wave_lds_sync();
             store_chunk(bk, bv, pc, ktile, vtile);
             wave_lds_sync();
-            load_chunk<PAGED>(c + 12, lane, pc, cm, kbase, vbase, bk, bv);
-            gather_step(st, qf, c + 4, gl);
+            load_chunk<PAGED>(c + 3 * kGatherWaves, lane, pc, cm, kbase, vbase, bk, bv);
+            gather_step(st, qf, c + kGatherWaves, gl);
             wave_lds_sync();
-            c += 8;
+            c += 2 * kGatherWaves;
         } while (c < c_hi);
     }
     float lsum = st.lsum;
@@ -340,7 +344,7 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, Attn
     lsum = xor32_sum(xor16_sum(lsum));
     const float mrow = m_use * sl2;
 
-    // ---- merge the four wavefronts ----
+    // ---- merge the wavefronts ----
     __syncthreads();
     float* buf = (float*)tiles[w];
 #pragma unroll
@@ -354,18 +358,18 @@ __global__ __launch_bounds__(256, 2) void sparse_attn_kernel(SeqTable seqs, Attn
     __syncthreads();
 
     const int64_t rg = (sq.ws_row + qi) * kGroups + g;     // partials row
-    for (int e = threadIdx.x; e < kHeadsPerGroup * kHeadDim; e += 256) {
+    for (int e = threadIdx.x; e < kHeadsPerGroup * kHeadDim; e += kGatherThreads) {
         const int head = e / kHeadDim;
-        float mw[4], M = -INFINITY;
+        float mw[kGatherWaves], M = -INFINITY;
 #pragma unroll
-        for (int ww = 0; ww < 4; ++ww) {
+        for (int ww = 0; ww < kGatherWaves; ++ww) {
             mw[ww] = ((const float*)tiles[ww])[kHeadsPerGroup * kHeadDim + head];
             M = fmaxf(M, mw[ww]);
         }
         float L = 0.f, O = 0.f;
         if (M != -INFINITY) {
 #pragma unroll
-            for (int ww = 0; ww < 4; ++ww) {
+            for (int ww = 0; ww < kGatherWaves; ++ww) {
                 const float sc = exp2f(mw[ww] - M);
                 L += ((const float*)tiles[ww])[kHeadsPerGroup * kHeadDim + kHeadsPerGroup + head] * sc;
                 O += ((const float*)tiles[ww])[e] * sc;
@@ -436,7 +440,7 @@ static hipError_t launch_sparse_attn_t(const SeqTable& seqs, int64_t max_nq, con
     hipError_t e = set_dynamic_lds((const void*)sparse_attn_kernel<PAGED>, lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(max_nq * kGroups * a.n_split), (unsigned)seqs.n);
-    hipLaunchKernelGGL((sparse_attn_kernel<PAGED>), grid, dim3(256), lds, stream, seqs, a);
+    hipLaunchKernelGGL((sparse_attn_kernel<PAGED>), grid, dim3(kGatherThreads), lds, stream, seqs, a);
     return hipGetLastError();
 }
 
