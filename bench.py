@@ -171,8 +171,8 @@ def recorded_counters(workload: str, kernels):
     """HBM bytes per call of the attention kernels `kernels` on `workload`,
     summed over them, from committed counter summaries under profiles/
     (FETCH_SIZE and WRITE_SIZE, calibrated against a device copy), or None
-    when a kernel has no summary for that workload or its source has changed
-    since the counters were taken."""
+    when a kernel has no summary for that workload or one of its source files
+    has changed since the counters were taken."""
     import glob
     import hashlib
     recs = {}
@@ -193,10 +193,15 @@ def recorded_counters(workload: str, kernels):
         rec = recs.get((workload, kernel))
         if rec is None:
             return None
-        src = os.path.join(ROOT, rec.get("source_file", ""))
-        if not os.path.isfile(src):
-            return None
-        if hashlib.sha256(open(src, "rb").read()).hexdigest() != rec.get("source_sha256"):
+        # source_file lists the files the kernel's code and launch depend on
+        # (space-separated); source_sha256 is over their bytes in that order
+        h = hashlib.sha256()
+        for name in rec.get("source_file", "").split():
+            src = os.path.join(ROOT, name)
+            if not os.path.isfile(src):
+                return None
+            h.update(open(src, "rb").read())
+        if not rec.get("source_file") or h.hexdigest() != rec.get("source_sha256"):
             return None
         total["fetch"] += int(rec["traffic_fetch_bytes_per_launch"])
         total["write"] += int(rec["traffic_write_bytes_per_launch"])
@@ -569,8 +574,12 @@ def bench_workload(name: str, args, primary: bool, peaks=None) -> dict:
         # the gather, the rate it moves the selected K/V rows at and the HBM
         # fraction of the bytes it fetched (FETCH_SIZE records, when current)
         per_k = {}
-        for kname, w_k, ctr_name in ((union_name, wm_d, union_k),
-                                     (gather_name, wm_g, "sparse_attn_kernel<false>")):
+        kinds = ((union_name, wm_d, union_k), (gather_name, wm_g, "sparse_attn_kernel<false>"))
+        if wm_d is not None and wm_g is not None and not kernel_ms:
+            # both kernels ran in the call but were not timed apart (paged
+            # caches or neighbours): one entry for the two
+            kinds = ((f"{union_name} + {gather_name}", wm, None),)
+        for kname, w_k, ctr_name in kinds:
             if w_k is None:
                 continue
             ms = kernel_ms.get(kname, attn_ms)
@@ -581,7 +590,7 @@ def bench_workload(name: str, args, primary: bool, peaks=None) -> dict:
                  "mfma_frac": w_k["attn_flops"] / (ms * 1e-3) / PEAK_BF16_FLOPS,
                  "gathered_bytes": w_k["attn_gather_bytes"],
                  "gathered_GBps": w_k["attn_gather_bytes"] / (ms * 1e-3) / 1e9}
-            c1 = recorded_counters(wl.name, [ctr_name]) if plain else None
+            c1 = recorded_counters(wl.name, [ctr_name]) if plain and ctr_name else None
             if c1:
                 e["fetched_bytes"] = c1["fetch"]
                 e["hbm_GBps"] = c1["fetch"] / (ms * 1e-3) / 1e9
