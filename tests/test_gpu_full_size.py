@@ -87,8 +87,8 @@ def test_prefill_8k_bench_configuration():
 
 @pytest.mark.timeout(900)
 def test_prefill_64k():
-    st = _check("prefill_64k", 512, store_blocks=2048)
-    assert st["rows"] >= 512 and st["sel_rows"] == 4 * st["rows"]
+    st = _check("prefill_64k", 1024, store_blocks=2048)
+    assert st["rows"] >= 1024 and st["sel_rows"] == 4 * st["rows"]
 
 
 @pytest.mark.timeout(900)
@@ -105,8 +105,8 @@ def test_decode_64_sequences():
 
 @pytest.mark.timeout(900)
 def test_chunk_over_1m_cache():
-    st = _check("chunk_1m", 256, store_blocks=4096)
-    assert st["rows"] >= 256
+    st = _check("chunk_1m", 512, store_blocks=4096)
+    assert st["rows"] >= 512
     # the chunk's long rows go through candidate lists; some lists cannot give
     # the exact top k and those rows are scored again over every candidate:
     # the device counted them and the checked rows include them
