@@ -29,6 +29,15 @@ Definition (every value is a pure function of its index):
    in fp32), ``inv = 1 / sqrt(ss / width + 1e-6)`` with correctly rounded
    fp32 division and square root, value ``= bf16(x_bf16 * inv)``.
 
+6. "Correlated" rows (an optional variant of the indexer queries and weights
+   in which neighbouring query rows are alike): the value at (row r, column
+   e) of a tensor of row width ``width`` is ``x = sum_j y_j`` over
+   ``j = 0 .. W-1`` added in that order in fp32, with
+   ``y_j = draw(tid, (r + W - 1 - j) * width + e)``, then ``x * c_W``
+   rounded once, ``c_W = float32(1 / sqrt(W))`` (a moving sum of W
+   independent draws: rows d apart share W - d of them, correlation
+   (W - d) / W, and every value keeps the draws' variance).
+
 Tensor ids: 1 Q, 2 K cache, 3 V cache, 4 indexer queries, 5 indexer weights,
 6 proxy keys, 7 compression logits, 8 sequence lengths.
 """
@@ -124,3 +133,17 @@ def seq_lengths(seed: int, n: int, lo: int, hi: int) -> np.ndarray:
     h = _hash(seed, TID_LEN, np.arange(n, dtype=np.uint64))
     span = np.uint64(hi - lo + 1)
     return (h % span).astype(np.int64) + np.int64(lo)
+
+
+def corr_rows_f32(seed: int, tid: int, rows: np.ndarray, width: int, window: int,
+                  scale: np.float32 = C_UNIT) -> np.ndarray:
+    """Correlated rows ``[len(rows), width]`` (item 6 above): a moving sum of
+    ``window`` draws along the row index, added in a fixed order."""
+    rows = np.asarray(rows, dtype=np.int64).reshape(-1)
+    cols = np.arange(width, dtype=np.int64)[None, :]
+    acc = np.zeros((rows.shape[0], width), dtype=np.float32)
+    for j in range(window):
+        idx = (rows[:, None] + np.int64(window - 1 - j)) * np.int64(width) + cols
+        acc = (acc + normal_f32(seed, tid, idx.astype(np.uint64), scale)).astype(np.float32)
+    c = np.float32(1.0 / np.sqrt(float(window)))
+    return (acc * c).astype(np.float32)

@@ -28,7 +28,9 @@ def lib() -> ctypes.CDLL:
         L.synth_fill_bf16.argtypes = [P, U64, U64, U32, U64, F, P]
         L.synth_fill_f32.argtypes = [P, U64, U64, U32, U64, F, P]
         L.synth_fill_rms_rows_bf16.argtypes = [P, U64, ctypes.c_int32, U64, U32, U64, F, F, P]
-        for f in (L.synth_fill_bf16, L.synth_fill_f32, L.synth_fill_rms_rows_bf16):
+        I32 = ctypes.c_int32
+        L.synth_fill_corr.argtypes = [P, I32, U64, I32, I32, U64, U32, U64, F, F, P]
+        for f in (L.synth_fill_bf16, L.synth_fill_f32, L.synth_fill_rms_rows_bf16, L.synth_fill_corr):
             f.restype = ctypes.c_int
         _lib = L
     return _lib
@@ -71,3 +73,18 @@ def fill_rms_rows(t: torch.Tensor, seed: int, tid: int, row0: int = 0) -> torch.
 
 __all__ = ["fill_bf16", "fill_f32", "fill_rms_rows", "lib", "TID_Q", "TID_K", "TID_V",
            "TID_QIDX", "TID_W", "TID_PROXY", "TID_LOGITS", "C_W"]
+
+
+def fill_corr_rows(t: torch.Tensor, seed: int, tid: int, window: int, row0: int = 0,
+                   scale=C_UNIT) -> torch.Tensor:
+    """Correlated rows along dim 0 (a moving sum of `window` draws per value,
+    see :mod:`synth`); bf16 or fp32 tensors, the row width is numel / size(0)."""
+    import numpy as np
+    assert t.dtype in (torch.bfloat16, torch.float32) and t.is_cuda and t.is_contiguous()
+    n_rows = t.shape[0]
+    width = t.numel() // max(n_rows, 1)
+    c = float(np.float32(1.0 / np.sqrt(float(window))))
+    _check(lib().synth_fill_corr(t.data_ptr(), 1 if t.dtype == torch.bfloat16 else 0, n_rows, width,
+                                 int(window), seed, tid, row0, float(scale), c, _stream()),
+           "synth_fill_corr")
+    return t

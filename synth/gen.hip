@@ -67,6 +67,26 @@ __global__ void fill_rms_rows_kernel(uint16_t* out, uint64_t n_rows, int width, 
     }
 }
 
+// correlated rows: x = sum over j = 0 .. window-1 (in that order) of the draw
+// at ((row + window - 1 - j) * width + e), then x * c (c = fp32(1/sqrt(window)))
+__global__ void fill_corr_kernel(void* out, int bf16_out, uint64_t n_rows, int width, int window,
+                                 uint64_t base, uint64_t row0, float scale, float c) {
+    const uint64_t n = n_rows * (uint64_t)width;
+    for (uint64_t i = (uint64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n;
+         i += (uint64_t)gridDim.x * blockDim.x) {
+        const uint64_t r = row0 + i / (uint64_t)width;
+        const uint64_t e = i % (uint64_t)width;
+        float acc = 0.0f;
+        for (int j = 0; j < window; ++j)
+            acc = acc + draw(base, (r + (uint64_t)(window - 1 - j)) * (uint64_t)width + e, scale);
+        const float x = acc * c;
+        if (bf16_out)
+            ((uint16_t*)out)[i] = to_bf16(x);
+        else
+            ((float*)out)[i] = x;
+    }
+}
+
 unsigned grid_for(uint64_t n, unsigned block) {
     uint64_t g = (n + block - 1) / block;
     return (unsigned)(g > 65536 * 4 ? 65536 * 4 : (g == 0 ? 1 : g));
@@ -100,6 +120,16 @@ int synth_fill_rms_rows_bf16(void* out, uint64_t n_rows, int32_t width, uint64_t
     hipLaunchKernelGGL(fill_rms_rows_kernel, dim3(grid_for(n_rows, 128)), dim3(128), 0,
                        (hipStream_t)stream, (uint16_t*)out, n_rows, (int)width,
                        stream_base(seed, tid), row0, scale, eps);
+    return (int)hipGetLastError();
+}
+
+int synth_fill_corr(void* out, int32_t bf16_out, uint64_t n_rows, int32_t width, int32_t window,
+                    uint64_t seed, uint32_t tid, uint64_t row0, float scale, float c, void* stream) {
+    if (n_rows == 0) return 0;
+    if (width <= 0 || window <= 0) return (int)hipErrorInvalidValue;
+    const uint64_t n = n_rows * (uint64_t)width;
+    hipLaunchKernelGGL(fill_corr_kernel, dim3(grid_for(n, 256)), dim3(256), 0, (hipStream_t)stream, out,
+                       (int)bf16_out, n_rows, (int)width, (int)window, stream_base(seed, tid), row0, scale, c);
     return (int)hipGetLastError();
 }
 

@@ -40,8 +40,8 @@ from typing import Dict, List
 
 import numpy as np
 
-from . import (C_W, TID_K, TID_LOGITS, TID_PROXY, TID_Q, TID_QIDX, TID_V, TID_W,
-               normal_bf16_bits, normal_f32, rms_rows_bf16_bits, seq_lengths)
+from . import (C_W, TID_K, TID_LOGITS, TID_PROXY, TID_Q, TID_QIDX, TID_V, TID_W, corr_rows_f32,
+               f32_to_bf16_bits, normal_bf16_bits, normal_f32, rms_rows_bf16_bits, seq_lengths)
 
 H, G, D, HI, DI = 64, 4, 192, 4, 128
 
@@ -79,6 +79,10 @@ class Workload:
     # i's part of call s
     loop_steps: int = 0
     loop_seqs: int = 0
+    # > 0: the indexer queries and weights of neighbouring query rows are
+    # correlated (a moving sum of this many draws along the row index, see
+    # synth item 6), so neighbouring queries select overlapping blocks
+    corr_window: int = 0
 
     def step_seqs(self, s: int) -> List[SeqLayout]:
         return self.seqs[s * self.loop_seqs:(s + 1) * self.loop_seqs]
@@ -152,6 +156,15 @@ def _multi(name, parts, B, K, row_gap=0, order=None) -> Workload:
 
 
 def make(name: str, seed: int = 0, store_q8: int = 2) -> Workload:
+    if "_corr" in name:
+        # <workload>_corr<W>: the same workload with correlated indexer
+        # queries and weights along the query rows (a variant outside the
+        # benchmark configurations)
+        base, _, win = name.rpartition("_corr")
+        w = make(base, seed=seed, store_q8=store_q8)
+        w.name = name
+        w.corr_window = int(win)
+        return w
     if name == "tiny_prefill_256":
         w = _prefill(name, 256, 8, 16)
     elif name == "prefill_8k":
@@ -234,8 +247,16 @@ def device_inputs(wl: Workload, device="cuda") -> DeviceInputs:
     t["q"] = dv.fill_rms_rows(torch.empty((Nq, H, D), dtype=bf, device=device), wl.seed, TID_Q)
     t["k"] = dv.fill_rms_rows(torch.empty((R, G, D), dtype=bf, device=device), wl.seed, TID_K)
     t["v"] = dv.fill_bf16(torch.empty((R, G, D), dtype=bf, device=device), wl.seed, TID_V)
-    t["q_idx"] = dv.fill_bf16(torch.empty((Nq, G, HI, DI), dtype=bf, device=device), wl.seed, TID_QIDX)
-    t["w"] = dv.fill_f32(torch.empty((Nq, G, HI), dtype=f32, device=device), wl.seed, TID_W, scale=C_W)
+    if wl.corr_window:
+        t["q_idx"] = dv.fill_corr_rows(torch.empty((Nq, G, HI, DI), dtype=bf, device=device), wl.seed,
+                                       TID_QIDX, wl.corr_window)
+        t["w"] = dv.fill_corr_rows(torch.empty((Nq, G, HI), dtype=f32, device=device), wl.seed, TID_W,
+                                   wl.corr_window, scale=C_W)
+    else:
+        t["q_idx"] = dv.fill_bf16(torch.empty((Nq, G, HI, DI), dtype=bf, device=device), wl.seed,
+                                  TID_QIDX)
+        t["w"] = dv.fill_f32(torch.empty((Nq, G, HI), dtype=f32, device=device), wl.seed, TID_W,
+                             scale=C_W)
     t["proxy_k"] = dv.fill_bf16(torch.empty((R, DI), dtype=bf, device=device), wl.seed, TID_PROXY)
     t["logits"] = dv.fill_f32(torch.empty((R, DI), dtype=f32, device=device), wl.seed, TID_LOGITS)
     t["store"] = torch.zeros((S, DI), dtype=torch.uint8 if wl.store_q8 == 2 else bf, device=device)
@@ -286,10 +307,15 @@ def host_v(wl: Workload, kv_rows) -> np.ndarray:
 
 
 def host_q_idx(wl: Workload, qrows) -> np.ndarray:
+    if wl.corr_window:
+        x = corr_rows_f32(wl.seed, TID_QIDX, qrows, G * HI * DI, wl.corr_window)
+        return f32_to_bf16_bits(x).reshape(-1, G, HI, DI)
     return normal_bf16_bits(wl.seed, TID_QIDX, _flat(qrows, G * HI * DI)).reshape(-1, G, HI, DI)
 
 
 def host_w(wl: Workload, qrows) -> np.ndarray:
+    if wl.corr_window:
+        return corr_rows_f32(wl.seed, TID_W, qrows, G * HI, wl.corr_window, C_W).reshape(-1, G, HI)
     return normal_f32(wl.seed, TID_W, _flat(qrows, G * HI), C_W).reshape(-1, G, HI)
 
 

@@ -24,6 +24,15 @@ def test_device_generator_matches_host():
     r = dv.fill_rms_rows(torch.empty((512, 192), dtype=torch.bfloat16, device="cuda"), 0, synth.TID_K, 1000)
     host = synth.rms_rows_bf16_bits(0, synth.TID_K, np.arange(1000, 1512), 192)
     assert np.array_equal(r.cpu().view(torch.int16).numpy().view(np.uint16), host)
+    # correlated rows (indexer queries and weights of the correlated variant)
+    c = dv.fill_corr_rows(torch.empty((300, 4, 4, 128), dtype=torch.bfloat16, device="cuda"), 0,
+                          synth.TID_QIDX, 64, row0=777)
+    host = synth.f32_to_bf16_bits(synth.corr_rows_f32(0, synth.TID_QIDX, np.arange(777, 1077), 2048, 64))
+    assert np.array_equal(c.cpu().view(torch.int16).numpy().view(np.uint16).reshape(300, -1), host)
+    cw = dv.fill_corr_rows(torch.empty((300, 4, 4), dtype=torch.float32, device="cuda"), 0, synth.TID_W, 64,
+                           scale=synth.C_W)
+    assert np.array_equal(cw.cpu().numpy().reshape(300, -1),
+                          synth.corr_rows_f32(0, synth.TID_W, np.arange(300), 16, 64, synth.C_W))
 
 
 def test_tiny_prefill_all_rows():

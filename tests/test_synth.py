@@ -66,3 +66,21 @@ def test_group_slices_equal_full_rows():
     for g in range(4):
         assert np.array_equal(k[:, g], W.host_k_group(wl, rows, g))
         assert np.array_equal(v[:, g], W.host_v_group(wl, rows, g))
+
+
+def test_correlated_rows_are_moving_sums():
+    """Item 6 of the generator: each value is the sum of `window` draws at the
+    documented indices (checked in float64 against the fp32 result within
+    its rounding), neighbouring rows share draws, and the variance is kept."""
+    W_, width = 16, 24
+    rows = np.array([0, 1, 5, 900], dtype=np.int64)
+    got = synth.corr_rows_f32(7, synth.TID_QIDX, rows, width, W_)
+    for a, r in enumerate(rows):
+        idx = ((r + W_ - 1 - np.arange(W_))[:, None] * width + np.arange(width)[None, :]).astype(np.uint64)
+        ref = synth.normal_f32(7, synth.TID_QIDX, idx).astype(np.float64).sum(axis=0) / np.sqrt(W_)
+        assert np.allclose(got[a], ref, rtol=0, atol=1e-5)
+    many = synth.corr_rows_f32(7, synth.TID_QIDX, np.arange(4000), 64, W_)
+    assert abs(float(many.std()) - 1.0) < 0.03
+    d1 = np.mean([np.corrcoef(many[i], many[i + 1])[0, 1] for i in range(0, 3900, 50)])
+    d8 = np.mean([np.corrcoef(many[i], many[i + 8])[0, 1] for i in range(0, 3900, 50)])
+    assert abs(d1 - (W_ - 1) / W_) < 0.05 and abs(d8 - (W_ - 8) / W_) < 0.08
