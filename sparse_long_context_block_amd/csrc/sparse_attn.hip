@@ -213,16 +213,29 @@ __global__ __launch_bounds__(kGatherThreads, 2) void sparse_attn_kernel(SeqTable
     __shared__ __align__(16) char tiles[kGatherWaves][kWaveLds];
     __shared__ int s_nsel;
 
-    // group-major order: the workgroups in flight read one group's K/V
+    // Group-major order: the workgroups in flight read one group's K/V
     // (disjoint cache lines per group), a quarter of the cache's footprint,
-    // which keeps the re-read rows of neighbouring queries in the last-level
-    // cache
+    // which keeps the re-read rows in the last-level cache.  Within a group,
+    // workgroups are dealt to the 8 XCDs round-robin by id; each XCD takes a
+    // contiguous run of queries (and, for range splits, the same range for
+    // all of them), so queries that run together on one XCD are neighbours
+    // and share whatever blocks their selections have in common through
+    // that XCD's L2.  (Any bijection is correct; this one needs the group's
+    // workgroup count to be a multiple of 8 and n_split to divide 8.)
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t per_group = (int64_t)(gridDim.x / kGroups);
     const int g = (int)(blockIdx.x / per_group);
-    const int64_t rem = blockIdx.x - g * per_group;
-    const int split = (int)(rem % a.n_split);
-    const int64_t qi = rem / a.n_split;
+    const int64_t loc = blockIdx.x - g * per_group;
+    int split;
+    int64_t qi;
+    if (per_group % 8 == 0 && 8 % a.n_split == 0) {
+        const int xcd = (int)(loc % 8);
+        split = xcd % a.n_split;
+        qi = (int64_t)(xcd / a.n_split) * (per_group / 8) + loc / 8;
+    } else {
+        split = (int)(loc % a.n_split);
+        qi = loc / a.n_split;
+    }
     if (qi >= sq.n_q) return;
     const int64_t t = sq.pos0 + qi;
     const int64_t row = sq.q_offset + qi;
