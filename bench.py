@@ -10,7 +10,9 @@ Default run: the 8,192-query chunk at positions 1,040,384..1,048,575 over a
 per group, B=8, k = 512 blocks = 4,096 tokens) is the headline record; the
 65,536-token prefill and the 64-sequence decode step over up to 262,144
 cached tokens ride along as sub-records of the same JSON line, each with its
-own roofline.
+own roofline, and so does the same 1M chunk with the correlated variant of
+the indexer inputs (`chunk_1m_corr64`, labelled `variant`: neighbouring
+queries select overlapping blocks; not a benchmark configuration).
 
 Per workload: whole-step throughput over the timed steps, the distribution
 of single step times (warm, and cold: a 512 MiB write and a 512 MiB read
@@ -301,7 +303,7 @@ def event_time_ms(fn, stream, reps: int) -> float:
 # ---------------------------------------------------------------------------
 
 DEFAULT_WORKLOAD = "chunk_1m"
-DEFAULT_SUBS = ("prefill_64k", "decode_64x256k")
+DEFAULT_SUBS = ("prefill_64k", "decode_64x256k", "chunk_1m_corr64")
 
 
 def dense_split(wl, seqs):
@@ -610,6 +612,9 @@ def bench_workload(name: str, args, primary: bool, peaks=None) -> dict:
                    + ("+neighbours" if nb else ""), "queries": wm["queries"],
                    "block_size": wl.block_size, "topk_blocks": wl.topk, "store_q8": wl.store_q8,
                    "heads": H, "kv_groups": G, "head_dim": D},
+        **({"variant": f"indexer queries and weights correlated along the query rows (moving sum "
+                       f"of {wl.corr_window} draws); not a benchmark configuration"}
+           if wl.corr_window else {}),
         "per_op_ms": per_op,
         "step_times": dist,
         "in_step_ms": in_step,

@@ -111,3 +111,12 @@ def test_chunk_over_1m_cache():
     # the exact top k and those rows are scored again over every candidate:
     # the device counted them and the checked rows include them
     assert st["rescored_rows"] >= 1 and st["rescored_checked"] >= 1
+
+
+@pytest.mark.timeout(900)
+def test_chunk_over_1m_cache_correlated_inputs():
+    """The 1M chunk with the correlated variant of the indexer inputs
+    (neighbouring queries select overlapping blocks, so the gather's
+    neighbouring workgroups share rows through the L2)."""
+    st = _check("chunk_1m_corr64", 128, store_blocks=2048)
+    assert st["rows"] >= 128
