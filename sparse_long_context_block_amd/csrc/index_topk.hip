@@ -554,10 +554,13 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
     // every row of the tile has at most k candidates and takes them all: the
     // keys are read only for score outputs
     if (!a.sel_scores && (sq.pos0 + q0 + n_valid - 1) / a.block_size <= a.topk) return;
-    const int64_t nb_max = (sq.pos0 + q0 + n_valid - 1) / a.block_size;
+    // the candidate range as wavefront-uniform values (the 64-bit division
+    // runs in vector registers), so the store resource and the per-query
+    // limits below stay in scalar registers
+    const int64_t nb_max = uniform_i64((sq.pos0 + q0 + n_valid - 1) / a.block_size);
     const int64_t r_lo = (int64_t)split * a.split_blocks;
     const int64_t r_hi = nb_max < r_lo + a.split_blocks ? nb_max : r_lo + a.split_blocks;
-    const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+    const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
     const int qq = lane >> 4;     // operand k-chunk; result group
     const int m = lane & 15;      // operand row (4*group + head); result column
 
@@ -570,9 +573,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
     const uint32_t krow_bytes = (uint32_t)(kGroups * a.key_stride * 4);
     const uint32_t kofs0 = (uint32_t)((4 * wave * kGroups + qq) * a.key_stride * 4) +
                            (LISTED ? 0u : 4u * (uint32_t)r_lo);
-    // listed: entries of the current segment per query, 8 bits each
-    // (saturating at 255: anything above kSegCap marks an overflow)
-    uint32_t cnts = 0u;
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
         const int qo = 4 * wave + j;
@@ -642,6 +642,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
     gload(0, stage);
     lstore(tiles[0], stage);
     int cur = 0;
+    // steps of 16 blocks below lim_min are candidates of all four queries
+    const int lim_min = min(min(lim[0], lim[1]), min(lim[2], lim[3]));
+    // listed: entries of the current segment per query (above kSegCap when
+    // entries were dropped)
+    uint32_t cnt[4] = {0u, 0u, 0u, 0u};
+    const uint32_t below = (1u << m) - 1u;          // group lanes below this one
     for (int64_t r0 = r_lo; r0 < r_hi; r0 += kStoreTile) {
         const int rt = (int)(r0 - r_lo);
         const bool more = r0 + kStoreTile < r_hi;
@@ -668,48 +674,68 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
             for (int kk = 0; kk < 4; ++kk)
 #pragma unroll
                 for (int j = 0; j < 4; ++j) acc[j] = mfma_16x16x32(af[j][kk], bf[kk], acc[j]);
-            const int rr = rt + 16 * sub + m;
+            const int rb = rt + 16 * sub;
+            const int rr = rb + m;
+            // every row of the step is a candidate of the four queries
+            // (wavefront-uniform): no per-row limit test
+            const bool full = rb + 16 <= lim_min;
+            float sc[4];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-                const float sc = head_score(acc[j], wq[j]);
-                const uint32_t kofs = kofs0 + (uint32_t)j * krow_bytes;
-                if (!LISTED) {
-                    const uint32_t off = rr < lim[j] ? kofs + 4u * (uint32_t)rr : kDropped;
-                    __builtin_amdgcn_raw_buffer_store_b32(score_key_nz(sc), krs, (int)off, 0, 0);
+            for (int j = 0; j < 4; ++j) sc[j] = head_score(acc[j], wq[j]);
+            if (!LISTED) {
+                if (full) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                        __builtin_amdgcn_raw_buffer_store_b32(
+                            score_key_nz(sc[j]), krs, (int)(kofs0 + (uint32_t)j * krow_bytes + 4u * (uint32_t)rr), 0, 0);
                 } else {
-                    // append (key, block id) to the segment's list: the 16
-                    // lanes of group qq count the passing lanes below them.
-                    // Few candidates pass the threshold, so a wavefront whose
-                    // lanes all fail skips the bookkeeping.
-                    const bool pass = rr < lim[j] && sc >= tauf[j];
-                    const uint64_t bal = __ballot(pass);
-                    if (bal) {                              // wavefront-uniform
-                        const uint32_t gm = (uint32_t)(bal >> (16 * qq)) & 0xFFFFu;
-                        const uint32_t cj = (cnts >> (8 * j)) & 0xFFu;
-                        const uint32_t pos = cj + (uint32_t)__builtin_popcount(gm & ((1u << m) - 1u));
-                        const uint32_t off = pass && pos < (uint32_t)kSegCap
-                            ? kofs + 4u * ((uint32_t)a.list_off + seg * (2 * kSegCap) + 2u * pos)
-                            : kDropped;
-                        const uint32_t blk = (uint32_t)(r_lo + rr);
-                        typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
-                        __builtin_amdgcn_raw_buffer_store_b64(u32x2{score_key_nz(sc), blk}, krs, (int)off, 0, 0);
-                        const uint32_t cn = cj + (uint32_t)__builtin_popcount(gm);
-                        cnts = (cnts & ~(0xFFu << (8 * j))) | ((cn < 255u ? cn : 255u) << (8 * j));
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                        const uint32_t off = rr < lim[j] ? kofs0 + (uint32_t)j * krow_bytes + 4u * (uint32_t)rr
+                                                         : kDropped;
+                        __builtin_amdgcn_raw_buffer_store_b32(score_key_nz(sc[j]), krs, (int)off, 0, 0);
                     }
+                }
+            } else {
+                // append (key, block id) to the segment's list of (query j,
+                // group qq): the 16 lanes of the group count the passing
+                // lanes below them.  Few candidates pass the threshold, so a
+                // query whose lanes all fail skips the bookkeeping.
+                uint64_t bal[4];
+                if (full) {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bal[j] = __ballot(sc[j] >= tauf[j]);
+                } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) bal[j] = __ballot(rr < lim[j] && sc[j] >= tauf[j]);
+                }
+                const uint32_t blk = (uint32_t)(r_lo + rr);
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                    if (bal[j] == 0u) continue;                           // wavefront-uniform
+                    const uint32_t gm = (uint32_t)(bal[j] >> (16 * qq)) & 0xFFFFu;
+                    const uint32_t pos = cnt[j] + (uint32_t)__builtin_popcount(gm & below);
+                    const uint32_t off = ((gm >> m) & 1u) && pos < (uint32_t)kSegCap
+                        ? kofs0 + (uint32_t)j * krow_bytes +
+                              4u * ((uint32_t)a.list_off + seg * (2 * kSegCap) + 2u * pos)
+                        : kDropped;
+                    typedef unsigned int u32x2 __attribute__((ext_vector_type(2)));
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{score_key_nz(sc[j]), blk}, krs, (int)off, 0, 0);
+                    cnt[j] += (uint32_t)__builtin_popcount(gm);
                 }
             }
         }
         if (LISTED && (((r0 + kStoreTile) % kSegBlocks) == 0 || r0 + kStoreTile >= r_hi)) {
-            // the segment ends: its count (above kSegCap when entries were
-            // dropped), for every query whose range reaches into it
+            // the segment ends: its count, for every query whose range
+            // reaches into it
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
                 const bool wr = m == 0 && (int64_t)seg * kSegBlocks - r_lo < lim[j];
-                __builtin_amdgcn_raw_buffer_store_b32((cnts >> (8 * j)) & 0xFFu, krs,
+                __builtin_amdgcn_raw_buffer_store_b32(cnt[j], krs,
                                                       (int)(wr ? kofs0 + (uint32_t)j * krow_bytes + 4u * seg
                                                                : kDropped), 0, 0);
+                cnt[j] = 0u;
             }
-            cnts = 0u;
         }
         if (more) lstore(tiles[cur ^ 1], stage);
         cur ^= 1;

@@ -171,7 +171,7 @@ constexpr int64_t kTiledMaxStride = ((int64_t)1 << 32) / (16 * sgqa::kGroups * 4
 // launches' fixed costs -- sample, threshold, list select, rescue -- are paid
 // a quarter as often; 8 and 16 GiB measured no faster)
 constexpr size_t kTiledKeyBudget = (size_t)1 << 32;
-constexpr int kTiledSplitBlocks = 512;
+constexpr int kTiledSplitBlocks = 2048;
 
 struct AttnPlan {
     int n_split = 1;

@@ -341,6 +341,13 @@ __device__ __forceinline__ float key_score(uint32_t k) {
     return __uint_as_float(u);
 }
 
+// a value the wavefront holds in every lane, as a uniform (scalar) value
+__device__ __forceinline__ int64_t uniform_i64(int64_t v) {
+    const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+    const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)((uint64_t)v >> 32));
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+
 // number of set bits of `mask` at lanes below this one
 __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
     return __builtin_amdgcn_mbcnt_hi((uint32_t)(mask >> 32),
