@@ -1506,23 +1506,29 @@ __global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, I
 }
 
 // Failed listed rows, again in full: every key of the row's query (all four
-// groups, one wavefront per range of split_blocks candidates) into its key
-// rows, over the launch's failed-row list (a grid-stride loop: the count is
-// known only on the device).
+// groups, one wavefront per range of kRescoreBlocks candidates: a range is a
+// chain of dependent MFMAs, so short ranges keep the few failed rows' latency
+// low) into its key rows, over the launch's failed-row list (a grid-stride
+// loop: the count is known only on the device).
+constexpr int kRescoreBlocks = 256;
+
 template <bool FP8>
 __global__ __launch_bounds__(256) void index_rescore_kernel(SeqTable seqs, IndexArgs a) {
     using F = StoreFmt<FP8>;
     const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
     const int qq = lane >> 4, m = lane & 15;
-    const int64_t units = (int64_t)a.ctl[0] * a.n_split;
+    // ranges per row: enough for the longest row (a key row holds at least
+    // every candidate of its query)
+    const int64_t n_rng = (a.key_stride + kRescoreBlocks - 1) / kRescoreBlocks;
+    const int64_t units = (int64_t)a.ctl[0] * n_rng;
     for (int64_t u = (int64_t)blockIdx.x * 4 + wave; u < units; u += (int64_t)gridDim.x * 4) {
-        const uint32_t item = a.ctl[1 + u / a.n_split];
-        const int split = (int)(u % a.n_split);
+        const uint32_t item = a.ctl[1 + u / n_rng];
+        const int64_t rng = u % n_rng;
         const DevSeq sq = seqs.s[(item >> 2) & 63];
         const int64_t qi = item >> 8;
         const int64_t nb = (sq.pos0 + qi) / a.block_size;
-        const int64_t r_lo = (int64_t)split * a.split_blocks;
-        const int64_t r_hi = nb < r_lo + a.split_blocks ? nb : r_lo + a.split_blocks;
+        const int64_t r_lo = rng * kRescoreBlocks;
+        const int64_t r_hi = nb < r_lo + kRescoreBlocks ? nb : r_lo + kRescoreBlocks;
         if (r_lo >= r_hi) continue;
         bf16x8 af[4];
         const uint4* qf = a.q_frag + (sq.ws_row + qi) * 256;
@@ -1542,14 +1548,17 @@ __global__ __launch_bounds__(256) void index_rescore_kernel(SeqTable seqs, Index
     }
 }
 
-// Failed listed rows: the long-row select over the keys just written.
-__global__ __launch_bounds__(256) void index_select_rescue_kernel(SeqTable seqs, IndexArgs a) {
+// Failed listed rows: the long-row select over the keys just written.  The
+// failed rows are few, so each gets sixteen wavefronts when the candidate
+// list of k plus one 16384-key step fits LDS (k <= 1024), else four.
+template <int NW>
+__global__ __launch_bounds__(64 * NW) void index_select_rescue_kernel(SeqTable seqs, IndexArgs a) {
     extern __shared__ uint32_t lds_keys[];
-    __shared__ SelectShared<4> sh;
+    __shared__ SelectShared<NW> sh;
     const uint32_t count = a.ctl[0];
     for (uint32_t it = blockIdx.x; it < count; it += gridDim.x) {
         const uint32_t item = a.ctl[1 + it];
-        select_row<true, 4>(seqs.s[(item >> 2) & 63], item >> 8, (int)(item & 3), a, lds_keys, sh);
+        select_row<true, NW>(seqs.s[(item >> 2) & 63], item >> 8, (int)(item & 3), a, lds_keys, sh);
         __syncthreads();
     }
 }
@@ -1709,10 +1718,17 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
     else
         hipLaunchKernelGGL(index_rescore_kernel<false>, dim3(1024), dim3(256), 0, stream, seqs, a);
     if ((e = hipGetLastError()) != hipSuccess) return e;
-    const size_t lds_r = select_long_lds<4>(a);
-    if ((e = set_dynamic_lds((const void*)index_select_rescue_kernel, lds_r)) != hipSuccess)
-        return e;
-    hipLaunchKernelGGL(index_select_rescue_kernel, dim3(512), dim3(256), lds_r, stream, seqs, a);
+    if (a.topk <= 1024) {
+        const size_t lds_r = select_long_lds<16>(a);
+        if ((e = set_dynamic_lds((const void*)index_select_rescue_kernel<16>, lds_r)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(index_select_rescue_kernel<16>, dim3(256), dim3(1024), lds_r, stream, seqs, a);
+    } else {
+        const size_t lds_r = select_long_lds<4>(a);
+        if ((e = set_dynamic_lds((const void*)index_select_rescue_kernel<4>, lds_r)) != hipSuccess)
+            return e;
+        hipLaunchKernelGGL(index_select_rescue_kernel<4>, dim3(512), dim3(256), lds_r, stream, seqs, a);
+    }
     return hipGetLastError();
 }
 
