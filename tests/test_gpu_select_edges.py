@@ -111,21 +111,23 @@ def test_sample_overestimate_falls_back_exactly(K, hot_groups):
         assert (hs > 100.0).all() and (hs == hs[0]).all()
 
 
-def test_listed_threshold_above_kth_falls_back_exactly():
+@pytest.mark.parametrize("K,hot_groups", [(512, 4), (2048, 10)])
+def test_listed_threshold_above_kth_falls_back_exactly(K, hot_groups):
     # 1024 queries at B = 1 from t = 40960: tiles start at 40960+ candidates,
     # so their rows are listed.  The list threshold is the j-th largest of a
     # sample of 2048 scores taken as 128 groups of 16 consecutive blocks, group
     # g starting at g * (n0 - 16) // 127 (n0 = the tile's first position);
-    # j = ceil(m k S / n0) = 51 here.  The blocks of the first four groups of
-    # the first tile are the only positive scores: 64 >= j of them, fewer
-    # than k, so the threshold admits fewer than k candidates and the row
-    # must be scored again (later tiles sample other blocks: their lists
-    # overflow instead); every row's answer is still the hot blocks plus the
-    # lowest-numbered others.
-    B, K, n_q, pos0 = 1, 512, 1024, 40960
+    # j = ceil(m k S / n0) (51 at k = 512, 153 at k = 2048).  The blocks of the
+    # first hot_groups groups of the first tile are the only positive scores:
+    # at least j of them, fewer than k, so the threshold admits fewer than k
+    # candidates and the row must be scored again (later tiles sample other
+    # blocks: their lists overflow instead); every row's answer is still the
+    # hot blocks plus the lowest-numbered others.  k = 512 takes the failed
+    # rows' sixteen-wavefront select, k = 2048 the four-wavefront one.
+    B, n_q, pos0 = 1, 1024, 40960
     S, ngrp = 2048, 128
     n0 = pos0 // B
-    hot = sorted({(g * (n0 - 16)) // (ngrp - 1) + i for g in range(4) for i in range(16)})
+    hot = sorted({(g * (n0 - 16)) // (ngrp - 1) + i for g in range(hot_groups) for i in range(16)})
     m = 1.0 + 5.0 / np.sqrt(K * S / n0)
     j = int(np.ceil(m * K * S / n0))
     assert j <= len(hot) < K
