@@ -347,6 +347,13 @@ def stage_times(stages, stream, n: int, flush=None) -> dict:
     return out
 
 
+def _ws_need(sg, cfg, seqs) -> int:
+    """One workspace for the timed forward calls and the separate stage calls
+    timed after them (a forward call run in pieces needs less than its index
+    step alone)."""
+    return max(sg.workspace_size(cfg, seqs, op) for op in (sg.OP_FORWARD, sg.OP_INDEX_TOPK, sg.OP_SPARSE_ATTN))
+
+
 def bench_workload(name: str, args, primary: bool, peaks=None) -> dict:
     """Prepare `name`, time it and return its record (the JSON line's fields
     for the headline workload, a sub-record otherwise)."""
@@ -387,15 +394,15 @@ def bench_workload(name: str, args, primary: bool, peaks=None) -> dict:
     # around; repeating a call recomputes the same outputs
     if wl.loop_steps:
         loop = [[lib_seq(s) for s in wl.step_seqs(k)] for k in range(wl.loop_steps)]
-        ws_n = max(sg.workspace_size(cfg, sq, sg.OP_FORWARD) for sq in loop)
+        ws_n = max(_ws_need(sg, cfg, sq) for sq in loop)
         op_layouts = wl.step_seqs(wl.loop_steps - 1)
     elif args.paged:
         loop = [[lib_seq(s) for s in layouts]]
-        ws_n = sg.workspace_size(cfg, loop[0], sg.OP_FORWARD)
+        ws_n = _ws_need(sg, cfg, loop[0])
         op_layouts = layouts
     else:
         loop = [lib_seqs(wl)]
-        ws_n = sg.workspace_size(cfg, loop[0], sg.OP_FORWARD)
+        ws_n = _ws_need(sg, cfg, loop[0])
         op_layouts = wl.seqs
     stream = torch.cuda.current_stream()
     ws = torch.empty(max(ws_n, 1) + 256, dtype=torch.uint8, device="cuda")

@@ -137,7 +137,9 @@ enum {
  * whose queries are spread over several workgroups (decode-sized calls), for
  * 64 consecutive seqs[] entries at a time.  The size depends on the entries'
  * n_q, pos0 and order, not on their q_offset.  SGQA_OP_FORWARD needs the
- * larger of the two (the steps run one after the other).
+ * larger of the two (the steps run one after the other), except for calls
+ * sgqa_forward runs in pieces (see there): those hold the pieces' index
+ * region, then their attention region, then one 256-byte diagnostics block.
  */
 size_t sgqa_workspace_size(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                            int32_t op);
@@ -157,9 +159,18 @@ size_t sgqa_workspace_size(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
  * (calls of that size never split their attention).  Returns -1, with no
  * block kept, when the index step of these arguments does not use the tiled
  * mode or the arguments are invalid (sgqa_last_error() says which).  The
- * offset is the same for SGQA_OP_INDEX_TOPK and SGQA_OP_FORWARD workspaces.
+ * offset is for sgqa_index_topk workspaces; sgqa_forward_diag_offset gives
+ * it for sgqa_forward's.
  */
 int64_t sgqa_index_diag_offset(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs);
+
+/*
+ * The same diagnostics block in an sgqa_forward workspace: for calls run in
+ * pieces, one block at the end of the workspace that every piece's index
+ * step adds to (cleared by the first); otherwise the offset
+ * sgqa_index_diag_offset gives.  -1 as there.
+ */
+int64_t sgqa_forward_diag_offset(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs);
 
 /*
  * Step 1 -- block-wise token merging (page section "Eight tokens become one
@@ -242,9 +253,23 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
                      void* hip_stream);
 
 /*
- * Steps 1 -> 2+3 -> 4 in order on hip_stream: sgqa_compress, sgqa_index_topk,
- * sgqa_sparse_attn with the arguments above (sel is written and then read).
+ * Steps 1 -> 2+3 -> 4: sgqa_compress, sgqa_index_topk, sgqa_sparse_attn with
+ * the arguments above (sel is written and then read), ordered on hip_stream.
  * ws_bytes must be at least sgqa_workspace_size(..., SGQA_OP_FORWARD).
+ *
+ * Calls of at least 2048 queries whose index step works in the tiled mode and
+ * whose every query takes the unsplit gather attention (long histories, e.g.
+ * a prefill chunk over a 1M-token cache) run in pieces of at least 1024
+ * queries: each piece's index step on hip_stream, its attention on a second
+ * stream of the same device that the library creates on the device's first
+ * such call (default priority, kept until the process ends), after an event
+ * recorded behind that index step -- so a piece's attention overlaps the next
+ * piece's index step.  hip_stream then waits for the second stream, so work
+ * the caller puts on hip_stream later, and an event the caller records there,
+ * come after the whole call, and HIP graph capture of hip_stream captures
+ * both streams.  The outputs equal those of the three calls above run in
+ * order.  Concurrent calls from several host threads on one device are
+ * serialised while they queue their work.
  */
 int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                  const void* proxy_k, const float* comp_logits, const void* ln_gamma,

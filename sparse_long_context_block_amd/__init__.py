@@ -31,7 +31,7 @@ __all__ = [
     "index_topk", "sparse_attn", "forward", "compress_paged", "sparse_attn_paged", "forward_paged",
     "QkConfig", "qk_config", "qk_prep", "sparse_attn_gated", "forward_gated",
     "LIB_PATH", "OP_COMPRESS", "OP_INDEX_TOPK", "OP_SPARSE_ATTN", "OP_FORWARD",
-    "index_diag_offset", "index_diagnostics", "forward_noalloc",
+    "index_diag_offset", "forward_diag_offset", "index_diagnostics", "forward_noalloc",
 ]
 
 LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libsgqa.so")
@@ -175,6 +175,8 @@ def lib() -> ctypes.CDLL:
     L.sgqa_abi_version.restype = I32
     L.sgqa_index_diag_offset.argtypes = [cfgp, seqp, I32]
     L.sgqa_index_diag_offset.restype = I64
+    L.sgqa_forward_diag_offset.argtypes = [cfgp, seqp, I32]
+    L.sgqa_forward_diag_offset.restype = I64
     L.sgqa_forward_noalloc.argtypes = [cfgp, seqp, I32, P, P, P, P, P, P, P, P, P, P, P, P, P, P,
                                        P, P]
     L.sgqa_forward_noalloc.restype = ctypes.c_int
@@ -369,11 +371,19 @@ def index_topk(cfg: Config, seqs: Sequence[Seq], q_idx, w, store, sel, sel_score
 
 
 def index_diag_offset(cfg: Config, seqs: Sequence[Seq]) -> Optional[int]:
-    """Byte offset of the index step's diagnostics block in an OP_INDEX_TOPK or
-    OP_FORWARD workspace of these arguments, or None when the call keeps none
+    """Byte offset of the index step's diagnostics block in an OP_INDEX_TOPK
+    workspace of these arguments, or None when the call keeps none
     (include/sgqa.h, sgqa_index_diag_offset)."""
     arr, n = _seq_array(seqs)
     off = int(lib().sgqa_index_diag_offset(ctypes.byref(cfg), arr, n))
+    return off if off >= 0 else None
+
+
+def forward_diag_offset(cfg: Config, seqs: Sequence[Seq]) -> Optional[int]:
+    """The same block's byte offset in an OP_FORWARD workspace, or None
+    (include/sgqa.h, sgqa_forward_diag_offset)."""
+    arr, n = _seq_array(seqs)
+    off = int(lib().sgqa_forward_diag_offset(ctypes.byref(cfg), arr, n))
     return off if off >= 0 else None
 
 

@@ -187,6 +187,32 @@ def test_prefill_key_workspace(L):
     assert (1 << 20) * 16 <= ws <= (1 << 32) + (1 << 25)
 
 
+def test_forward_pieces_workspace(L):
+    # a chunk of 8,192 queries over a 1M-token cache runs in pieces: its
+    # forward workspace holds the pieces' index region (a piece's key rows,
+    # not the whole call's), their attention region (none: no split) and one
+    # diagnostics block at the end, apart from the index call's layout
+    cfg = sg.config()
+    chunk = [sg.seq(8192, pos0=1_040_384)]
+    fwd = sg.workspace_size(cfg, chunk, sg.OP_FORWARD)
+    idx = sg.workspace_size(cfg, chunk, sg.OP_INDEX_TOPK)
+    assert sg.workspace_size(cfg, chunk, sg.OP_SPARSE_ATTN) == 0
+    assert 0 < fwd < idx
+    assert sg.forward_diag_offset(cfg, chunk) == fwd - 256
+    assert sg.index_diag_offset(cfg, chunk) == idx - 256
+    # the last (longest) piece of 1,024 queries: keys of 131,071 candidates
+    # in rows of 131,136 (64 x an odd count), its indexer rows, the failed-row
+    # list
+    piece = 1024 * 4 * 131136 * 4 + 1024 * 16 * 128 * 2 + (1 + 1024 * 4) * 4 // 256 * 256 + 256 + 256
+    assert fwd == piece + 256
+    # calls that are not split (dense-ish queries, or too few queries) keep
+    # the index call's layout
+    for seqs in ([sg.seq(8192)], [sg.seq(2047, pos0=1_040_384)], [sg.seq(1, pos0=200_000)]):
+        assert sg.forward_diag_offset(cfg, seqs) == sg.index_diag_offset(cfg, seqs)
+        assert sg.workspace_size(cfg, seqs, sg.OP_FORWARD) == max(
+            sg.workspace_size(cfg, seqs, sg.OP_INDEX_TOPK), sg.workspace_size(cfg, seqs, sg.OP_SPARSE_ATTN))
+
+
 def test_workspace_ignores_query_row_offsets(L):
     # workspace rows are numbered per launch, so the size follows the queries
     # a launch holds, not where their rows sit in the caller's tensors (a

@@ -34,7 +34,7 @@ def _forward_then_index(wl, di, cfg):
     more only to expose q_hat for the check (same store, same selections)."""
     seqs = lib_seqs(wl)
     ws = _aligned_ws(sg.workspace_size(cfg, seqs, sg.OP_FORWARD))
-    off = sg.index_diag_offset(cfg, seqs)
+    off = sg.forward_diag_offset(cfg, seqs)
     if off is not None:
         ws[off:off + 256].fill_(0xFF)          # the call must clear it
     run_steps(wl, di, cfg, use_forward=True, ws=ws)
