@@ -743,32 +743,39 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void i
 }
 
 // Top-k of one (query, group) from its score keys: the k largest, equal keys
-// to the lower block id, output in ascending block id, by NW wavefronts (4;
-// 16 for the long rows of calls with few rows).
+// to the lower block id, output in ascending block id.  Rows of at most
+// kWaveSelectKeys keys take one wavefront each (index_select_wave_kernel);
+// longer ones a workgroup of NW wavefronts (4; 16 for the rows of calls with
+// few rows, and for rescued rows).
 // The k-th largest key v and the number krem of entries equal to v that are
 // kept come from a radix select (8-bit digits from the highest bit in which
-// the keys differ, one histogram per wavefront per digit).  Short rows
-// (n <= kSelectStageKeys) are staged in LDS and selected there.  Long rows
-// first bound v from below with a sample (up to 2048 keys, groups of 16
-// consecutive keys spread over the row): the sample's j-th largest key tau,
-// j chosen so that about m k keys are expected at or above it (m = 1 +
-// 5 / sqrt(k S / n), as for the candidate lists).  One
-// pass over the row then streams every key >= tau, with its block id, into
-// an LDS candidate list kept in block order; when a step would overflow it
-// (the sample misjudged a row whose high keys cluster), the list is cut to
+// the keys differ, one histogram per wavefront per digit).  A workgroup
+// first bounds v from below with a sample (a sixteenth of the row, at most
+// 2048 keys, in groups of 16 consecutive keys spread over the row): the
+// sample's j-th largest key tau, j chosen so that about m k keys are expected
+// at or above it (m = 1 + 5 / sqrt(k S / n), as for the candidate lists).
+// One pass over the row then streams every key >= tau, with its block id,
+// into an LDS candidate list kept in block order; when a step would overflow
+// it (the sample misjudged a row whose high keys cluster), the list is cut to
 // its top k and the threshold raised, as in the fused kernel's streaming
 // top-k.  The list then holds every key >= v, so the select and the ordered
 // output run on it alone.  Only a row with fewer than k keys >= tau falls
-// back to selecting over the whole row in global memory.  Outputs are written in block order from four
-// contiguous segments whose offsets come from one exchange.
-constexpr int kSelectStageKeys = 4096;
-constexpr int kSelectSampleMax = 2048;     // sample keys (LDS words) for long rows
+// back to selecting over the whole row in global memory.  Outputs are written
+// in block order from NW contiguous segments whose offsets come from one
+// exchange.
+constexpr int kWaveSelectKeys = 1024;
+constexpr int kSelectSampleMax = 2048;     // sample keys (LDS words)
 
-// candidate list capacity: k plus one step of 1024 keys per wavefront (a
-// step always fits after a cut to the top k); the m k entries expected above
-// the sampled threshold (m from 1.2 to 3.5) fit it without a cut on all but
-// the longest rows
-__host__ __device__ constexpr int select_capacity(int k, int nw) { return k + 1024 * nw; }
+// keys a wavefront scans per step of the candidate pass.  Four-wavefront
+// workgroups take many rows of a few thousand keys: short steps keep the
+// list, and so each workgroup's LDS, small, and more rows run at once per
+// CU.  Sixteen-wavefront workgroups take few long rows: long steps keep more
+// loads in flight per row.
+__host__ __device__ constexpr int select_step(int nw) { return nw == 4 ? 256 : 1024; }
+// candidate list capacity: k plus one step of every wavefront (a step always
+// fits after a cut to the top k)
+__host__ __device__ constexpr int select_capacity(int k, int nw) { return k + select_step(nw) * nw; }
+static_assert(2 * select_capacity(1, 4) >= kSelectSampleMax, "the sample fits the candidate area");
 
 // shared state of a select workgroup of NW wavefronts
 template <int NW>
@@ -966,10 +973,7 @@ __device__ void select_ordered_output(const uint32_t* keys, const int32_t* idx, 
     }
 }
 
-// LONG = false takes the rows of n <= kSelectStageKeys candidates, LONG =
-// true the others (two instantiations, so the short rows keep the smaller
-// register footprint)
-template <bool LONG, int NW>
+template <int NW>
 __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs& a, uint32_t* lds_keys,
                            SelectShared<NW>& sh) {
     constexpr int NT = 64 * NW;
@@ -993,17 +997,10 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
 
     uint32_t prefix = 0, pmask = 0;
     int krem = K;
-    if (!LONG) {
-        for (int i = tid; i < n; i += NT) lds_keys[i] = gkeys[i];
-        __syncthreads();
-        radix_kth(lds_keys, n, K, sh, prefix, pmask, krem);
-        select_ordered_output(lds_keys, nullptr, n, prefix, pmask, krem, sel, ssc, sh);
-        return;
-    }
 
     // ---- threshold tau: the j-th largest of a sample of S keys taken as
     //      S/16 groups of 16 consecutive keys spread over the row ----
-    const int smax = kSelectSampleMax < n / 4 ? kSelectSampleMax : n / 4;
+    const int smax = kSelectSampleMax < n / 16 ? kSelectSampleMax : n / 16;
     const int S = smax / 16 * 16;
     const int ngrp = S / 16;
     for (int i = tid; i < S; i += NT) {
@@ -1024,9 +1021,9 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
     int trem;
     radix_kth(lds_keys, S, j, sh, tau, tmask, trem, 16);
 
-    // ---- candidates: the wavefronts scan the row in steps of 1024 keys
-    //      per wavefront (wavefront w takes the w-th 1024, 16 loads in flight per
-    //      lane) and append the (key, block) pairs that pass the threshold
+    // ---- candidates: the wavefronts scan the row in steps of STEP keys
+    //      per wavefront (wavefront w takes the w-th STEP, STEP / 64 loads in
+    //      flight per lane) and append the (key, block) pairs that pass the threshold
     //      to one list in block order, counts exchanged once per step.  A
     //      step that would overflow the list first compacts it to its top k
     //      (block order kept) and raises the threshold to the k-th key: only
@@ -1038,21 +1035,22 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
     uint32_t thr = tau;
     bool strict = false;          // accept key > thr (after a compaction) or key >= thr
     int pool = 0, par = 0;
-    for (int base = 0; base < n; base += 1024 * NW) {
-        const int wb = base + 1024 * w;
-        uint32_t kv[16];
+    constexpr int STEP = select_step(NW), NU = STEP / 64;
+    for (int base = 0; base < n; base += STEP * NW) {
+        const int wb = base + STEP * w;
+        uint32_t kv[NU];
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < NU; ++u) {
             const int i = wb + 64 * u + lane;
             kv[u] = i < n ? gkeys[i] : 0u;
         }
-        int pos[16];
+        int pos[NU];
         int total = 0, off = 0;
 #pragma unroll 1
         for (int attempt = 0; attempt < 2; ++attempt) {
             int cw = 0;
 #pragma unroll
-            for (int u = 0; u < 16; ++u) {
+            for (int u = 0; u < NU; ++u) {
                 const int i = wb + 64 * u + lane;
                 const bool take = i < n && (strict ? kv[u] > thr : kv[u] >= thr);
                 const uint64_t m = __ballot(take);
@@ -1076,7 +1074,7 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
             strict = true;
         }
 #pragma unroll
-        for (int u = 0; u < 16; ++u) {
+        for (int u = 0; u < NU; ++u) {
             if (pos[u] >= 0) {
                 ckeys[off + pos[u]] = kv[u];
                 cidx[off + pos[u]] = wb + 64 * u + lane;
@@ -1101,7 +1099,6 @@ __device__ void select_row(const DevSeq& sq, int64_t qi, int g, const IndexArgs&
 // key v comes from four 8-bit digit passes over a wavefront-private LDS
 // histogram (bins scanned from the top by a wavefront prefix sum), and the
 // output goes out in block order from ballots -- no workgroup barrier.
-constexpr int kWaveSelectKeys = 1024;
 
 __global__ __launch_bounds__(256) void index_select_wave_kernel(SeqTable seqs, IndexArgs a) {
     constexpr int KPL = kWaveSelectKeys / 64;
@@ -1193,19 +1190,18 @@ __device__ __forceinline__ bool listed_row(const DevSeq& sq, int64_t qi, const I
     return a.listed && list_tile((sq.pos0 + (qi & ~(int64_t)(kScoreTileQueries - 1))) / a.block_size, a.topk);
 }
 
-template <bool LONG, int NW>
+template <int NW>
 __global__ __launch_bounds__(64 * NW) void index_select_kernel(SeqTable seqs, IndexArgs a) {
-    extern __shared__ uint32_t lds_keys[];    // staged row, or candidate keys + block ids
+    extern __shared__ uint32_t lds_keys[];    // the sample, then candidate keys + block ids
     __shared__ SelectShared<NW> sh;
     const DevSeq sq = seqs.s[blockIdx.y];
     const int64_t qi = blockIdx.x / kGroups;
     const int g = blockIdx.x % kGroups;
     if (qi >= sq.n_q) return;
     const int64_t n = (sq.pos0 + qi) / a.block_size;
-    if ((n > kSelectStageKeys) != LONG) return;
-    if (!LONG && n <= kWaveSelectKeys) return;     // one wavefront per row
-    if (LONG && listed_row(sq, qi, a)) return;    // selected from its lists
-    select_row<LONG, NW>(sq, qi, g, a, lds_keys, sh);
+    if (n <= kWaveSelectKeys) return;              // one wavefront per row
+    if (listed_row(sq, qi, a)) return;             // selected from its lists
+    select_row<NW>(sq, qi, g, a, lds_keys, sh);
 }
 
 // ---------------------------------------------------------------------------
@@ -1558,28 +1554,26 @@ __global__ __launch_bounds__(64 * NW) void index_select_rescue_kernel(SeqTable s
     const uint32_t count = a.ctl[0];
     for (uint32_t it = blockIdx.x; it < count; it += gridDim.x) {
         const uint32_t item = a.ctl[1 + it];
-        select_row<true, NW>(seqs.s[(item >> 2) & 63], item >> 8, (int)(item & 3), a, lds_keys, sh);
+        select_row<NW>(seqs.s[(item >> 2) & 63], item >> 8, (int)(item & 3), a, lds_keys, sh);
         __syncthreads();
     }
 }
 
 }  // namespace
 
+// the candidate list (keys, then block ids), which the sample uses first
 template <int NW>
 static size_t select_long_lds(const IndexArgs& a) {
-    const int64_t max_b = a.key_stride;
-    const int64_t cand = 2 * (int64_t)select_capacity(a.topk, NW);
-    const int64_t samp = max_b / 4 < kSelectSampleMax ? max_b / 4 : kSelectSampleMax;
-    return (size_t)(cand > samp ? cand : samp) * sizeof(uint32_t);
+    return (size_t)2 * select_capacity(a.topk, NW) * sizeof(uint32_t);
 }
 
 template <int NW>
 static hipError_t launch_select_long(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a, hipStream_t stream) {
     const size_t lds = select_long_lds<NW>(a);
-    hipError_t e = set_dynamic_lds((const void*)index_select_kernel<true, NW>, lds);
+    hipError_t e = set_dynamic_lds((const void*)index_select_kernel<NW>, lds);
     if (e != hipSuccess) return e;
     dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
-    hipLaunchKernelGGL((index_select_kernel<true, NW>), grid, dim3(64 * NW), lds, stream, seqs, a);
+    hipLaunchKernelGGL((index_select_kernel<NW>), grid, dim3(64 * NW), lds, stream, seqs, a);
     return hipGetLastError();
 }
 
@@ -1588,16 +1582,12 @@ static hipError_t launch_select_long(const SeqTable& seqs, int64_t max_nq, const
 static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
                                 hipStream_t stream, bool keyed_long = true) {
     const int64_t max_b = a.key_stride;
-    dim3 grid((unsigned)(max_nq * kGroups), (unsigned)seqs.n);
     // short rows (skipped when every sequence's first query already has a
-    // long row): a wavefront per row up to kWaveSelectKeys keys, then the
-    // staged row
-    int64_t min_b = INT64_MAX, max_rows_b = 0, rows = 0;
+    // long row): a wavefront per row up to kWaveSelectKeys keys
+    int64_t min_b = INT64_MAX, rows = 0;
     for (int i = 0; i < seqs.n; ++i) {
         const int64_t b = seqs.s[i].pos0 / a.block_size;
-        const int64_t bl = (seqs.s[i].pos0 + seqs.s[i].n_q - 1) / a.block_size;   // the last query's
         min_b = b < min_b ? b : min_b;
-        max_rows_b = seqs.s[i].n_q > 0 && bl > max_rows_b ? bl : max_rows_b;
         rows += seqs.s[i].n_q * kGroups;
     }
     hipError_t e = hipSuccess;
@@ -1606,18 +1596,11 @@ static hipError_t launch_select(const SeqTable& seqs, int64_t max_nq, const Inde
                            stream, seqs, a);
         if ((e = hipGetLastError()) != hipSuccess) return e;
     }
-    if (min_b <= kSelectStageKeys && max_rows_b > kWaveSelectKeys) {
-        const size_t lds_s = (size_t)(max_b < kSelectStageKeys ? max_b : kSelectStageKeys) * sizeof(uint32_t);
-        e = set_dynamic_lds((const void*)index_select_kernel<false, 4>, lds_s);
-        if (e != hipSuccess) return e;
-        hipLaunchKernelGGL((index_select_kernel<false, 4>), grid, dim3(256), lds_s, stream, seqs, a);
-        if ((e = hipGetLastError()) != hipSuccess) return e;
-    }
-    if (max_b <= kSelectStageKeys || !keyed_long) return e;
-    // long rows: a few rows (decode) get sixteen wavefronts each, so each
-    // row's scan has four times the loads in flight
-    // (the candidate list then takes k plus one 16384-key step: k <= 1024
-    // keeps it within LDS)
+    if (max_b <= kWaveSelectKeys || !keyed_long) return e;
+    // longer rows: a few rows (decode) get sixteen wavefronts each, with
+    // 1024-key steps, so each row's scan has sixteen times the loads in
+    // flight (the candidate list then takes k plus one 16384-key step:
+    // k <= 1024 keeps it within LDS)
     return rows <= 1024 && a.topk <= 1024 ? launch_select_long<16>(seqs, max_nq, a, stream)
                                           : launch_select_long<4>(seqs, max_nq, a, stream);
 }
@@ -1669,7 +1652,7 @@ hipError_t launch_index_tiled(const SeqTable& seqs, int64_t max_nq, const IndexA
             if (l && n0 > n0_listed) n0_listed = n0;
             any_keyed |= !l;
             const int64_t q1 = q0 + kScoreTileQueries < d.n_q ? q0 + kScoreTileQueries : d.n_q;
-            keyed_long |= !l && (d.pos0 + q1 - 1) / a.block_size > kSelectStageKeys;
+            keyed_long |= !l && (d.pos0 + q1 - 1) / a.block_size > kWaveSelectKeys;
         }
     }
     hipError_t e;

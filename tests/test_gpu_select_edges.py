@@ -6,11 +6,11 @@ id), so no oracle run is needed:
 
 * every score equal (indexer weights zero): every row keeps blocks
   0..min(n, k)-1 -- rows of up to 1024 candidates in the one-wavefront
-  select, longer ones staged in LDS or sampled.  Long rows (more than 4096 candidates) then start from a
+  select, longer ones in the sampled select, which then starts from a
   threshold every key passes, so the candidate list overflows and is cut to
   its top k, repeatedly -- the compaction path, with all keys tied;
 * a row whose only positive scores sit at positions the long-row select
-  samples (2048 blocks at k = 3072, 512 at k = 1024): the sampled threshold
+  samples (1008 blocks at k = 3072, 512 at k = 1024): the sampled threshold
   admits fewer than k keys, so the select must fall back to a radix over
   the whole row; the answer is those blocks plus the lowest-numbered others
   (score 0, ties to the lower id);
@@ -52,7 +52,7 @@ def _run_index(cfg, seqs, n_rows, q_idx, w, store):
     (2, 40000, 1, 512),           # decode-sized, k <= 1024: 16-wavefront select
     (1100, 300000, 8, 512),       # tiled call, listed rows: every segment's list overflows
     (1100, 4000, 8, 64),          # tiled call, rows of 500..637 candidates: one wavefront per row
-    (1100, 0, 1, 64),             # rows of 0..1099 candidates: per-wavefront rows, then staged
+    (1100, 0, 1, 64),             # rows of 0..1099 candidates: per-wavefront rows, then sampled
 ])
 def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
     log("case equal scores", n_q, pos0, B, K)
@@ -71,19 +71,20 @@ def test_equal_scores_keep_lowest_block_ids(n_q, pos0, B, K):
     assert (ssc == 0.0).all()
 
 
-@pytest.mark.parametrize("K,hot_groups", [(3072, 128), (1024, 32)])
+@pytest.mark.parametrize("K,hot_groups", [(3072, 63), (1024, 32)])
 def test_sample_overestimate_falls_back_exactly(K, hot_groups):
     B = 1
     t = 16383                        # one query; n = 16383 candidate blocks
     n = t // B
-    # the long-row select's sample: S keys in S/16 groups of 16 consecutive
-    # keys, group g starting at g * (n - 16) // (S/16 - 1); the first
-    # hot_groups groups hold the only positive scores, fewer than k of them
-    # but more than the sample rank the threshold is taken at
-    S = min(2048, n // 4) // 16 * 16
+    # the long-row select's sample: S keys (a sixteenth of the row, at most
+    # 2048) in S/16 groups of 16 consecutive keys, group g starting at
+    # g * (n - 16) // (S/16 - 1); the first hot_groups groups hold the only
+    # positive scores, fewer than k of them but more than the sample rank the
+    # threshold is taken at
+    S = min(2048, n // 16) // 16 * 16
     ngrp = S // 16
     hot = sorted({(g * (n - 16)) // (ngrp - 1) + i for g in range(hot_groups) for i in range(16)})
-    assert len(hot) == 16 * hot_groups < K and hot[-1] < n
+    assert hot_groups <= ngrp and len(hot) == 16 * hot_groups < K and hot[-1] < n
     assert len(hot) >= -(-3 * K * S // n)
     log("case sampled-threshold fallback", n, K, len(hot))
     # u: zero on the rotary span (dims 0..31), one elsewhere, so q_hat . u

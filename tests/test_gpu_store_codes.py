@@ -37,7 +37,7 @@ def _forward(wl):
     "prefill_300_b8_k64",            # every row has <= k candidates: fused kernel
     "tiny_prefill_256",              # split scoring, short rows
     "decode_small",                  # split scoring, long rows, split attention
-    "prefill_2000_b1_k64",           # tiled keyed scoring, wave and staged selects
+    "prefill_2000_b1_k64",           # tiled keyed scoring, wave and sampled selects
     "chunk_40000_1024_b1_k64",       # listed tiles: sample, threshold, candidate lists
     "chunk_1003_1997_b8_k64",        # a chunk over an existing cache
 ])
