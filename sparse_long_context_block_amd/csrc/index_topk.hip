@@ -1484,20 +1484,18 @@ __global__ __launch_bounds__(256) void index_list_select_kernel(SeqTable seqs, I
     // entry's output slot is the number of kept entries before it
     const int quota = K - n_gt;
     int gt_run = gt_off, eq_run = off - gt_off;   // every listed key is >= tau
+    // (both counters advance by value, not through a selected reference,
+    // which kept them in scratch memory)
     list_entries(krow, lists, s0, s1, [&](uint2 kv) {
-        if (kv.x > thr) {
-            const int pos = gt_run + (eq_run < quota ? eq_run : quota);
+        const bool gt = kv.x > thr;
+        const int eq_kept = eq_run < quota ? eq_run : quota;
+        if (gt || eq_run < quota) {
+            const int pos = gt_run + eq_kept;
             sel[pos] = (int32_t)kv.y;
             if (ssc) ssc[pos] = key_score(kv.x);
-            ++gt_run;
-        } else {
-            if (eq_run < quota) {
-                const int pos = gt_run + eq_run;
-                sel[pos] = (int32_t)kv.y;
-                if (ssc) ssc[pos] = key_score(kv.x);
-            }
-            ++eq_run;
         }
+        gt_run += gt ? 1 : 0;
+        eq_run += gt ? 0 : 1;
     });
 }
 
