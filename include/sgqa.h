@@ -32,7 +32,11 @@
  *           and are meaningless after the call.
  * Streams.  Work is enqueued on hip_stream (a hipStream_t; NULL = the null
  *           stream) and returns before it completes.  Buffers must stay alive
- *           until the stream reaches the end of the call's work.
+ *           until the stream reaches the end of the call's work.  hip_stream
+ *           must belong to the calling thread's current device (kernel
+ *           attributes and the library's per-device state follow the current
+ *           device); a stream of another device returns SGQA_ERR_CONFIG
+ *           before any work is enqueued.
  * Sequences. A call processes n_seqs >= 1 independent sequences described by
  *           a HOST array of sgqa_seq.  Query-side tensors are packed over all
  *           sequences (rows q_offset .. q_offset+n_q-1 belong to a sequence);
@@ -41,8 +45,9 @@
  *           pos0 + i and cache_len == pos0 + n_q (the new tokens' K/V, proxy
  *           keys and compression logits are already written into the caches).
  * Errors.   Every check of arguments, shapes and descriptors runs on the host
- *           before the first HIP call, so a rejected call has enqueued nothing
- *           and touched no memory.  Entry points return SGQA_OK (0) or a
+ *           before any work is enqueued (the only HIP calls before that are
+ *           device and stream queries), so a rejected call has enqueued
+ *           nothing and touched no memory.  Entry points return SGQA_OK (0) or a
  *           negative sgqa_status; sgqa_last_error() then holds a message for
  *           the calling thread.  A failing HIP launch returns SGQA_ERR_HIP
  *           (work enqueued before it may still run).  Nothing aborts and no

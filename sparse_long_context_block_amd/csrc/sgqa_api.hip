@@ -55,6 +55,21 @@ int hip_fail(hipError_t e, const char* what) {
     return fail(SGQA_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
 
+// the stream must belong to the current device: kernel attributes, the
+// static scratch and the forward's second stream are kept per current device
+int check_stream(void* hip_stream) {
+    int dev = 0;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+    if (!hip_stream) return SGQA_OK;
+    int sdev = 0;
+    e = hipStreamGetDevice((hipStream_t)hip_stream, &sdev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    if (sdev != dev)
+        return fail(SGQA_ERR_CONFIG, "hip_stream belongs to device %d, the current device is %d", sdev, dev);
+    return SGQA_OK;
+}
+
 constexpr int64_t kMaxExtent = (int64_t)1 << 40;   // bound on offsets / lengths
 constexpr size_t kAlign = 256;
 
@@ -926,6 +941,7 @@ int sgqa_compress(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
     if (!proxy_k || !comp_logits || !store)
         return fail(SGQA_ERR_NULL, "proxy_k, comp_logits and store are required");
     if ((rc = check_aligned({{proxy_k, "proxy_k"}, {comp_logits, "comp_logits"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}}))) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, Paging(), ln_gamma, ln_beta, store,
                         (hipStream_t)hip_stream);
 }
@@ -947,6 +963,7 @@ int sgqa_compress_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_
     Paging pg;
     pg.table = page_table;
     pg.n_pages = n_pages;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_compress(cfg, seqs, n_seqs, proxy_pages, logit_pages, pg, ln_gamma, ln_beta, store,
                         (hipStream_t)hip_stream);
 }
@@ -963,6 +980,7 @@ int sgqa_index_topk(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs
     if ((rc = check_aligned({{q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {store, "store"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q_hat_out, "q_hat_out"}}))) return rc;
     const IndexPlan p = plan_index(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_index(cfg, seqs, n_seqs, p, q_idx, w, rms_gamma, store, sel, sel_scores,
                      q_hat_out, ws, (hipStream_t)hip_stream);
 }
@@ -980,6 +998,7 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
     if ((rc = check_aligned({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {sel, "sel"}, {out, "out"}, {lse, "lse"}}))) return rc;
     const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, nullptr, ws,
                     (hipStream_t)hip_stream);
 }
@@ -997,6 +1016,7 @@ int sgqa_sparse_attn_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
     if ((rc = check_aligned({{q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {sel, "sel"}, {out, "out"}, {lse, "lse"}, {gate, "gate"}}))) return rc;
     const AttnPlan p = plan_attn(cfg, seqs, n_seqs);
     if ((rc = check_ws(p.ws, ws, ws_bytes))) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_attn(cfg, seqs, n_seqs, p, q, k_cache, v_cache, Paging(), sel, out, lse, gate, ws,
                     (hipStream_t)hip_stream);
 }
@@ -1018,6 +1038,7 @@ int sgqa_sparse_attn_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t
     Paging pg;
     pg.table = page_table;
     pg.n_pages = n_pages;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_attn(cfg, seqs, n_seqs, p, q, k_pages, v_pages, pg, sel, out, lse, gate, ws,
                     (hipStream_t)hip_stream);
 }
@@ -1038,6 +1059,7 @@ int sgqa_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs,
                     "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache and out "
                     "are required");
     if ((rc = check_aligned({{proxy_k, "proxy_k"}, {comp_logits, "comp_logits"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}, {q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {out, "out"}, {lse, "lse"}}))) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
                        rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, nullptr, ws,
                        ws_bytes, (hipStream_t)hip_stream);
@@ -1068,6 +1090,7 @@ int sgqa_forward_noalloc(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n
                     need, kNoAllocScratchBytes);
     void* ws = scratch_address(&rc);
     if (!ws) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
                        rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, nullptr, ws,
                        kNoAllocScratchBytes, (hipStream_t)hip_stream, false);
@@ -1089,6 +1112,7 @@ int sgqa_forward_gated(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_s
                     "proxy_k, comp_logits, store, q_idx, w, sel, q, k_cache, v_cache, out and gate "
                     "are required");
     if ((rc = check_aligned({{proxy_k, "proxy_k"}, {comp_logits, "comp_logits"}, {ln_gamma, "ln_gamma"}, {ln_beta, "ln_beta"}, {store, "store"}, {q_idx, "q_idx"}, {w, "w"}, {rms_gamma, "rms_gamma"}, {sel, "sel"}, {sel_scores, "sel_scores"}, {q, "q"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}, {out, "out"}, {lse, "lse"}, {gate, "gate"}}))) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_forward(cfg, seqs, n_seqs, proxy_k, comp_logits, ln_gamma, ln_beta, store, q_idx, w,
                        rms_gamma, sel, sel_scores, q, k_cache, v_cache, Paging(), out, lse, gate, ws,
                        ws_bytes, (hipStream_t)hip_stream);
@@ -1114,6 +1138,7 @@ int sgqa_forward_paged(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_s
     Paging pg;
     pg.table = page_table;
     pg.n_pages = n_pages;
+    if ((rc = check_stream(hip_stream))) return rc;
     return run_forward(cfg, seqs, n_seqs, proxy_pages, logit_pages, ln_gamma, ln_beta, store, q_idx, w,
                        rms_gamma, sel, sel_scores, q, k_pages, v_pages, pg, out, lse, gate, ws, ws_bytes,
                        (hipStream_t)hip_stream);
@@ -1138,6 +1163,7 @@ int sgqa_qk_prep(const sgqa_config* cfg, const sgqa_qk_config* qk, const sgqa_se
         return fail(SGQA_ERR_NULL, "v_raw and v_cache go together");
     if ((rc = check_aligned({{q_raw, "q_raw"}, {k_raw, "k_raw"}, {v_raw, "v_raw"}, {q_gamma, "q_gamma"}, {k_gamma, "k_gamma"}, {q_out, "q_out"}, {k_cache, "k_cache"}, {v_cache, "v_cache"}}))) return rc;
     if (page_table && (rc = check_paging(seqs, n_seqs, page_table, page_table_len, n_pages))) return rc;
+    if ((rc = check_stream(hip_stream))) return rc;
     sgqa::QkPrepArgs a;
     a.q_raw = (const uint16_t*)q_raw;
     a.k_raw = (const uint16_t*)k_raw;
