@@ -26,6 +26,9 @@ CASES = {
     # the first and second sequences
     "three sequences": lambda: W._multi("pieces_multi", [(1500, 200_000), (1300, 150_003), (900, 140_000)],
                                         B=8, K=512),
+    # B = 1, k = 2048: listed rows of 150,000+ candidates, pieces of 1,040 and
+    # 1,060 queries (k above 1024: four-wavefront rescue select)
+    "one sequence, B = 1": lambda: W.make("chunk_150000_2100_b1_k2048"),
 }
 
 
