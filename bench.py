@@ -12,7 +12,11 @@ per group, B=8, k = 512 blocks = 4,096 tokens) is the headline record; the
 cached tokens ride along as sub-records of the same JSON line, each with its
 own roofline, and so does the same 1M chunk with the correlated variant of
 the indexer inputs (`chunk_1m_corr64`, labelled `variant`: neighbouring
-queries select overlapping blocks; not a benchmark configuration).
+queries select overlapping blocks; not a benchmark configuration).  The
+1M-token prefill as 128 chained calls of 8,192 queries, at B=8 (k = 512
+blocks) and at B=1 (k = 2,048 blocks), closes the line: each such
+sub-record times one pass over all 128 calls (`loop_pass_s`, one layer),
+without warmup, whatever --steps says.
 
 Per workload: whole-step throughput over the timed steps, the distribution
 of single step times (warm, and cold: a 512 MiB write and a 512 MiB read
@@ -303,7 +307,8 @@ def event_time_ms(fn, stream, reps: int) -> float:
 # ---------------------------------------------------------------------------
 
 DEFAULT_WORKLOAD = "chunk_1m"
-DEFAULT_SUBS = ("prefill_64k", "decode_64x256k", "chunk_1m_corr64")
+DEFAULT_SUBS = ("prefill_64k", "decode_64x256k", "chunk_1m_corr64", "prefill_1m_chained",
+                "prefill_1m_chained_b1")
 
 
 def dense_split(wl, seqs):
@@ -702,9 +707,16 @@ def main() -> int:
     if peaks:
         rec["measured_peaks"] = peaks
     if subs:
+        from synth import workloads as W
         rec["sub_records"] = {}
         for s in subs:
-            rec["sub_records"][s] = bench_workload(s, args, primary=False, peaks=peaks)
+            sargs = args
+            steps = W.make(s).loop_steps
+            if steps:
+                # a chained workload: one pass over all of its calls
+                sargs = argparse.Namespace(**vars(args))
+                sargs.steps, sargs.warmup = steps, 0
+            rec["sub_records"][s] = bench_workload(s, sargs, primary=False, peaks=peaks)
     print(json.dumps(rec), flush=True)
     return 0
 
