@@ -105,8 +105,8 @@ def test_decode_64_sequences():
 
 @pytest.mark.timeout(900)
 def test_chunk_over_1m_cache():
-    st = _check("chunk_1m", 512, store_blocks=4096)
-    assert st["rows"] >= 512
+    st = _check("chunk_1m", 1024, store_blocks=4096)
+    assert st["rows"] >= 1024
     # the chunk's long rows go through candidate lists; some lists cannot give
     # the exact top k and those rows are scored again over every candidate:
     # the device counted them and the checked rows include them
