@@ -22,8 +22,10 @@ from .gpu_setup import poison_store
 
 pytestmark = pytest.mark.gpu
 
+# chunk_150000_2100: 2,100 queries over a 152,100-token cache, which both
+# forward calls run in two pieces over the second stream
 @pytest.mark.parametrize("name", ["chunk_1003_997_b8_k64", "decode_small", "decode_64_small", "prefill_2000_b1_k64",
-                                  "prefill_1003_b16_k8"])
+                                  "prefill_1003_b16_k8", "chunk_150000_2100"])
 def test_paged_forward_matches_contiguous(name):
     wl = W.make(name)
     log("case paged", name)
