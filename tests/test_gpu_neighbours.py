@@ -96,10 +96,11 @@ def test_qk_prep_matches_oracle(span, base):
                                v_cache[s.kv_offset + t].view(torch.int16))
 
 
-@pytest.mark.parametrize("name", ["chunk_1003_1997_b8_k64", "decode_small"])
+@pytest.mark.parametrize("name", ["chunk_1003_1997_b8_k64", "decode_small", "chunk_150000_2100"])
 def test_gated_attention(name):
     # the chunk's queries t < 2048 take the tiled kernel, the rest the
-    # gather kernel; the decode is split and merged
+    # gather kernel; the decode is split and merged; the forward calls over
+    # the 152K-token cache run in two pieces over the second stream
     wl = W.make(name)
     log("case gated", name)
     di, cfg = prepare(wl)
