@@ -262,6 +262,12 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
  * the arguments above (sel is written and then read), ordered on hip_stream.
  * ws_bytes must be at least sgqa_workspace_size(..., SGQA_OP_FORWARD).
  *
+ * Decode-shaped calls (the index step scores with per-query wavefronts and
+ * every sequence's queries lie inside one block, e.g. one new token per
+ * sequence) read none of the blocks they complete, so step 1 runs inside the
+ * index step's scoring launch instead of a launch of its own; the store rows
+ * written are the same.
+ *
  * Calls of at least 2048 queries whose index step works in the tiled mode and
  * whose every query takes the unsplit gather attention (long histories, e.g.
  * a prefill chunk over a 1M-token cache) run in pieces of at least 1024

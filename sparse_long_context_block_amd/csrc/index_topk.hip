@@ -32,7 +32,7 @@
 //     each query's candidates over many score wavefronts that write keys;
 //   * index_score_tile_kernel + index_select_kernel -- calls of 1024+
 //     queries score 16 queries per workgroup against store tiles in LDS.
-#include "sgqa_internal.hpp"
+#include "compress_block.hpp"
 
 namespace sgqa {
 namespace {
@@ -424,13 +424,14 @@ struct LaneRows {
     }
 };
 
+// one scoring wavefront: column bx of sequence entry sq (query bx / n_split,
+// candidate split bx % n_split); xp is the wavefront's 1 KiB of LDS
 template <bool FP8>
-__global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArgs a) {
+__device__ __forceinline__ void score_split_wave(const DevSeq& sq, int64_t bx, const IndexArgs& a,
+                                                 uint4 (*xp)[4][16]) {
     using F = LaneRows<FP8>;
-    __shared__ uint4 xp[4][4][16];
-    const DevSeq sq = seqs.s[blockIdx.y];
-    const int64_t qi = blockIdx.x / a.n_split;
-    const int split = blockIdx.x % a.n_split;
+    const int64_t qi = bx / a.n_split;
+    const int split = (int)(bx % a.n_split);
     if (qi >= sq.n_q) return;
     const int64_t t = sq.pos0 + qi;
     const int64_t row = sq.q_offset + qi;
@@ -478,6 +479,29 @@ __global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArg
             if (r0 + m < r_hi) keys[r0 + m] = score_key(s);
         }
     }
+}
+
+template <bool FP8>
+__global__ __launch_bounds__(64) void index_score_kernel(SeqTable seqs, IndexArgs a) {
+    __shared__ uint4 xp[4][4][16];
+    score_split_wave<FP8>(seqs.s[blockIdx.y], blockIdx.x, a, xp);
+}
+
+// The same scoring launch carrying step 1 for calls whose queries read none
+// of the blocks the call completes (each sequence's queries lie inside one
+// block, e.g. one new token per sequence): column 0 of each sequence merges
+// its completed block, if any, into the store row that no score of the
+// launch reads; the other columns score.  One launch fewer per decode step.
+template <bool FP8, int B>
+__global__ __launch_bounds__(64) void index_score_merge_kernel(SeqTable seqs, IndexArgs a, CompressArgs c) {
+    __shared__ uint4 xp[4][4][16];
+    const DevSeq sq = seqs.s[blockIdx.y];
+    if (blockIdx.x == 0) {
+        const int64_t r = sq.pos0 / B;
+        if (r < (sq.pos0 + sq.n_q) / B) compress_block<B>(sq, r, c);
+        return;
+    }
+    score_split_wave<FP8>(sq, (int64_t)blockIdx.x - 1, a, xp);
 }
 
 // ---------------------------------------------------------------------------
@@ -1620,15 +1644,36 @@ hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexAr
     return hipGetLastError();
 }
 
-hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
+template <bool FP8>
+hipError_t launch_score_merge(const SeqTable& seqs, dim3 grid, const IndexArgs& a, const CompressArgs& c,
                               hipStream_t stream) {
+    switch (c.block_size) {
+        case 1: hipLaunchKernelGGL((index_score_merge_kernel<FP8, 1>), grid, dim3(64), 0, stream, seqs, a, c); break;
+        case 2: hipLaunchKernelGGL((index_score_merge_kernel<FP8, 2>), grid, dim3(64), 0, stream, seqs, a, c); break;
+        case 4: hipLaunchKernelGGL((index_score_merge_kernel<FP8, 4>), grid, dim3(64), 0, stream, seqs, a, c); break;
+        case 8: hipLaunchKernelGGL((index_score_merge_kernel<FP8, 8>), grid, dim3(64), 0, stream, seqs, a, c); break;
+        case 16: hipLaunchKernelGGL((index_score_merge_kernel<FP8, 16>), grid, dim3(64), 0, stream, seqs, a, c); break;
+        default: return hipErrorInvalidValue;
+    }
+    return hipGetLastError();
+}
+
+hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
+                              hipStream_t stream, const CompressArgs* merge) {
     if (max_nq <= 0 || seqs.n <= 0) return hipSuccess;
     dim3 grid((unsigned)(max_nq * a.n_split), (unsigned)seqs.n);
-    if (a.store_fp8)
-        hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(64), 0, stream, seqs, a);
-    else
-        hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(64), 0, stream, seqs, a);
-    hipError_t e = hipGetLastError();
+    hipError_t e;
+    if (merge) {
+        grid.x += 1;
+        e = a.store_fp8 ? launch_score_merge<true>(seqs, grid, a, *merge, stream)
+                        : launch_score_merge<false>(seqs, grid, a, *merge, stream);
+    } else {
+        if (a.store_fp8)
+            hipLaunchKernelGGL(index_score_kernel<true>, grid, dim3(64), 0, stream, seqs, a);
+        else
+            hipLaunchKernelGGL(index_score_kernel<false>, grid, dim3(64), 0, stream, seqs, a);
+        e = hipGetLastError();
+    }
     if (e != hipSuccess) return e;
     return launch_select(seqs, max_nq, a, stream);
 }

@@ -418,9 +418,8 @@ int64_t fill_table(sgqa::SeqTable& tab, const sgqa_seq* s, int32_t first, int32_
 // ---------------------------------------------------------------------------
 // the three steps (arguments already validated)
 // ---------------------------------------------------------------------------
-int run_compress(const sgqa_config* c, const sgqa_seq* s, int32_t n, const void* proxy_k,
-                 const float* logits, const Paging& pg, const void* ln_gamma, const void* ln_beta,
-                 void* store, hipStream_t st) {
+sgqa::CompressArgs compress_args(const sgqa_config* c, const void* proxy_k, const float* logits,
+                                 const Paging& pg, const void* ln_gamma, const void* ln_beta, void* store) {
     sgqa::CompressArgs a;
     a.proxy_k = (const uint16_t*)proxy_k;
     a.logits = logits;
@@ -433,6 +432,24 @@ int run_compress(const sgqa_config* c, const sgqa_seq* s, int32_t n, const void*
     a.store_q8 = c->store_q8;
     a.eps = c->eps_ln;
     rope_table(c, a.theta);
+    return a;
+}
+
+// true when no query of the call has a block the call completes among its
+// candidates: every sequence's queries lie inside one block (query t sees
+// blocks below t / B; the call completes the blocks below (pos0 + n_q) / B
+// from pos0 / B on, so at most the block of its queries)
+bool merge_unread_by_call(const sgqa_config* c, const sgqa_seq* s, int32_t n) {
+    const int64_t B = c->block_size;
+    for (int32_t i = 0; i < n; ++i)
+        if (s[i].n_q > 0 && (s[i].pos0 + s[i].n_q - 1) / B != s[i].pos0 / B) return false;
+    return true;
+}
+
+int run_compress(const sgqa_config* c, const sgqa_seq* s, int32_t n, const void* proxy_k,
+                 const float* logits, const Paging& pg, const void* ln_gamma, const void* ln_beta,
+                 void* store, hipStream_t st) {
+    const sgqa::CompressArgs a = compress_args(c, proxy_k, logits, pg, ln_gamma, ln_beta, store);
     const int B = c->block_size;
     for (int32_t first = 0; first < n; first += sgqa::kMaxSeqsPerLaunch) {
         const int32_t cnt = std::min<int32_t>(sgqa::kMaxSeqsPerLaunch, n - first);
@@ -450,10 +467,13 @@ int run_compress(const sgqa_config* c, const sgqa_seq* s, int32_t n, const void*
 // diag_at: the diagnostics block to use instead of the plan's own (the
 // pieces of a split forward call share one), cleared by this call only when
 // diag_clear is set
+// merge: step 1 for split-mode calls whose queries read none of the blocks
+// they complete, carried in the scoring launch (null: run separately)
 int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPlan& p,
               const void* q_idx, const float* w, const void* rms_gamma, const void* store,
               int32_t* sel, float* sel_scores, void* q_hat_out, void* ws, hipStream_t st,
-              uint32_t* diag_at = nullptr, bool diag_clear = true) {
+              uint32_t* diag_at = nullptr, bool diag_clear = true,
+              const sgqa::CompressArgs* merge = nullptr) {
     sgqa::IndexArgs a;
     a.q_idx = (const uint16_t*)q_idx;
     a.w = w;
@@ -530,7 +550,7 @@ int run_index(const sgqa_config* c, const sgqa_seq* s, int32_t n, const IndexPla
         sgqa::SeqTable tab;
         const int64_t mx = fill_table(tab, s, first, cnt, [](const sgqa_seq& q) { return q.n_q; });
         if (tab.n == 0) continue;
-        hipError_t e = p.mode == IndexMode::Split ? sgqa::launch_index_split(tab, mx, a, st)
+        hipError_t e = p.mode == IndexMode::Split ? sgqa::launch_index_split(tab, mx, a, st, merge)
                                                   : sgqa::launch_index_topk(tab, mx, a, st);
         if (e != hipSuccess) return hip_fail(e, "index_topk launch");
     }
@@ -780,16 +800,23 @@ int run_forward(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seqs, co
     const ForwardLayout fl = plan_forward(cfg, seqs, n_seqs, allow_pieces);
     int rc = check_ws(fl.ws, ws, ws_bytes);
     if (rc) return rc;
-    if ((rc = run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, pg, ln_gamma, ln_beta, store, st)))
-        return rc;
     if (!fl.pieces) {
         const IndexPlan ip = plan_index(cfg, seqs, n_seqs);
         const AttnPlan ap = plan_attn(cfg, seqs, n_seqs);
+        // decode-shaped calls: the merge rides in the scoring launch (no
+        // score of the call reads the rows it writes)
+        const bool carry = ip.mode == IndexMode::Split && merge_unread_by_call(cfg, seqs, n_seqs);
+        const sgqa::CompressArgs ca = compress_args(cfg, proxy_k, comp_logits, pg, ln_gamma, ln_beta, store);
+        if (!carry &&
+            (rc = run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, pg, ln_gamma, ln_beta, store, st)))
+            return rc;
         if ((rc = run_index(cfg, seqs, n_seqs, ip, q_idx, w, rms_gamma, store, sel, sel_scores, nullptr, ws,
-                            st)))
+                            st, nullptr, true, carry ? &ca : nullptr)))
             return rc;
         return run_attn(cfg, seqs, n_seqs, ap, q, k_cache, v_cache, pg, sel, out, lse, gate, ws, st);
     }
+    if ((rc = run_compress(cfg, seqs, n_seqs, proxy_k, comp_logits, pg, ln_gamma, ln_beta, store, st)))
+        return rc;
     // pieces: over the side stream, or one after the other on the caller's
     // stream if the side stream could not be created (same layout)
     SideStream* side = side_stream();

@@ -210,6 +210,8 @@ struct QkPrepArgs {
 static_assert(sizeof(SeqTable) + sizeof(IndexArgs) <= 4096, "index kernel arguments fit");
 static_assert(sizeof(SeqTable) + sizeof(AttnArgs) + 8 <= 4096, "attention kernel arguments fit");
 static_assert(sizeof(SeqTable) + sizeof(CompressArgs) <= 4096, "compress kernel arguments fit");
+static_assert(sizeof(SeqTable) + sizeof(IndexArgs) + sizeof(CompressArgs) <= 4096,
+              "scoring-with-merge kernel arguments fit");
 
 // ---------------------------------------------------------------------------
 // launchers (defined next to their kernels); return hipError_t of the launch
@@ -222,9 +224,11 @@ constexpr size_t kMaxLds = 160 * 1024;
 hipError_t launch_index_topk(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
                              hipStream_t stream);
 // decode-sized calls: score wavefronts over candidate splits, then one
-// select workgroup per (query, group)
+// select workgroup per (query, group).  merge: step 1 carried in the
+// scoring launch (calls whose queries read none of the blocks they
+// complete), or null
 hipError_t launch_index_split(const SeqTable& seqs, int64_t max_nq, const IndexArgs& a,
-                              hipStream_t stream);
+                              hipStream_t stream, const CompressArgs* merge = nullptr);
 // prefill-sized calls: 16-query workgroups score candidate ranges of
 // a.split_blocks blocks against store tiles shared through LDS, then one
 // select workgroup per (query, group)

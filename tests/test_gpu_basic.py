@@ -1,5 +1,6 @@
 """First GPU parity checks: generator twin, the tiny prefill in full, forward
-vs the three calls, determinism."""
+vs the three calls (also a decode call whose merge rides in the scoring
+launch), determinism."""
 import numpy as np
 import pytest
 import torch
@@ -8,6 +9,7 @@ import synth
 from synth import workloads as W
 
 from .gpu_checks import Checker, log, prepare, run_steps
+from .gpu_setup import poison_store
 
 pytestmark = pytest.mark.gpu
 
@@ -62,4 +64,28 @@ def test_forward_equals_steps_and_is_deterministic():
         assert torch.equal(di[k], v), k
     run_steps(wl, di, cfg, use_forward=True)
     for k, v in a.items():
+        assert torch.equal(di[k], v), k
+
+
+def test_decode_forward_carries_the_merge():
+    """A decode call (one new token per sequence) reads none of the blocks it
+    completes, so sgqa_forward merges them inside the scoring launch.  The
+    store rows it completes (NaN codes before the call), the selections and
+    the outputs equal those of the three separate calls bit for bit."""
+    wl = W.make("decode_64_small")
+    B = wl.block_size
+    done = [s for s in wl.seqs if (s.pos0 + 1) % B == 0]
+    log("case decode_64_small: sequences completing a block:", len(done))
+    assert len(done) >= 8
+    di, cfg = prepare(wl)
+    run_steps(wl, di, cfg)
+    keys = ("store", "sel", "sel_scores", "out", "lse")
+    ref = {k: di[k].clone() for k in keys}
+    for s in done:
+        r = s.store_offset + s.pos0 // B
+        poison_store(di["store"][r:r + 1])
+    for k in keys[1:]:
+        di[k].zero_()
+    run_steps(wl, di, cfg, use_forward=True)
+    for k, v in ref.items():
         assert torch.equal(di[k], v), k
