@@ -269,9 +269,11 @@ int sgqa_sparse_attn(const sgqa_config* cfg, const sgqa_seq* seqs, int32_t n_seq
  * written are the same.
  *
  * Calls of at least 2048 queries whose index step works in the tiled mode and
- * whose every query takes the unsplit gather attention (long histories, e.g.
- * a prefill chunk over a 1M-token cache) run in pieces of at least 1024
- * queries: each piece's index step on hip_stream, its attention on a second
+ * whose gather attention takes at least 1024 of them (long histories, e.g. a
+ * prefill chunk over a 1M-token cache or a 64K-token prefill) run in pieces
+ * of at least 1024 queries, when cutting them into pieces leaves every
+ * query's attention kernel and the gather's ranges unchanged: each piece's
+ * index step on hip_stream, its attention on a second
  * stream of the same device that the library creates on the device's first
  * such call (default priority, kept until the process ends), after an event
  * recorded behind that index step -- so a piece's attention overlaps the next

@@ -722,26 +722,51 @@ ForwardLayout plan_forward(const sgqa_config* c, const sgqa_seq* s, int32_t n, b
     const IndexPlan ip = plan_index(c, s, n);
     const AttnPlan ap = plan_attn(c, s, n);
     f.ws = std::max(ip.ws, ap.ws);
-    // pieces only where every query takes the unsplit gather (so each
-    // query's attention runs exactly as in a single-stream call)
-    if (!allow_pieces || ip.mode != IndexMode::Tiled || ap.n_split != 1) return f;
-    int64_t total_q = 0;
+    // pieces only where the gather takes queries (whose memory-bound
+    // attention can run beside the next piece's index step), and only when
+    // every query's attention runs in the pieces exactly as in a
+    // single-stream call (checked below)
+    if (!allow_pieces || ip.mode != IndexMode::Tiled) return f;
+    int64_t total_q = 0, gather_q = 0;
     for (int32_t i = 0; i < n; ++i) {
-        if (s[i].n_q > 0 && dense_queries(c, s[i]) > 0) return f;
         total_q += s[i].n_q;
+        gather_q += s[i].n_q - dense_queries(c, s[i]);
     }
-    if (total_q < 2 * kPieceQueries) return f;
+    if (total_q < 2 * kPieceQueries || gather_q < kPieceQueries) return f;
     // pieces of a multiple of 16 queries (the index tiles keep their
     // boundaries) and at least kPieceQueries each (their index steps stay
     // tiled)
     const int64_t np = std::min<int64_t>(kMaxPieces, total_q / kPieceQueries);
     const int64_t per = total_q / np / 16 * 16;
     const auto piece = cut_pieces(s, n, per, np);
+    // each query keeps its kernel (the tiled kernel for a sequence's leading
+    // dense-ish queries, else the gather) and the gather keeps its ranges
+    // (the same split count and split length), so every query's attention is
+    // the same arithmetic as in the single-stream call
+    std::vector<int64_t> dense(n);
+    for (int32_t i = 0; i < n; ++i) dense[i] = dense_queries(c, s[i]);
     size_t idx_ws = 0, attn_ws = 0;
+    int32_t si = 0;                   // the call's sequence of the next part (parts
+    int64_t done = 0;                 // follow the sequences in order), its queries so far
     for (const auto& pc : piece) {
         const IndexPlan pi = plan_index(c, pc.data(), (int32_t)pc.size());
         const AttnPlan pa = plan_attn(c, pc.data(), (int32_t)pc.size());
-        if (pi.mode != IndexMode::Tiled || pa.n_split != 1) return f;
+        if (pi.mode != IndexMode::Tiled) return f;
+        int64_t pg = 0;
+        for (const sgqa_seq& q : pc) {
+            while (si < n && done >= s[si].n_q) {
+                ++si;
+                done = 0;
+            }
+            if (si == n) return f;
+            const int64_t want = std::max<int64_t>(0, std::min<int64_t>(q.n_q, dense[si] - done));
+            if (dense_queries(c, q) != want) return f;
+            pg += q.n_q - want;
+            done += q.n_q;
+        }
+        if (pg > 0 && (pa.n_split != ap.n_split || pa.range_split != ap.range_split ||
+                       (ap.n_split > 1 && pa.chunks_per_split != ap.chunks_per_split)))
+            return f;
         idx_ws = std::max(idx_ws, pi.ws);
         attn_ws = std::max(attn_ws, pa.ws);
     }

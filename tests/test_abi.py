@@ -183,8 +183,14 @@ def test_prefill_key_workspace(L):
     assert sg.workspace_size(cfg, [sg.seq(8192)], sg.OP_SPARSE_ATTN) == 0
     # long prefills run in passes over query rows: the keys stay within 4 GiB
     cfg1 = sg.config(block_size=1, topk_blocks=2048)
-    ws = sg.workspace_size(cfg1, [sg.seq(65536, block_size=1)], sg.OP_FORWARD)
-    assert (1 << 20) * 16 <= ws <= (1 << 32) + (1 << 25)
+    seqs1 = [sg.seq(65536, block_size=1)]
+    ws_idx = sg.workspace_size(cfg1, seqs1, sg.OP_INDEX_TOPK)
+    assert (1 << 20) * 16 <= ws_idx <= (1 << 32) + (1 << 25)
+    # the forward call runs in pieces: a piece's keys, then the gather's
+    # partial results, then the diagnostics block
+    ws = sg.workspace_size(cfg1, seqs1, sg.OP_FORWARD)
+    assert ws_idx <= ws <= ws_idx + sg.workspace_size(cfg1, seqs1, sg.OP_SPARSE_ATTN) + (1 << 20)
+    assert sg.forward_diag_offset(cfg1, seqs1) == ws - 256
 
 
 def test_forward_pieces_workspace(L):

@@ -1,9 +1,12 @@
-"""sgqa_forward in pieces: calls whose index step is tiled and whose every
-query takes the unsplit gather attention run each piece's index step on the
-caller's stream and its attention on the library's second stream.  Checked
-against the same three steps as separate calls on one stream (bit-identical
-sel, sel_scores, out and lse), the shared diagnostics block at
-sgqa_forward_diag_offset, and the oracle on sampled rows."""
+"""sgqa_forward in pieces: calls whose index step is tiled and whose gather
+attention takes queries run each piece's index step on the caller's stream
+and its attention on the library's second stream, when every query keeps
+its attention kernel and the gather its ranges.  Checked against the same
+three steps as separate calls on one stream (bit-identical sel, sel_scores,
+out and lse), the shared diagnostics block at sgqa_forward_diag_offset, and
+the oracle on sampled rows.  The cases cover the unsplit gather over long
+caches, and prefills whose leading queries take the tiled attention kernel
+and the rest the gather with range splits."""
 import time
 
 import numpy as np
@@ -29,6 +32,11 @@ CASES = {
     # B = 1, k = 2048: listed rows of 150,000+ candidates, pieces of 1,040 and
     # 1,060 queries (k above 1024: four-wavefront rescue select)
     "one sequence, B = 1": lambda: W.make("chunk_150000_2100_b1_k2048"),
+    # a prefill from t = 0: queries below t = 16,384 take the tiled attention
+    # kernel, the rest the gather with four range splits; 16 pieces of 1,248
+    "prefill, tiled and range-split gather": lambda: W.make("prefill_20000"),
+    # the same at B = 1, k = 2048 (tiled below t = 8,192); 11 pieces of 1,088
+    "prefill, tiled and range-split gather, B = 1": lambda: W.make("prefill_12000_b1_k2048"),
 }
 
 
@@ -51,9 +59,11 @@ def test_forward_pieces_match_separate_calls(case):
     di, cfg = prepare(wl)
     seqs = lib_seqs(wl)
     fwd = sg.workspace_size(cfg, seqs, sg.OP_FORWARD)
-    # the call is run in pieces: its workspace is the pieces' layout, with
-    # the diagnostics block at its end
-    assert 0 < fwd < sg.workspace_size(cfg, seqs, sg.OP_INDEX_TOPK)
+    # the call is run in pieces: its workspace is the pieces' layout (not the
+    # larger of the single-stream index and attention workspaces), with the
+    # diagnostics block at its end
+    single = max(sg.workspace_size(cfg, seqs, sg.OP_INDEX_TOPK), sg.workspace_size(cfg, seqs, sg.OP_SPARSE_ATTN))
+    assert 0 < fwd != single
     off = sg.forward_diag_offset(cfg, seqs)
     assert off == fwd - 256
     ws = _aligned_ws(fwd)
